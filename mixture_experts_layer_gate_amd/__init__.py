@@ -1,0 +1,12 @@
+"""MI355X-native forward pass of one Mixture-of-Experts layer.
+
+Route (gate GEMM + top-k softmax), dispatch (histogram, scan, stable
+permutation), grouped SwiGLU expert FFN and weighted combine, each a
+hand-written HIP kernel for gfx950 behind the C-ABI declared in
+``include/moe.h``. The Python functions here only marshal torch tensors into
+that ABI; the library is loaded on first use and a missing build is an error.
+"""
+from .api import (  # noqa: F401
+    MoeError, Dims, workspace_bytes, route, permute, grouped_ffn, combine, layer_forward,
+    library_path, load_library, STAGES, EXPORTS, make_workspace, timing_enable, timing_disable, timing_read,
+)

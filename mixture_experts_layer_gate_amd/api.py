@@ -1,0 +1,240 @@
+"""Thin ctypes binding of the C ABI in ``include/moe.h``.
+
+Each function takes torch tensors that already live on the GPU, checks their
+dtype and shape, and passes ``data_ptr()`` values, the workspace and the
+current HIP stream to the library. No step of the layer runs here. The library
+is loaded on first use; if it is missing, calls raise -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmoe_amd.so"
+
+STAGES = ["gate", "topk", "hist", "scan", "scatter", "plan", "fc1", "fc2", "combine"]
+MOE_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+# Every symbol include/moe.h declares.
+EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route", "moe_permute",
+           "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
+           "moe_timing_disable", "moe_timing_read"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("f", ctypes.c_int64),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    T: int
+    d: int
+    f: int
+    E: int
+    k: int
+    dtype: torch.dtype = torch.bfloat16
+
+    def c(self) -> _Dims:
+        return _Dims(self.T, self.d, self.f, self.E, self.k, MOE_DTYPE.get(self.dtype, -1))
+
+
+def library_path() -> str:
+    return os.environ.get("MOE_AMD_LIB", os.path.join(_PKG, _LIB_NAME))
+
+
+_lib = None
+_P = ctypes.c_void_p
+_S = ctypes.c_size_t
+_DP = ctypes.POINTER(_Dims)
+
+
+def load_library():
+    """Load the built library (and declare its signatures). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.moe_version.restype = ctypes.c_int
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_workspace_bytes.restype = _S
+    lib.moe_workspace_bytes.argtypes = [_DP]
+    lib.moe_route.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _S, _P]
+    lib.moe_permute.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _S, _P]
+    lib.moe_grouped_ffn.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
+    lib.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P]
+    lib.moe_layer_forward.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
+    lib.moe_timing_enable.argtypes = [ctypes.c_int]
+    lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+               "moe_timing_enable", "moe_timing_disable", "moe_timing_read"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status, load_library().moe_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(dims: Dims) -> int:
+    return int(load_library().moe_workspace_bytes(ctypes.byref(dims.c())))
+
+
+def make_workspace(dims: Dims, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(dims), 256), dtype=torch.uint8, device=device)
+
+
+def _ws(dims: Dims, ws: Optional[torch.Tensor]):
+    if ws is None:
+        ws = make_workspace(dims)
+    return ws, ws.numel()
+
+
+def route(dims: Dims, x, wg, bias=None, logits=None, topk_idx=None, topk_w=None, ws=None, stream=None):
+    """Gate logits, top-k indices and weights. Returns (logits, topk_idx, topk_w)."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    _need(wg, "wg", dims.dtype, (dims.E, dims.d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (dims.E,))
+    logits = torch.empty((dims.T, dims.E), dtype=torch.float32, device=dev) if logits is None else logits
+    topk_idx = torch.empty((dims.T, dims.k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_w = torch.empty((dims.T, dims.k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    ws, nws = _ws(dims, ws)
+    _check("moe_route", lib.moe_route(ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(logits),
+                                      _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nws, _stream(stream)))
+    return logits, topk_idx, topk_w
+
+
+def permute(dims: Dims, topk_idx, ws=None, stream=None):
+    """Returns (counts, offsets, perm, inv_perm)."""
+    lib = load_library()
+    dev = topk_idx.device
+    _need(topk_idx, "topk_idx", torch.int32, (dims.T, dims.k))
+    n = dims.T * dims.k
+    counts = torch.empty(dims.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(dims.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    inv = torch.empty(n, dtype=torch.int32, device=dev)
+    ws, nws = _ws(dims, ws)
+    _check("moe_permute", lib.moe_permute(ctypes.byref(dims.c()), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                                          _ptr(perm), _ptr(inv), _ptr(ws), nws, _stream(stream)))
+    return counts, offsets, perm, inv
+
+
+def grouped_ffn(dims: Dims, x, perm, counts, offsets, w1, w3, w2, y_sorted=None, ws=None, stream=None):
+    """Returns y_sorted [T*k, d]."""
+    lib = load_library()
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    _need(perm, "perm", torch.int32, (dims.T * dims.k,))
+    _need(counts, "counts", torch.int32, (dims.E,))
+    _need(offsets, "offsets", torch.int32, (dims.E + 1,))
+    if y_sorted is None:
+        y_sorted = torch.empty((dims.T * dims.k, dims.d), dtype=dims.dtype, device=x.device)
+    ws, nws = _ws(dims, ws)
+    _check("moe_grouped_ffn", lib.moe_grouped_ffn(ctypes.byref(dims.c()), _ptr(x), _ptr(perm), _ptr(counts),
+                                                  _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y_sorted),
+                                                  _ptr(ws), nws, _stream(stream)))
+    return y_sorted
+
+
+def combine(dims: Dims, y_sorted, inv_perm, topk_w, out=None, stream=None):
+    """Returns out [T, d]."""
+    lib = load_library()
+    _need(y_sorted, "y_sorted", dims.dtype, (dims.T * dims.k, dims.d))
+    _need(inv_perm, "inv_perm", torch.int32, (dims.T * dims.k,))
+    _need(topk_w, "topk_w", torch.float32, (dims.T, dims.k))
+    if out is None:
+        out = torch.empty((dims.T, dims.d), dtype=dims.dtype, device=y_sorted.device)
+    _check("moe_combine", lib.moe_combine(ctypes.byref(dims.c()), _ptr(y_sorted), _ptr(inv_perm), _ptr(topk_w),
+                                          _ptr(out), _stream(stream)))
+    return out
+
+
+def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False):
+    """The whole layer. With return_routing, also returns the routing arrays as a dict."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    _need(wg, "wg", dims.dtype, (dims.E, dims.d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (dims.E,))
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    if out is None:
+        out = torch.empty((dims.T, dims.d), dtype=dims.dtype, device=dev)
+    r = {}
+    if return_routing:
+        n = dims.T * dims.k
+        r = {"logits": torch.empty((dims.T, dims.E), dtype=torch.float32, device=dev),
+             "topk_idx": torch.empty((dims.T, dims.k), dtype=torch.int32, device=dev),
+             "topk_w": torch.empty((dims.T, dims.k), dtype=torch.float32, device=dev),
+             "counts": torch.empty(dims.E, dtype=torch.int32, device=dev),
+             "offsets": torch.empty(dims.E + 1, dtype=torch.int32, device=dev),
+             "perm": torch.empty(n, dtype=torch.int32, device=dev),
+             "inv_perm": torch.empty(n, dtype=torch.int32, device=dev)}
+    ws, nws = _ws(dims, ws)
+    g = r.get
+    _check("moe_layer_forward", lib.moe_layer_forward(
+        ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+        _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")), _ptr(g("counts")), _ptr(g("offsets")),
+        _ptr(g("perm")), _ptr(g("inv_perm")), _ptr(ws), nws, _stream(stream)))
+    return (out, r) if return_routing else out
+
+
+def timing_enable(capacity: int):
+    _check("moe_timing_enable", load_library().moe_timing_enable(capacity))
+
+
+def timing_disable():
+    _check("moe_timing_disable", load_library().moe_timing_disable())
+
+
+def timing_read(stage: str):
+    """(total kernel ms, launches) recorded for a stage since timing_enable."""
+    ms, n = ctypes.c_double(), ctypes.c_int()
+    _check("moe_timing_read", load_library().moe_timing_read(STAGES.index(stage), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

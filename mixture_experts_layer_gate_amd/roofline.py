@@ -1,0 +1,100 @@
+"""Work and roofline accounting for one MoE-layer forward call (host-side, pure Python).
+
+* util(): the expert-FFN utilisation bound of MegaScale-Infer, section 2.3:
+  util = min(topk/#expert * B/F * b, 1) for a batch of b tokens, memory
+  bandwidth B and compute rate F.
+* expert_weight_bytes(): 3*E*d*f parameters per layer (Piper, section III-A,
+  Table III), at the element size of the stored weights.
+* layer_flops() / layer_bytes(): the algorithmic work of one call, counted
+  from the actual per-expert row counts, so a skewed routing that leaves
+  experts idle is charged only for the experts it uses.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Iterable, Sequence
+
+# MI355X published peaks (dense, no sparsity)
+PEAK_HBM_BYTES_PER_S = 8.0e12
+PEAK_MFMA_BF16_FLOPS = 2.5e15
+PEAK_MFMA_FP32_FLOPS = 157.3e12
+PEAK_VALU_FP32_FLOPS = 157.3e12
+
+
+def util(topk: int, experts: int, B: float, F: float, b: float) -> float:
+    """Utilisation bound of the expert FFN for a global batch of b tokens."""
+    return min(topk / experts * B / F * b, 1.0)
+
+
+def min_full_util_batch(B: float, F: float) -> float:
+    """Tokens one weight matrix needs to be compute-bound (F/B)."""
+    return F / B
+
+
+def expert_weight_bytes(E: int, d: int, f: int, elt_bytes: int = 2) -> int:
+    """Bytes of one layer's expert weights: three d x f matrices per expert."""
+    return 3 * E * d * f * elt_bytes
+
+
+def layer_flops(T: int, d: int, f: int, E: int, k: int) -> int:
+    """Algorithmic FLOP: gate GEMM 2*T*d*E plus FC1 (4*d*f per row) and FC2 (2*d*f per row)."""
+    return 2 * T * d * E + 6 * d * f * T * k
+
+
+def ffn_flops(rows: int, d: int, f: int) -> int:
+    return 6 * d * f * rows
+
+
+def fc1_flops(rows: int, d: int, f: int) -> int:
+    return 4 * d * f * rows
+
+
+def fc2_flops(rows: int, d: int, f: int) -> int:
+    return 2 * d * f * rows
+
+
+def active_experts(counts: Iterable[int]) -> int:
+    return sum(1 for c in counts if int(c) > 0)
+
+
+def layer_bytes(T: int, d: int, f: int, E: int, counts: Sequence[int], elt: int = 2) -> int:
+    """Algorithmic HBM bytes of one call: weights of the experts that receive
+    at least one row, the gate weight, x read once and out written once."""
+    a = active_experts(counts)
+    return 3 * d * f * elt * a + d * E * elt + 2 * T * d * elt
+
+
+def fc1_bytes(T: int, d: int, f: int, k: int, counts: Sequence[int], elt: int = 2) -> int:
+    """FC1 kernel: W1 and W3 of active experts, the T*k gathered x rows, h written."""
+    a = active_experts(counts)
+    return 2 * d * f * elt * a + T * k * d * elt + T * k * f * elt
+
+
+def fc2_bytes(T: int, d: int, f: int, k: int, counts: Sequence[int], elt: int = 2) -> int:
+    """FC2 kernel: W2 of active experts, h read, y written."""
+    a = active_experts(counts)
+    return d * f * elt * a + T * k * f * elt + T * k * d * elt
+
+
+def kappa(counts: Sequence[int]) -> float:
+    """Routing-skew statistic: max rows per expert over the mean (1 for uniform)."""
+    c = [int(v) for v in counts]
+    mean = sum(c) / len(c)
+    return max(c) / mean if mean > 0 else 0.0
+
+
+@dataclass
+class Roofline:
+    bound: str          # "hbm" or "mfma"
+    t_flop_s: float
+    t_byte_s: float
+
+    @property
+    def floor_s(self) -> float:
+        return max(self.t_flop_s, self.t_byte_s)
+
+
+def classify(flops: float, nbytes: float, F: float = PEAK_MFMA_BF16_FLOPS,
+             B: float = PEAK_HBM_BYTES_PER_S) -> Roofline:
+    tf, tb = flops / F, nbytes / B
+    return Roofline("mfma" if tf >= tb else "hbm", tf, tb)
