@@ -1,0 +1,170 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of one Mixture-of-Experts layer.
+ *
+ * One layer call computes, for T tokens x[t] (hidden size d), E routed experts
+ * (SwiGLU, FFN size f) and top-k routing:
+ *
+ *   l[t,e]   = x[t] . Wg[e] + bias[e]                      gate GEMM + bias
+ *   S_t      = the k largest l[t,.]  (ties: lower e)         top-k
+ *   w[t,j]   = softmax over the k selected logits            renormalised weights
+ *   out[t]   = sum_j w[t,j] * W2_e ( SiLU(W1_e x[t]) * (W3_e x[t]) ),  e = S_t[j]
+ *
+ * Sources: the gating network and its routing steps (top-k, per-expert counts,
+ * weight normalisation, scatter into per-expert buffers) follow MegaScale-Infer,
+ * "3.2 Big-Picture Architecture" and "Supporting Implementation Details / Fused
+ * Kernels"; the per-expert assignment order (token, then top-k position) follows
+ * MegaFlux appendix A.2; tile-aligned token blocks follow MegaFlux section 3.1;
+ * the SwiGLU expert (gate, up and down matrices) follows Piper section III-A.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All pointers are DEVICE pointers unless stated otherwise; `dims` is a HOST
+ *   pointer. The caller owns every buffer; the library never allocates device
+ *   memory and keeps no pointer after the call returns.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream). Buffers must stay valid until the stream has passed the call.
+ * - Arguments are validated on the host before anything is enqueued. On an
+ *   invalid argument nothing is launched and a nonzero moe_status_t comes back.
+ *   Faults during execution surface at the caller's next synchronisation.
+ * - Layouts are row-major; "[a][b]" lists dimensions outermost first. Weights
+ *   use the linear-layer layout [out][in] per expert.
+ * - dtype MOE_DTYPE_BF16: x, Wg, W1, W3, W2, the intermediate h, y_sorted and
+ *   out are bf16 (fp32 accumulation, round-to-nearest-even stores).
+ *   dtype MOE_DTYPE_F32: all of them are fp32. bias, logits and topk_w are fp32
+ *   in both cases; indices and counts are int32.
+ * - Assignment a = t*k + j (token t, slot j). Sorted position p orders the
+ *   assignments by expert, then by a.
+ * - Shape limits: T >= 0 (T = 0 is a no-op), d >= 1, f >= 1, 1 <= k <= E <= 1024,
+ *   T*k < 2^31, T*E < 2^31. The GPU path needs d % 64 == 0 and f % 64 == 0
+ *   (MOE_ERR_UNSUPPORTED otherwise; moe_route alone accepts d % 8 == 0).
+ *   Device pointers to bf16/fp32 tensors must be 16-byte aligned.
+ * - Non-finite inputs give unspecified results.
+ * - Thread safety: calls are independent except for the stage-timing state,
+ *   which is process-wide.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1
+} moe_dtype_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* null pointer, bad shape, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid shape the GPU path does not run (see limits) */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes below what the call needs */
+  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} moe_status_t;
+
+typedef struct {
+  int64_t T;     /* tokens */
+  int64_t d;     /* hidden size */
+  int64_t f;     /* expert FFN size */
+  int32_t E;     /* routed experts */
+  int32_t k;     /* experts per token */
+  int32_t dtype; /* moe_dtype_t */
+} moe_dims_t;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* moe_status_string(int status);
+
+/* Workspace bytes that make every call below succeed for `dims` (the maximum
+ * over the calls; moe_layer_forward with every optional output NULL needs the
+ * most). 0 if dims is invalid. The workspace must be 256-byte aligned. */
+size_t moe_workspace_bytes(const moe_dims_t* dims);
+
+/* Gate GEMM + bias, top-k selection and renormalised weights
+ * (MegaScale-Infer, Fused Kernels, steps 1 and 3).
+ *   x      [T][d]   tokens
+ *   wg     [E][d]   gate weight
+ *   bias   [E] fp32 per-expert gate-logit bias, or NULL for none
+ *   logits [T][E] fp32 output, or NULL (then kept in ws)
+ *   topk_idx [T][k] int32 output: slot j = expert with the j-th largest logit
+ *   topk_w   [T][k] fp32 output: exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * Logits are bit-reproducible: each is the fp32 sum of the products
+ * x[t,i]*Wg[e,i] in a fixed order -- 64 lane classes i mod 64, each summed in
+ * increasing i from +0.0, then a butterfly over offsets 32,16,8,4,2,1, then
+ * one add of bias[e] -- with fp32 products rounded before each add. */
+int moe_route(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: per-expert histogram, exclusive scan and stable permutation
+ * (MegaScale-Infer, Fused Kernels, steps 2 and 4; MegaFlux appendix A.2).
+ *   topk_idx [T][k] int32 input, every entry in [0, E)
+ *   counts   [E]    rows per expert
+ *   offsets  [E+1]  exclusive prefix sum; offsets[E] = T*k
+ *   perm     [T*k]  perm[p] = a
+ *   inv_perm [T*k]  inv_perm[a] = p
+ * Out-of-range expert ids in topk_idx give unspecified (in-bounds) output. */
+int moe_permute(const moe_dims_t* dims, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU expert FFN over the sorted rows (Piper, section III-A;
+ * MegaFlux, sections 2.1 and 3.1): for each sorted row p of expert e,
+ * with t = perm[p] / k,
+ *   h[p]        = SiLU(W1_e x[t]) * (W3_e x[t])      (h rounded to dtype, kept in ws)
+ *   y_sorted[p] = W2_e h[p]
+ *   x [T][d]; w1, w3 [E][f][d]; w2 [E][d][f]; y_sorted [T*k][d] output.
+ * perm, counts, offsets as produced by moe_permute. */
+int moe_grouped_ffn(const moe_dims_t* dims, const void* x, const int32_t* perm,
+                    const int32_t* counts, const int32_t* offsets,
+                    const void* w1, const void* w3, const void* w2, void* y_sorted,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (MegaFlux section 2.1, the separate final top-k sum):
+ *   out[t] = sum_{j ascending} topk_w[t][j] * y_sorted[inv_perm[t*k+j]]
+ * accumulated in fp32, stored in dtype. out [T][d]. */
+int moe_combine(const moe_dims_t* dims, const void* y_sorted, const int32_t* inv_perm,
+                const float* topk_w, void* out, void* stream);
+
+/* The whole layer: route -> permute -> grouped FFN -> combine, all on `stream`,
+ * with no host synchronisation. logits, topk_idx, topk_w, counts, offsets,
+ * perm and inv_perm are optional outputs (NULL = kept in ws). */
+int moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+                      const void* w1, const void* w3, const void* w2, void* out,
+                      float* logits, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---- stage timing (instrumentation; process-wide, not thread-safe) ----
+ * While enabled, every kernel the library launches is bracketed by HIP events
+ * recorded on the stream it is launched on. Stages: */
+enum {
+  MOE_STAGE_GATE = 0,     /* gate logits */
+  MOE_STAGE_TOPK = 1,     /* top-k + weights */
+  MOE_STAGE_HIST = 2,     /* dispatch histogram */
+  MOE_STAGE_SCAN = 3,     /* dispatch scan */
+  MOE_STAGE_SCATTER = 4,  /* dispatch permutation */
+  MOE_STAGE_PLAN = 5,     /* tile plan */
+  MOE_STAGE_FC1 = 6,      /* grouped FC1 + SiLU*mul */
+  MOE_STAGE_FC2 = 7,      /* grouped FC2 */
+  MOE_STAGE_COMBINE = 8,  /* weighted combine */
+  MOE_NUM_STAGES = 9
+};
+/* Start recording; `capacity` = launches per stage to keep (host memory only).
+ * Discards earlier records. */
+int moe_timing_enable(int capacity);
+/* Stop recording (records are kept until the next enable). */
+int moe_timing_disable(void);
+/* Synchronises on the recorded events of `stage` and returns the summed
+ * kernel time in ms and the number of launches recorded. */
+int moe_timing_read(int stage, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

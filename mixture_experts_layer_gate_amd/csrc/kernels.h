@@ -1,0 +1,45 @@
+// Host-side launchers of the MoE-layer kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Rows per m-block of the grouped GEMM (tile-aligned token blocks).
+constexpr int kBlockRows = 128;
+
+// Gate logits l[t][e] in the fixed fp32 order. Requires d % 8 == 0.
+hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const float* bias,
+                              float* logits, int64_t T, int64_t d, int E, hipStream_t s);
+// Top-k selection + renormalised softmax weights from logits.
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t s);
+
+// Dispatch. n = T*k assignments, cut into n_chunks chunks of `chunk` assignments.
+void dispatch_chunking(int64_t n, int* chunk, int* n_chunks);
+hipError_t launch_hist(const int32_t* idx, int64_t n, int E, int chunk, int n_chunks,
+                       int32_t* block_hist, hipStream_t s);
+hipError_t launch_scan(int32_t* block_hist, int n_chunks, int E, int32_t* counts, int32_t* offsets,
+                       hipStream_t s);
+hipError_t launch_scatter(const int32_t* idx, int64_t n, int E, int chunk, int n_chunks,
+                          const int32_t* block_base, int32_t* perm, int32_t* inv_perm, hipStream_t s);
+
+// Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most kBlockRows rows.
+int64_t max_mblocks(int64_t n_assign, int E);
+hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,
+                       int64_t max_mb, int4* mblocks, int32_t* n_mblocks, hipStream_t s);
+
+// Grouped GEMMs over the m-block list.
+hipError_t launch_fc1(int dtype, const void* x, const int32_t* perm, int k, int64_t T,
+                      const void* w1, const void* w3, void* h, const int4* mblocks,
+                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
+hipError_t launch_fc2(int dtype, const void* h, const void* w2, void* y, const int4* mblocks,
+                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
+
+// Weighted combine.
+hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, const float* w,
+                          void* out, int64_t T, int64_t d, int k, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

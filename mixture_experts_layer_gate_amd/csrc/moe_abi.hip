@@ -1,0 +1,352 @@
+// C ABI of the MoE-layer library: argument validation, workspace carving,
+// stage timing and the launch sequence. Declarations and the contract of each
+// entry point are in include/moe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "moe.h"
+#include "kernels.h"
+
+namespace moe {
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------- stage timing ----------------
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  int cap = 0;
+  std::vector<hipEvent_t> ev[MOE_NUM_STAGES][2];
+  int n[MOE_NUM_STAGES] = {0};
+} g_timing;
+
+struct StageScope {
+  int stage;
+  hipStream_t s;
+  int slot = -1;
+  StageScope(int st, hipStream_t stream) : stage(st), s(stream) {
+    if (!g_timing.on) return;
+    if (g_timing.n[stage] < g_timing.cap) {
+      slot = g_timing.n[stage]++;
+      (void)hipEventRecord(g_timing.ev[stage][0][slot], s);
+    }
+  }
+  ~StageScope() {
+    if (slot >= 0) (void)hipEventRecord(g_timing.ev[stage][1][slot], s);
+  }
+};
+
+// ---------------- validation ----------------
+int check_dims(const moe_dims_t* dm) {
+  if (!dm) return MOE_ERR_INVALID;
+  if (dm->T < 0 || dm->d < 1 || dm->f < 1) return MOE_ERR_INVALID;
+  if (dm->d >= (int64_t(1) << 31) || dm->f >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
+  if (dm->k < 1 || dm->E < dm->k || dm->E > 1024) return MOE_ERR_INVALID;
+  if (dm->dtype != MOE_DTYPE_F32 && dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (dm->T * dm->k >= (int64_t(1) << 31) || dm->T * dm->E >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+int elt_bytes(const moe_dims_t* dm) { return dm->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+bool ok16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool ok4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+bool ok4_or_null(const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+// ---------------- workspace layouts ----------------
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off = align_up(off + bytes);
+    return p;
+  }
+};
+
+struct RouteWs { float* logits; };
+size_t route_ws(const moe_dims_t* dm, void* ws, bool need_logits, RouteWs* out) {
+  Carver c(ws);
+  RouteWs r{};
+  if (need_logits) r.logits = c.take<float>(sizeof(float) * dm->T * dm->E);
+  if (out) *out = r;
+  return c.off;
+}
+
+struct PermuteWs { int32_t* block_hist; int chunk, n_chunks; };
+size_t permute_ws(const moe_dims_t* dm, void* ws, PermuteWs* out) {
+  Carver c(ws);
+  PermuteWs r{};
+  dispatch_chunking(dm->T * dm->k, &r.chunk, &r.n_chunks);
+  r.block_hist = c.take<int32_t>(sizeof(int32_t) * size_t(r.n_chunks) * dm->E);
+  if (out) *out = r;
+  return c.off;
+}
+
+struct FfnWs { int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; };
+size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out) {
+  Carver c(ws);
+  FfnWs r{};
+  r.max_mb = max_mblocks(dm->T * dm->k, dm->E);
+  r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
+  r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
+  r.h = c.take<char>(size_t(elt_bytes(dm)) * dm->T * dm->k * dm->f);
+  if (out) *out = r;
+  return c.off;
+}
+
+struct LayerWs {
+  float* logits; int32_t* idx; float* w; int32_t* counts; int32_t* offsets; int32_t* perm;
+  int32_t* inv; void* y; void* sub;  // sub: start of the permute / ffn scratch (shared)
+};
+size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out) {
+  Carver c(ws);
+  LayerWs r{};
+  const size_t n = size_t(dm->T) * dm->k;
+  r.logits = c.take<float>(sizeof(float) * dm->T * dm->E);
+  r.idx = c.take<int32_t>(sizeof(int32_t) * n);
+  r.w = c.take<float>(sizeof(float) * n);
+  r.counts = c.take<int32_t>(sizeof(int32_t) * dm->E);
+  r.offsets = c.take<int32_t>(sizeof(int32_t) * (dm->E + 1));
+  r.perm = c.take<int32_t>(sizeof(int32_t) * n);
+  r.inv = c.take<int32_t>(sizeof(int32_t) * n);
+  r.y = c.take<char>(size_t(elt_bytes(dm)) * n * dm->d);
+  const size_t sub = permute_ws(dm, nullptr, nullptr) > ffn_ws(dm, nullptr, nullptr)
+                         ? permute_ws(dm, nullptr, nullptr) : ffn_ws(dm, nullptr, nullptr);
+  r.sub = c.take<char>(sub);
+  if (out) *out = r;
+  return c.off;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---------------- launch sequences (arguments already validated) ----------------
+int do_route(const moe_dims_t* dm, const void* x, const void* wg, const float* bias, float* logits,
+             int32_t* idx, float* w, hipStream_t s) {
+  {
+    StageScope sc(MOE_STAGE_GATE, s);
+    if (int st = hip_status(launch_gate_logits(dm->dtype, x, wg, bias, logits, dm->T, dm->d, dm->E, s))) return st;
+  }
+  StageScope sc(MOE_STAGE_TOPK, s);
+  return hip_status(launch_topk(logits, dm->T, dm->E, dm->k, idx, w, s));
+}
+
+int do_permute(const moe_dims_t* dm, const int32_t* idx, int32_t* counts, int32_t* offsets,
+               int32_t* perm, int32_t* inv, const PermuteWs& pw, hipStream_t s) {
+  const int64_t n = dm->T * dm->k;
+  {
+    StageScope sc(MOE_STAGE_HIST, s);
+    if (int st = hip_status(launch_hist(idx, n, dm->E, pw.chunk, pw.n_chunks, pw.block_hist, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_SCAN, s);
+    if (int st = hip_status(launch_scan(pw.block_hist, pw.n_chunks, dm->E, counts, offsets, s))) return st;
+  }
+  StageScope sc(MOE_STAGE_SCATTER, s);
+  return hip_status(launch_scatter(idx, n, dm->E, pw.chunk, pw.n_chunks, pw.block_hist, perm, inv, s));
+}
+
+int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
+           const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
+           const FfnWs& fw, hipStream_t s) {
+  {
+    StageScope sc(MOE_STAGE_PLAN, s);
+    if (int st = hip_status(launch_plan(counts, offsets, dm->E, dm->T * dm->k, fw.max_mb, fw.mblocks, fw.n_mblocks, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_FC1, s);
+    if (int st = hip_status(launch_fc1(dm->dtype, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
+                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, s))) return st;
+  }
+  StageScope sc(MOE_STAGE_FC2, s);
+  return hip_status(launch_fc2(dm->dtype, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb, dm->d, dm->f, s));
+}
+
+int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
+               hipStream_t s) {
+  StageScope sc(MOE_STAGE_COMBINE, s);
+  return hip_status(launch_combine(dm->dtype, y, inv, w, out, dm->T, dm->d, dm->k, s));
+}
+
+int ffn_shape_ok(const moe_dims_t* dm) {
+  return (dm->d % 64 == 0 && dm->f % 64 == 0) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument (null or misaligned pointer, or shape outside the limits)";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by the GPU path (needs d % 64 == 0 and f % 64 == 0)";
+    case MOE_ERR_WORKSPACE: return "workspace too small (see moe_workspace_bytes)";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_dims_t* dm) {
+  if (check_dims(dm) != MOE_OK) return 0;
+  size_t m = layer_ws(dm, nullptr, nullptr);
+  const size_t r = route_ws(dm, nullptr, true, nullptr);
+  const size_t p = permute_ws(dm, nullptr, nullptr);
+  const size_t f = ffn_ws(dm, nullptr, nullptr);
+  if (r > m) m = r;
+  if (p > m) m = p;
+  if (f > m) m = f;
+  return m;
+}
+
+int moe_route(const moe_dims_t* dm, const void* x, const void* wg, const float* bias, float* logits,
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok4_or_null(logits) || !ok4(topk_idx) || !ok4(topk_w))
+    return MOE_ERR_INVALID;
+  if (dm->d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  RouteWs rw{};
+  if (!logits) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+    if (ws_bytes < route_ws(dm, nullptr, true, nullptr)) return MOE_ERR_WORKSPACE;
+    route_ws(dm, ws, true, &rw);
+    logits = rw.logits;
+  }
+  return do_route(dm, x, wg, bias, logits, topk_idx, topk_w, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute(const moe_dims_t* dm, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (!ok4(counts) || !ok4(offsets)) return MOE_ERR_INVALID;
+  if (dm->T > 0 && (!ok4(topk_idx) || !ok4(perm) || !ok4(inv_perm))) return MOE_ERR_INVALID;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < permute_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  PermuteWs pw{};
+  permute_ws(dm, ws, &pw);
+  return do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
+                    const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                    void* y_sorted, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  if (!ok16(x) || !ok4(perm) || !ok4(counts) || !ok4(offsets) || !ok16(w1) || !ok16(w3) || !ok16(w2) ||
+      !ok16(y_sorted))
+    return MOE_ERR_INVALID;
+  if (int st = ffn_shape_ok(dm)) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < ffn_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  FfnWs fw{};
+  ffn_ws(dm, ws, &fw);
+  return do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, y_sorted, fw, static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const moe_dims_t* dm, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
+                void* out, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  if (!ok16(y_sorted) || !ok4(inv_perm) || !ok4(topk_w) || !ok16(out)) return MOE_ERR_INVALID;
+  if (dm->d % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  return do_combine(dm, y_sorted, inv_perm, topk_w, out, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const float* bias,
+                      const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                      int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                      int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(out) ||
+      !ok4_or_null(logits) || !ok4_or_null(topk_idx) || !ok4_or_null(topk_w) || !ok4_or_null(counts) ||
+      !ok4_or_null(offsets) || !ok4_or_null(perm) || !ok4_or_null(inv_perm))
+    return MOE_ERR_INVALID;
+  if (int st = ffn_shape_ok(dm)) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < layer_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  LayerWs lw{};
+  layer_ws(dm, ws, &lw);
+  if (!logits) logits = lw.logits;
+  if (!topk_idx) topk_idx = lw.idx;
+  if (!topk_w) topk_w = lw.w;
+  if (!counts) counts = lw.counts;
+  if (!offsets) offsets = lw.offsets;
+  if (!perm) perm = lw.perm;
+  if (!inv_perm) inv_perm = lw.inv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
+  PermuteWs pw{};
+  permute_ws(dm, lw.sub, &pw);
+  if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
+  FfnWs fw{};
+  ffn_ws(dm, lw.sub, &fw);
+  if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s)) return st;
+  return do_combine(dm, lw.y, inv_perm, topk_w, out, s);
+}
+
+int moe_timing_enable(int capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return MOE_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (int st = 0; st < MOE_NUM_STAGES; ++st)
+    for (int b = 0; b < 2; ++b) {
+      auto& v = g_timing.ev[st][b];
+      while (static_cast<int>(v.size()) < capacity) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_HIP;
+        v.push_back(e);
+      }
+    }
+  g_timing.cap = capacity;
+  for (int st = 0; st < MOE_NUM_STAGES; ++st) g_timing.n[st] = 0;
+  g_timing.on = true;
+  return MOE_OK;
+}
+
+int moe_timing_disable(void) {
+  g_timing.on = false;
+  return MOE_OK;
+}
+
+int moe_timing_read(int stage, double* total_ms, int* launches) {
+  if (stage < 0 || stage >= MOE_NUM_STAGES || !total_ms || !launches) return MOE_ERR_INVALID;
+  double tot = 0;
+  const int n = g_timing.n[stage];
+  for (int i = 0; i < n; ++i) {
+    if (hipEventSynchronize(g_timing.ev[stage][1][i]) != hipSuccess) return MOE_ERR_HIP;
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, g_timing.ev[stage][0][i], g_timing.ev[stage][1][i]) != hipSuccess)
+      return MOE_ERR_HIP;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Router: gate logits in a fixed fp32 order, then top-k + renormalised softmax weights.
+//
+// The gating network scores each token against each expert and the first
+// routing steps pick the top-k experts and normalise their weights
+// (MegaScale-Infer, 3.2 item 2 and "Fused Kernels" steps 1 and 3).
+//
+// Logit order (the library's contract, so routing is reproducible bit for bit):
+// lane class j = i mod 64 sums its products in increasing i starting at +0.0;
+// the 64 class sums are then combined by a butterfly with offsets
+// 32,16,8,4,2,1 (s_j += s_{j+off} for j < off); the bias is added last.
+//
+// Work mapping: a group of 8 threads owns a register tile of RT tokens x RE
+// experts; thread q of the group owns the 8 lane classes 8q..8q+7 and loads
+// them as one 16-byte vector per row per 64-element step. The butterfly's
+// first three levels (offsets 32, 16, 8) cross threads of the group
+// (lane distance 4, 2, 1); the last three stay inside a thread.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <int kDtype>
+__device__ __forceinline__ void load8(const void* base, int64_t elem_off, float (&v)[8]) {
+  if constexpr (kDtype == 1) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(base) + elem_off);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// acc + x*w with the product rounded first. For bf16 operands the product is
+// exact in fp32, so a fused multiply-add gives the same bits; fp32 operands
+// need the separate multiply.
+template <int kDtype>
+__device__ __forceinline__ float mac(float x, float w, float acc) {
+  if constexpr (kDtype == 1) {
+    return __builtin_fmaf(x, w, acc);
+  } else {
+#pragma clang fp contract(off)
+    const float p = x * w;
+    return acc + p;
+  }
+}
+
+template <int kDtype, int RT, int RE>
+__global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict__ x,
+                                                          const void* __restrict__ wg,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int T, int d,
+                                                          int E, int n_eb, int64_t n_pb) {
+  const int q = threadIdx.x & 7;
+  const int64_t pb = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 3);
+  const bool live = pb < n_pb;
+  const int64_t pbc = live ? pb : 0;
+  const int tb = static_cast<int>(pbc / n_eb), eb = static_cast<int>(pbc % n_eb);
+
+  int64_t xrow[RT], wrow[RE];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) xrow[r] = static_cast<int64_t>(min(tb * RT + r, T - 1)) * d;
+#pragma unroll
+  for (int r = 0; r < RE; ++r) wrow[r] = static_cast<int64_t>(min(eb * RE + r, E - 1)) * d;
+
+  float acc[RT][RE][8];
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b = 0; b < RE; ++b)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[a][b][r] = 0.0f;
+
+  for (int i0 = q * 8; i0 < d; i0 += 64) {
+    float xv[RT][8], wv[RE][8];
+#pragma unroll
+    for (int a = 0; a < RT; ++a) load8<kDtype>(x, xrow[a] + i0, xv[a]);
+#pragma unroll
+    for (int b = 0; b < RE; ++b) load8<kDtype>(wg, wrow[b] + i0, wv[b]);
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+#pragma unroll
+      for (int b = 0; b < RE; ++b)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[a][b][r] = mac<kDtype>(xv[a][r], wv[b][r], acc[a][b][r]);
+  }
+
+  // Butterfly. Class j = 8q + r. Offsets 32, 16, 8 pair thread q with q+4, q+2, q+1.
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b = 0; b < RE; ++b)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float s = acc[a][b][r];
+        s = s + __shfl_down(s, 4, 8);
+        s = s + __shfl_down(s, 2, 8);
+        s = s + __shfl_down(s, 1, 8);
+        acc[a][b][r] = s;
+      }
+  if (!live || q != 0) return;
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b = 0; b < RE; ++b) {
+      float s[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) s[r] = acc[a][b][r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = s[r] + s[r + 4];
+      s[0] = s[0] + s[2];
+      s[1] = s[1] + s[3];
+      s[0] = s[0] + s[1];
+      const int t = tb * RT + a, e = eb * RE + b;
+      if (t < T && e < E) {
+        const float bv = bias ? bias[e] : 0.0f;
+        logits[static_cast<int64_t>(t) * E + e] = s[0] + bv;
+      }
+    }
+}
+
+template <int kDtype, int RT, int RE>
+static hipError_t gate_launch(const void* x, const void* wg, const float* bias, float* logits,
+                              int64_t T, int64_t d, int E, hipStream_t s) {
+  const int n_tb = static_cast<int>((T + RT - 1) / RT);
+  const int n_eb = (E + RE - 1) / RE;
+  const int64_t n_pb = static_cast<int64_t>(n_tb) * n_eb;
+  const int64_t blocks = (n_pb + 31) / 32;
+  hipLaunchKernelGGL((gate_logits_kernel<kDtype, RT, RE>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(256), 0, s, x, wg, bias, logits, static_cast<int>(T), static_cast<int>(d),
+                     E, n_eb, n_pb);
+  return hipGetLastError();
+}
+
+template <int kDtype>
+static hipError_t gate_dispatch(const void* x, const void* wg, const float* bias, float* logits,
+                                int64_t T, int64_t d, int E, hipStream_t s) {
+  // Largest register tile that still gives >= 2048 waves (8 per CU); tiles no
+  // wider than E in the expert direction.
+  auto waves = [&](int rt, int re) {
+    const int64_t pbs = ((T + rt - 1) / rt) * ((E + re - 1) / re);
+    return pbs * 8 / kWave;
+  };
+  const int64_t want = 2048;
+  if (E >= 4 && waves(2, 4) >= want) return gate_launch<kDtype, 2, 4>(x, wg, bias, logits, T, d, E, s);
+  if (E >= 2 && waves(2, 2) >= want) return gate_launch<kDtype, 2, 2>(x, wg, bias, logits, T, d, E, s);
+  if (E >= 2 && waves(1, 2) >= want) return gate_launch<kDtype, 1, 2>(x, wg, bias, logits, T, d, E, s);
+  return gate_launch<kDtype, 1, 1>(x, wg, bias, logits, T, d, E, s);
+}
+
+hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const float* bias,
+                              float* logits, int64_t T, int64_t d, int E, hipStream_t s) {
+  if (dtype == 1) return gate_dispatch<1>(x, wg, bias, logits, T, d, E, s);
+  return gate_dispatch<0>(x, wg, bias, logits, T, d, E, s);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k: one wave per token. Order: logit descending, equal logits to the
+// lower expert index (IEEE compare, so -0 == +0). Weights: softmax over the k
+// selected logits, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+constexpr int kMaxE = 1024;
+constexpr int kPerLane = kMaxE / kWave;
+
+__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+  return va > vb || (va == vb && ea < eb);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w) {
+  __shared__ float sel_v[4][kMaxE];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  const float* row = logits + static_cast<int64_t>(t) * E;
+  float v[kPerLane];
+  bool taken[kPerLane];
+  const int per = (E + kWave - 1) / kWave;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = lane + i * kWave;
+    const bool ok = i < per && e < E;
+    v[i] = ok ? row[e] : 0.0f;
+    taken[i] = !ok;
+  }
+  float v0 = 0.0f, sum = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int e = lane + i * kWave;
+      if (!taken[i] && (be == 0x7fffffff || better(v[i], e, bv, be))) { bv = v[i]; be = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (oe != 0x7fffffff && (be == 0x7fffffff || better(ov, oe, bv, be))) { bv = ov; be = oe; }
+    }
+    // every lane now holds the same winner (bv, be)
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i)
+      if (lane + i * kWave == be) taken[i] = true;
+    if (j == 0) v0 = bv;
+    sum += expf(bv - v0);
+    if (lane == 0) {
+      idx[static_cast<int64_t>(t) * k + j] = be;
+      sel_v[wv][j] = bv;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float inv = 1.0f / sum;
+  for (int j = lane; j < k; j += kWave) w[static_cast<int64_t>(t) * k + j] = expf(sel_v[wv][j] - v0) * inv;
+}
+
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t s) {
+  const int64_t blocks = (T + 3) / 4;
+  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, logits,
+                     static_cast<int>(T), E, k, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad arguments
+before anything is enqueued. Host-only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mixture_experts_layer_gate_amd as moe
+from mixture_experts_layer_gate_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.library_path()), reason="HIP library not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(api.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = moe.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = moe.load_library()
+    for st in range(6):
+        assert lib.moe_status_string(st)
+    assert lib.moe_version() >= 100
+
+
+def _dims(**kw):
+    base = dict(T=64, d=128, f=256, E=8, k=2, dtype=1)
+    base.update(kw)
+    return api._Dims(base["T"], base["d"], base["f"], base["E"], base["k"], base["dtype"])
+
+
+@pytest.mark.parametrize("bad", [dict(k=0), dict(k=9), dict(E=1025, k=2), dict(d=0), dict(f=0), dict(T=-1),
+                                 dict(dtype=7), dict(T=2**30, k=4)])
+def test_workspace_bytes_rejects_bad_dims(bad):
+    assert moe.load_library().moe_workspace_bytes(ctypes.byref(_dims(**bad))) == 0
+
+
+def test_workspace_bytes_grows_with_shape():
+    lib = moe.load_library()
+    a = lib.moe_workspace_bytes(ctypes.byref(_dims()))
+    b = lib.moe_workspace_bytes(ctypes.byref(_dims(T=128)))
+    assert 0 < a < b
+    # bf16 mixtral decode: h (512 x 16384) and y (512 x 6144) in bf16 dominate
+    c = lib.moe_workspace_bytes(ctypes.byref(_dims(T=256, d=6144, f=16384, E=8, k=2)))
+    assert c >= 512 * (16384 + 6144) * 2
+
+
+# Validation cases: each has one bad argument; the library must return its code
+# without launching. Skipped when a GPU is visible, so that a validation bug can
+# never turn into a launch with the placeholder pointers below.
+needs_no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="host-only validation test")
+A = 0x10000  # 16-byte aligned placeholder, never dereferenced
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("case,expect", [
+    ("null_x", 1), ("misaligned_x", 1), ("null_idx", 1), ("bad_k", 1), ("small_ws", 3), ("d_not_8", 2),
+])
+def test_route_validation(case, expect):
+    lib = moe.load_library()
+    dm = _dims(d=100 if case == "d_not_8" else 128, k=0 if case == "bad_k" else 2)
+    x = {"null_x": None, "misaligned_x": A + 2}.get(case, A)
+    idx = None if case == "null_idx" else A
+    ws, wsb = (A, 16) if case == "small_ws" else (A, 1 << 30)
+    st = lib.moe_route(ctypes.byref(dm), x, A, None, None, idx, A, ws, wsb, None)
+    assert st == expect
+
+
+@needs_no_gpu
+def test_layer_validation():
+    lib = moe.load_library()
+    ok = lambda **kw: lib.moe_layer_forward(ctypes.byref(_dims(**kw.pop("dims", {}))), *[kw.get(n, A) for n in (  # noqa: E731
+        "x", "wg")], kw.get("bias"), *[kw.get(n, A) for n in ("w1", "w3", "w2", "out")],
+        None, None, None, None, None, None, None, kw.get("ws", A), kw.get("wsb", 1 << 40), None)
+    assert ok(w2=None) == 1
+    assert ok(out=A + 8) == 1
+    assert ok(dims=dict(d=96)) == 2            # d % 64 != 0
+    assert ok(dims=dict(f=100)) == 2           # f % 64 != 0
+    assert ok(wsb=1024) == 3
+    assert ok(ws=None) == 3
+    assert ok(ws=A + 64) == 1                  # workspace must be 256-byte aligned
+    assert ok(dims=dict(T=0)) == 0             # empty batch: nothing to do
+
+
+@needs_no_gpu
+def test_permute_ffn_combine_validation():
+    lib = moe.load_library()
+    dm = _dims()
+    assert lib.moe_permute(ctypes.byref(dm), A, None, A, A, A, A, 1 << 30, None) == 1
+    assert lib.moe_permute(ctypes.byref(dm), A, A, A, A, A, A, 4, None) == 3
+    assert lib.moe_grouped_ffn(ctypes.byref(dm), A, A, A, A, A, A + 4, A, A, A, 1 << 30, None) == 1
+    assert lib.moe_grouped_ffn(ctypes.byref(_dims(f=96)), A, A, A, A, A, A, A, A, A, 1 << 30, None) == 2
+    assert lib.moe_combine(ctypes.byref(dm), A, A, A, None, None) == 1
+    assert lib.moe_combine(ctypes.byref(_dims(d=12)), A, A, A, A, None) == 2
+    assert lib.moe_timing_read(99, None, None) == 1

@@ -1,0 +1,180 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Bar: routing indices, counts, offsets, permutations and gate logits bit-exact;
+combine weights within 1e-5 relative; outputs within max |g - r| / max(|r|, rms(r))
+<= 2e-2. Small shapes are compared element by element over every output; the
+full-size workloads compare all routing arrays and a sample of output rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+import mixture_experts_layer_gate_amd as moe
+from conftest import to_numpy
+from parity import (OUT_TOL, LazyExperts, assert_routing_equal, gpu_float, host_inputs, oracle_routing,
+                    rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dims(cfg, T=None):
+    return moe.Dims(cfg.T if T is None else T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype)
+
+
+def _run_layer(cfg, inp):
+    dims = _dims(cfg, inp["x"].shape[0])
+    out, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                               return_routing=True)
+    torch.cuda.synchronize()
+    return out, r
+
+
+def _full_oracle_check(cfg, inp):
+    out, r = _run_layer(cfg, inp)
+    h = {n: to_numpy(v, cfg.dtype) for n, v in inp.items()}
+    ref = oracle.layer_forward(h["x"], h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], cfg.k, cfg.dtype)
+    assert_routing_equal(r, ref)
+    err = rel_err(gpu_float(out), ref["out"])
+    _say(f"  {cfg.name} T={inp['x'].shape[0]} out rel_err={err:.3e}")
+    assert err <= OUT_TOL
+    return out, r, ref
+
+
+def test_tiny_fp32_layer():
+    cfg = moe_inputs.config("tiny_fp32")
+    _say(f"case tiny_fp32 {cfg}")
+    inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    _full_oracle_check(cfg, inp)
+
+
+SMALL = [
+    # T, d, f, E, k, dtype, bias scale
+    (300, 256, 192, 8, 2, "bf16", 0.0),     # several m-blocks, ragged tails
+    (1, 128, 64, 4, 1, "bf16", 0.0),        # one token
+    (5, 64, 64, 1, 1, "bf16", 0.0),         # one expert: dense SwiGLU
+    (257, 512, 384, 64, 6, "bf16", 1.0),    # many experts, skew
+    (130, 192, 128, 16, 4, "bf16", 2.0),    # d not a multiple of 128
+    (1000, 128, 256, 256, 8, "bf16", 2.0),  # fine-grained, strong skew: idle experts
+    (700, 256, 320, 8, 8, "bf16", 0.0),     # k = E: every expert gets every token
+    (96, 128, 256, 8, 2, "f32", 1.5),       # fp32 path with skew
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_{}_s{}".format(*s))
+def test_small_shapes(shape):
+    T, d, f, E, k, dt, s = shape
+    _say(f"case small {shape}")
+    cfg = moe_inputs.LayerConfig("small", T, d, f, E, k, dt, s)
+    inp = moe_inputs.make_layer_inputs(cfg, 1, "cuda")
+    _full_oracle_check(cfg, inp)
+
+
+def test_forced_skew_all_tokens_to_k_experts():
+    cfg = moe_inputs.LayerConfig("forced", 520, 256, 192, 16, 3, "bf16", 0.0)
+    _say("case forced skew")
+    inp = moe_inputs.make_layer_inputs(cfg, 2, "cuda")
+    bias = torch.zeros(cfg.E, dtype=torch.float32)
+    bias[:cfg.k] = 1e4
+    inp["bias"] = bias.cuda()
+    out, r, ref = _full_oracle_check(cfg, inp)
+    assert r["counts"].cpu().tolist() == [cfg.T] * cfg.k + [0] * (cfg.E - cfg.k)
+
+
+def test_determinism_bitwise():
+    cfg = moe_inputs.LayerConfig("det", 777, 256, 256, 32, 4, "bf16", 1.0)
+    _say("case determinism")
+    inp = moe_inputs.make_layer_inputs(cfg, 3, "cuda")
+    o1, r1 = _run_layer(cfg, inp)
+    o2, r2 = _run_layer(cfg, inp)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n
+
+
+def test_stage_calls_match_layer_forward():
+    cfg = moe_inputs.LayerConfig("stages", 333, 256, 192, 8, 2, "bf16", 1.0)
+    _say("case stage calls")
+    inp = moe_inputs.make_layer_inputs(cfg, 4, "cuda")
+    dims = _dims(cfg)
+    out_l, r = _run_layer(cfg, inp)
+    logits, idx, w = moe.route(dims, inp["x"], inp["wg"], inp["bias"])
+    counts, offsets, perm, inv = moe.permute(dims, idx)
+    y = moe.grouped_ffn(dims, inp["x"], perm, counts, offsets, inp["w1"], inp["w3"], inp["w2"])
+    out = moe.combine(dims, y, inv, w)
+    torch.cuda.synchronize()
+    for a, b in ((logits, r["logits"]), (idx, r["topk_idx"]), (w, r["topk_w"]), (perm, r["perm"]),
+                 (inv, r["inv_perm"]), (counts, r["counts"])):
+        assert torch.equal(a, b)
+    assert torch.equal(out.view(torch.int16), out_l.view(torch.int16))
+
+
+def test_permute_on_given_indices():
+    """moe_permute on hand-made routing: all assignments to one expert, and a random one."""
+    T, E, k = 1500, 64, 4
+    _say("case permute given idx")
+    dims = moe.Dims(T, 128, 128, E, k)
+    rng = np.random.default_rng(7)
+    for idx_np in (np.tile(np.array([[5, 9, 0, 63]], np.int32), (T, 1)),
+                   np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)):
+        counts, offsets, perm, inv = moe.permute(dims, torch.from_numpy(idx_np).cuda())
+        torch.cuda.synchronize()
+        rc, ro, rp, ri = oracle.dispatch(idx_np, E)
+        assert np.array_equal(counts.cpu().numpy(), rc) and np.array_equal(offsets.cpu().numpy(), ro)
+        assert np.array_equal(perm.cpu().numpy(), rp) and np.array_equal(inv.cpu().numpy(), ri)
+
+
+def test_grouped_ffn_round_robin_routing():
+    """Exactly balanced synthetic routing e = (t*k + j) mod E fed to moe_grouped_ffn."""
+    cfg = moe_inputs.LayerConfig("rr", 256, 256, 320, 8, 2, "bf16", 0.0)
+    _say("case round robin ffn")
+    inp = moe_inputs.make_layer_inputs(cfg, 5, "cuda")
+    dims = _dims(cfg)
+    idx_np = (np.arange(cfg.T * cfg.k) % cfg.E).reshape(cfg.T, cfg.k).astype(np.int32)
+    counts, offsets, perm, inv = oracle.dispatch(idx_np, cfg.E)
+    y = moe.grouped_ffn(dims, inp["x"], torch.from_numpy(perm).cuda(), torch.from_numpy(counts).cuda(),
+                        torch.from_numpy(offsets).cuda(), inp["w1"], inp["w3"], inp["w2"])
+    torch.cuda.synchronize()
+    h = {n: to_numpy(v, cfg.dtype) for n, v in inp.items()}
+    ref = oracle.expert_ffn_sorted(h["x"], perm, offsets, h["w1"], h["w3"], h["w2"], cfg.k, cfg.dtype)
+    assert rel_err(gpu_float(y), ref) <= OUT_TOL
+
+
+# ---------------- full-size workloads ----------------
+FULL = ["mixtral_decode", "dbrx_bal", "dbrx_zipf", "mixtral_prefill_skew", "mixtral_prefill_bal",
+        "deepseek_skew", "deepseek_bal"]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    cfg = moe_inputs.config(name)
+    _say(f"case full {name}: generating inputs on the GPU")
+    inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    torch.cuda.synchronize()
+    _say("  running the layer")
+    out, r = _run_layer(cfg, inp)
+    h = host_inputs(inp, cfg.dtype)
+    _say("  oracle routing")
+    ref = oracle_routing(h, cfg.k, cfg.dtype)
+    assert_routing_equal(r, ref)
+    counts = ref["counts"]
+    _say(f"  routing bit-exact; counts min {counts.min()} max {counts.max()} active {(counts > 0).sum()}")
+    # sampled output rows: first, last and a spread, fewer when experts are many
+    nsamp = 8 if cfg.E > 64 else 24
+    toks = np.unique(np.linspace(0, cfg.T - 1, nsamp).astype(np.int64))
+    w1, w3, w2 = (LazyExperts(inp[n], cfg.dtype) for n in ("w1", "w3", "w2"))
+    ro = oracle.token_outputs(h["x"], ref["topk_idx"], ref["topk_w"], w1, w3, w2, toks, cfg.dtype)
+    got = gpu_float(out[torch.from_numpy(toks).cuda()])
+    err = rel_err(got, ro)
+    _say(f"  sampled out rel_err={err:.3e} over {toks.size} tokens")
+    assert err <= OUT_TOL
+    assert torch.isfinite(out.float()).all()
