@@ -33,8 +33,23 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = whole batch")
-    p.add_argument("--stage-report", action="store_true", help="also print per-stage kernel times to stderr")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run 5 device copies of 1 GiB (reference kernel for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_probe():
+    """Plain device-to-device copies of a known size; their FETCH_SIZE / WRITE_SIZE
+    counter readings scale the counters taken on the layer's kernels."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 5}), flush=True)
 
 
 def cpu_baseline(cfg, inp, ntok: int):
@@ -65,12 +80,41 @@ def cpu_baseline(cfg, inp, ntok: int):
                       f"of workload {cfg.name}, seed 0 inputs; {dt:.1f} s"}
 
 
+def kernel_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("mixture_experts_layer_gate_amd/csrc/ffn.hip", "mixture_experts_layer_gate_amd/csrc/common.h"):
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    the counters were taken on a different kernel source or workload."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_source_sha256()
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        rec = json.loads(line)
+        if rec.get("workload") == workload and rec.get("kernel") == kernel and rec.get("source_sha256") == sha:
+            return rec["traffic_bytes"]
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer runs on one MI355X)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     import torch
     import moe_inputs
     import mixture_experts_layer_gate_amd as moe
@@ -126,7 +170,7 @@ def main():
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, "fc1")
     roof["kernel"] = "grouped_gemm_kernel (FC1 + SiLU*mul)"
     roof["kernel_ms"] = round(fc1_ms, 4)
 
