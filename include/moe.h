@@ -35,7 +35,8 @@
  * - Assignment a = t*k + j (token t, slot j). Sorted position p orders the
  *   assignments by expert, then by a.
  * - Shape limits: T >= 0 (T = 0 is a no-op), d >= 1, f >= 1, 1 <= k <= E <= 1024,
- *   T*k < 2^31, T*E < 2^31. The GPU path needs d % 64 == 0 and f % 64 == 0
+ *   T*k < 2^31, T*E < 2^31. The GPU path needs d % 64 == 0 and f % 64 == 0,
+ *   and x (T*d), h (T*k*f) and one expert matrix (d*f) each under 4 GiB
  *   (MOE_ERR_UNSUPPORTED otherwise; moe_route alone accepts d % 8 == 0).
  *   Device pointers to bf16/fp32 tensors must be 16-byte aligned.
  * - Non-finite inputs give unspecified results.

@@ -155,7 +155,7 @@ hipError_t launch_scatter(const int32_t* idx, int64_t n, int E, int chunk, int n
 
 // ---------------------------------------------------------------------------
 // Tile plan: every expert's sorted rows cut into m-blocks of at most
-// kBlockRows rows, only the last one partial (MegaFlux, section 3.1).
+// block_rows rows, only the last one partial (MegaFlux, section 3.1).
 // m-blocks are listed in expert order: (expert, first sorted row, rows, 0).
 int64_t max_mblocks(int64_t n_assign, int E) {
   const int64_t active = n_assign < E ? n_assign : E;
@@ -167,14 +167,14 @@ int64_t max_mblocks(int64_t n_assign, int E) {
 // bounds (they give unspecified rows instead).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ offsets, int E,
-                                                    int64_t n_assign, int64_t max_mb,
+                                                    int64_t n_assign, int64_t max_mb, int block_rows,
                                                     int4* __restrict__ mblocks,
                                                     int32_t* __restrict__ n_mblocks) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
   const int64_t row0 = e < E ? min(max(static_cast<int64_t>(offsets[e]), int64_t(0)), n_assign) : 0;
   const int c = e < E ? static_cast<int>(min(max(static_cast<int64_t>(counts[e]), int64_t(0)), n_assign - row0)) : 0;
-  const int nb = (c + kBlockRows - 1) / kBlockRows;
+  const int nb = (c + block_rows - 1) / block_rows;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int incl = nb;
 #pragma unroll
@@ -189,17 +189,17 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   const int start = before + incl - nb;
   if (e < E) {
     for (int i = 0; i < nb && start + i < max_mb; ++i) {
-      const int r = min(kBlockRows, c - i * kBlockRows);
-      mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * kBlockRows, r, 0);
+      const int r = min(block_rows, c - i * block_rows);
+      mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * block_rows, r, 0);
     }
   }
   if (e == 1023) n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(before + incl), max_mb));
 }
 
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,
-                       int64_t max_mb, int4* mblocks, int32_t* n_mblocks, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, n_assign, max_mb, mblocks,
-                     n_mblocks);
+                       int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, n_assign, max_mb, block_rows,
+                     mblocks, n_mblocks);
   return hipGetLastError();
 }
 

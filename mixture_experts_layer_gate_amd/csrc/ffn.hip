@@ -13,6 +13,11 @@
 // are gathered through perm (FC1) or read contiguously (FC2). Tiles are taken
 // from a persistent loop over (n-block, m-block) pairs; waves whose 32-row
 // sub-blocks lie entirely past the block's rows skip their MFMAs.
+#include <stdlib.h>
+
+#include <algorithm>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -22,7 +27,7 @@ constexpr int kBM = 128;     // rows per tile (== kBlockRows)
 constexpr int kBNW = 128;    // weight rows per tile
 constexpr int kBK = 64;      // K per step
 constexpr int kThreads = 256;
-static_assert(kBM == kBlockRows, "tile rows must match the plan's block rows");
+static_assert(kBM == kBlockRows, "small-tile rows must match the plan's smallest block rows");
 
 struct GemmArgs {
   const void* A;          // FC1: x [T][K]; FC2: h [T*k][K]
@@ -235,16 +240,331 @@ __global__ __launch_bounds__(kThreads, kDtype == 1 ? 2 : 1) void grouped_gemm_ke
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile variant for experts with many rows: tile BM x BN, K step BK,
+// NST LDS stages filled by buffer loads straight into LDS
+// (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at M0 + 16 * i), one
+// barrier per K step, loads for step kt + NST - 1 issued while step kt
+// computes. 4 waves as WM x WN, each (BM/WM) x (BN/WN) with 32x32x16 bf16
+// MFMAs; fragments are double-buffered across the 16-wide K sub-steps.
+// LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits in slot
+// c ^ f(r), f(r) = (r / R256) mod CPR with R256 = rows per 256 bytes. gfx950's
+// LDS has 64 four-byte banks, so a 16-byte-per-lane read is conflict-free when
+// every 16 consecutive lanes (16 consecutive rows of a fragment) touch 16
+// distinct 16-byte units of a 256-byte line; f spreads them exactly so. The
+// swizzle is applied on the load side: the lane filling slot c' of row r
+// fetches chunk c' ^ f(r).
+// Per-tile buffer descriptors give 32-bit row offsets, keep the K advance in
+// the scalar offset, and return zeros outside the tensor (num_records).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Scheduling pattern for M MFMAs and R LDS reads in one basic block: groups of
+// about M/R MFMAs, each followed by one LDS read.
+template <int M, int R, int... I>
+__device__ __forceinline__ void interleave_mfma_ds(std::integer_sequence<int, I...>) {
+  static_assert(M >= R, "at least one MFMA per LDS read");
+  ((__builtin_amdgcn_sched_group_barrier(0x008, ((I + 1) * M) / R - (I * M) / R, 0),
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0)),
+   ...);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() carries: that fence
+// makes the compiler wait for every outstanding load, including the LDS stages
+// still being prefetched. LDS readiness is handled by explicit vmcnt waits
+// before the barrier; the empty asm keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool kGated, int BM, int BN, int WM, int WN, int BK, int NST, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
+  // device-only body: the buffer-resource builtins have no host form, and the
+  // host pass only needs the kernel's launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int RB = BK * 2;               // bytes per LDS row
+  constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;            // rows per load instruction
+  constexpr int R256 = 16 / CPR;           // rows per 256 bytes
+  static_assert(CPR == 4 || CPR == 8, "BK of 32 or 64");
+  constexpr int STAGE = (BM + BN) * RB;
+  constexpr int AI = BM / (4 * RPI);       // A load instructions per wave per stage
+  constexpr int BI = BN / (4 * RPI);       // B load instructions per wave per stage
+  constexpr int LPS = AI + BI;             // loads per thread per stage
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int MI = TM / 32, NJ = TN / 32;
+  constexpr int KS = BK / 16;              // MFMA sub-steps per stage
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(NST >= 3, "stage kt+1 must be in flight before step kt starts");
+  static_assert(!kGated || (NJ % 2 == 0), "gated tiles pair gate and up blocks");
+  static_assert(AI * 4 * RPI == BM && BI * 4 * RPI == BN, "load tiling");
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
+  const int wm = wv / WN, wn = wv % WN;
+  const int64_t K = g.K, N = g.N;
+  const int nmb = g.n_mblocks[0];
+  const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
+  const int64_t ntiles = static_cast<int64_t>(nmb) * nbc;
+  const int nk = static_cast<int>(K / BK);
+  constexpr int GM = 8;  // m-blocks per group in the tile order
+  const int lrow = lane / CPR;                                          // row within a load instruction
+  // Chunk this lane fetches for a load instruction whose first row is R0.
+  // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
+  // and R0 / R256 mod CPR is 0 for 64-byte rows and 0 or 4 for 128-byte rows
+  // (alternating with the instruction index, which the code passes in).
+  auto chunk_off = [&](int r0_phase) -> uint32_t {
+    return static_cast<uint32_t>(((lane % CPR) ^ ((r0_phase + lrow / R256) % CPR)) * 16);
+  };
+  constexpr int PH = (RPI / R256) % CPR;  // phase step per load instruction (0 or 4)
+  const int fsw = ((lane & 31) / R256) % CPR;                           // read-side swizzle of row (lane & 31)
+  // x spans T*K*2 bytes (< 2^32, checked on the host)
+  const uint32_t a_bytes = kGated ? static_cast<uint32_t>(g.T * K * 2) : 0u;
+
+  // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+  // b % 8). Renumber so that the gridDim/8 workgroups of one XCD take
+  // consecutive tiles of each round, which share A and B blocks in that XCD's L2.
+  const int G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int64_t tile = slot; tile < ntiles; tile += G) {
+    const int64_t grp = tile / (static_cast<int64_t>(GM) * nbc);
+    const int64_t o = tile % (static_cast<int64_t>(GM) * nbc);
+    const int gm_n = static_cast<int>(min(static_cast<int64_t>(GM), nmb - grp * GM));
+    const int mb = static_cast<int>(grp * GM + o % gm_n);
+    const int nb = static_cast<int>(o / gm_n);
+    const int4 blk = g.mblocks[mb];
+    const int e = __builtin_amdgcn_readfirstlane(blk.x);
+    const int row0 = __builtin_amdgcn_readfirstlane(blk.y);
+    const int rows = __builtin_amdgcn_readfirstlane(blk.z);
+
+    // A: FC1 gathers token rows of x; FC2 reads rows row0.. of h.
+    __amdgpu_buffer_rsrc_t ars;
+    uint32_t aoff[AI];
+    if constexpr (kGated) {
+      ars = make_rsrc(g.A, a_bytes);
+#pragma unroll
+      for (int i = 0; i < AI; ++i) {
+        const int r = (wv * AI + i) * RPI + lrow;
+        const int rr = row0 + (r < rows ? r : 0);
+        int64_t tok = g.perm[rr] / g.ktop;
+        tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
+        aoff[i] = static_cast<uint32_t>(tok * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
+      }
+    } else {
+      ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(row0) * K * 2,
+                      static_cast<uint32_t>(static_cast<int64_t>(rows) * K * 2));
+#pragma unroll
+      for (int i = 0; i < AI; ++i) {
+        const int r = (wv * AI + i) * RPI + lrow;
+        aoff[i] = static_cast<uint32_t>((r < rows ? r : 0) * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
+      }
+    }
+    // B: weight rows of expert e (gated: first half W1, second half W3, same columns).
+    __amdgpu_buffer_rsrc_t brs0, brs1;
+    uint32_t boff[BI];
+    {
+      const int64_t ebytes = N * K * 2;
+      brs0 = make_rsrc(static_cast<const char*>(g.B0) + e * ebytes, static_cast<uint32_t>(ebytes));
+      brs1 = kGated ? make_rsrc(static_cast<const char*>(g.B1) + e * ebytes, static_cast<uint32_t>(ebytes)) : brs0;
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int r = (wv * BI + i) * RPI + lrow;
+        int64_t n;
+        if constexpr (kGated)
+          n = static_cast<int64_t>(nb) * (BN / 2) + (r % (BN / 2));
+        else
+          n = static_cast<int64_t>(nb) * BN + r;
+        if (n >= N) n = N - 1;  // column tail: computed on a valid row, never stored
+        boff[i] = static_cast<uint32_t>(n * K * 2) + chunk_off(((wv * BI + i) * PH) % CPR);
+      }
+    }
+
+    f32x16_t acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto issue = [&](int stage, int kt) {
+      char* sa = lds + stage * STAGE;
+      char* sb = sa + BM * RB;
+      const uint32_t koff = static_cast<uint32_t>(kt) * RB;
+#pragma unroll
+      for (int i = 0; i < AI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ars, (__attribute__((address_space(3))) void*)(sa + (wv * AI + i) * 1024), 16, aoff[i], koff, 0, 0);
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            second ? brs1 : brs0, (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024), 16,
+            boff[i], koff, 0, 0);
+      }
+    };
+
+    // Fragments of one stage live in registers, one set per 16-wide sub-step.
+    // Sub-step s of stage kt runs its MFMAs, then the same registers are
+    // refilled with sub-step s of stage kt+1, overlapping the MFMAs of the
+    // next sub-step; the MFMA stream never waits on an LDS read of its own stage.
+    bf16x8_t fa[KS][MI], fb[KS][NJ];
+    auto read_sub = [&](int s, int stage) {
+      const char* sa = lds + stage * STAGE;
+      const char* sb = sa + BM * RB;
+      const int ck = (((2 * s + (lane >> 5)) ^ fsw) % CPR) * 16;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        fa[s][i] = *reinterpret_cast<const bf16x8_t*>(sa + (wm * TM + 32 * i + (lane & 31)) * RB + ck);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        int brow;
+        if constexpr (kGated)
+          brow = (j < NJ / 2 ? 0 : BN / 2) + wn * (TN / 2) + 32 * (j % (NJ / 2)) + (lane & 31);
+        else
+          brow = wn * TN + 32 * j + (lane & 31);
+        fb[s][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow * RB + ck);
+      }
+    };
+
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+      if (st < nk) issue(st, st);
+    // stage 0 landed (later prologue stages may still be in flight)
+    if (nk - 1 >= NST - 2) wait_vmcnt<(NST - 2) * LPS>();
+    else if (NST > 3 && nk - 1 == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) read_sub(s, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) {
+        // stage kt+1 landed: at most min(NST-3, nk-2-kt) later stages may be outstanding
+        const int later = nk - 2 - kt;
+        if constexpr (NST >= 4) {
+          if (later >= NST - 3) wait_vmcnt<(NST - 3) * LPS>();
+          else wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        // every wave's copy of stage kt+1 is in LDS, and every wave's MFMAs have
+        // consumed stage kt-1 (its slot is refilled next)
+        lds_barrier();
+        if (kt + NST - 1 < nk) issue((kt + NST - 1) % NST, kt + NST - 1);
+      }
+      const int nxt = (kt + 1) % NST;  // read on the last step too (unused), to keep one block
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+        read_sub(s, nxt);
+      }
+      interleave_mfma_ds<KS * MI * NJ, KS * (MI + NJ)>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue through LDS: every wave writes its fragment values (bf16) into a
+    // row-major [BM][CW] tile, then all threads store whole 16-byte row chunks.
+    constexpr int CW = kGated ? BN / 2 : BN;  // output columns of the tile
+    static_assert(BM * CW * 2 <= NST * STAGE, "epilogue tile fits in the stage buffers");
+    lds_barrier();
+    bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * TM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if constexpr (kGated) {
+#pragma unroll
+          for (int j = 0; j < NJ / 2; ++j) {
+            const int c = wn * (TN / 2) + 32 * j + (lane & 31);
+            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + NJ / 2][v])));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int c = wn * TN + 32 * j + (lane & 31);
+            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    {
+      bf16_t* C = static_cast<bf16_t*>(g.C);
+      const int64_t col0 = static_cast<int64_t>(nb) * CW;
+      constexpr int VPR = CW / 8;  // 16-byte vectors per tile row
+      for (int q = tid; q < rows * VPR; q += kThreads) {
+        const int r = q / VPR, c8 = (q % VPR) * 8;
+        if (col0 + c8 < N)
+          *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
+              *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
+      }
+    }
+    __syncthreads();  // the tile buffer is read out before the next tile's loads refill the stages
+  }
+#endif
+}
+
 static int persistent_grid(int64_t max_tiles) {
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
   int64_t g = max_tiles < cap ? max_tiles : cap;
   return static_cast<int>(g < 1 ? 1 : g);
 }
 
-hipError_t launch_fc1(int dtype, const void* x, const int32_t* perm, int k, int64_t T,
+constexpr int kBigBK = 32, kBigNST = 4;  // 256 x 256 tiles: 4 stages of 32 KB
+constexpr int kMidBK = 32, kMidNST = 4;  // 128 x 256 tiles: 4 stages of 24 KB
+constexpr int kTallBK = 32, kTallNST = 3; // 256 x 128 tiles: 3 stages of 24 KB, two workgroups per CU
+
+int choose_gemm_regime(int64_t T, int k, int E) {
+  if (const char* env = getenv("MOE_GEMM_REGIME")) {
+    const int r = atoi(env);
+    if (r >= 0 && r <= 3) return r;
+  }
+  const int64_t mean_rows = (T * k) / E;
+  if (mean_rows >= 256) return 2;
+  if (mean_rows >= 96) return 1;
+  return 0;
+}
+
+int regime_block_rows(int regime) { return regime >= 2 ? 256 : 128; }
+
+hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f};
+  if (dtype == 1 && regime == 2) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 256, 2, 2, kBigBK, kBigNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && regime == 3) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 63) / 64), 2 * device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 128, 2, 2, kTallBK, kTallNST, 2>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && regime == 1) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<true, 128, 256, 1, 4, kMidBK, kMidNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -253,9 +573,24 @@ hipError_t launch_fc1(int dtype, const void* x, const int32_t* perm, int k, int6
   return hipGetLastError();
 }
 
-hipError_t launch_fc2(int dtype, const void* h, const void* w2, void* y, const int4* mblocks,
+hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d};
+  if (dtype == 1 && regime == 2) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 256, 2, 2, kBigBK, kBigNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && regime == 3) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 127) / 128), 2 * device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 128, 2, 2, kTallBK, kTallNST, 2>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && regime == 1) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<false, 128, 256, 1, 4, kMidBK, kMidNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);

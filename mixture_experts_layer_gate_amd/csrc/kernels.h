@@ -5,7 +5,8 @@
 
 namespace moe {
 
-// Rows per m-block of the grouped GEMM (tile-aligned token blocks).
+// Smallest rows per m-block of the grouped GEMM (tile-aligned token blocks);
+// the large-tile regime uses 256.
 constexpr int kBlockRows = 128;
 
 // Gate logits l[t][e] in the fixed fp32 order. Requires d % 8 == 0.
@@ -24,16 +25,21 @@ hipError_t launch_scan(int32_t* block_hist, int n_chunks, int E, int32_t* counts
 hipError_t launch_scatter(const int32_t* idx, int64_t n, int E, int chunk, int n_chunks,
                           const int32_t* block_base, int32_t* perm, int32_t* inv_perm, hipStream_t s);
 
-// Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most kBlockRows rows.
+// Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most block_rows rows.
 int64_t max_mblocks(int64_t n_assign, int E);
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,
-                       int64_t max_mb, int4* mblocks, int32_t* n_mblocks, hipStream_t s);
+                       int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s);
 
-// Grouped GEMMs over the m-block list.
-hipError_t launch_fc1(int dtype, const void* x, const int32_t* perm, int k, int64_t T,
+// Grouped GEMMs over the m-block list. regime: 0 = 128x128 tiles, register-staged
+// (few rows per expert, weight streaming); 1 = 128x256 tiles, direct-to-LDS;
+// 2 = 256x256 tiles, direct-to-LDS (many rows per expert); 3 = 256x128 tiles,
+// direct-to-LDS, two workgroups per CU.
+int choose_gemm_regime(int64_t T, int k, int E);
+int regime_block_rows(int regime);
+hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
-hipError_t launch_fc2(int dtype, const void* h, const void* w2, void* y, const int4* mblocks,
+hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
 
 // Weighted combine.

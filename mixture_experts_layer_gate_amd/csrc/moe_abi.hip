@@ -168,17 +168,19 @@ int do_permute(const moe_dims_t* dm, const int32_t* idx, int32_t* counts, int32_
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
            const FfnWs& fw, hipStream_t s) {
+  const int regime = dm->dtype == MOE_DTYPE_BF16 ? choose_gemm_regime(dm->T, dm->k, dm->E) : 0;
   {
     StageScope sc(MOE_STAGE_PLAN, s);
-    if (int st = hip_status(launch_plan(counts, offsets, dm->E, dm->T * dm->k, fw.max_mb, fw.mblocks, fw.n_mblocks, s))) return st;
+    if (int st = hip_status(launch_plan(counts, offsets, dm->E, dm->T * dm->k, fw.max_mb, regime_block_rows(regime),
+                                        fw.mblocks, fw.n_mblocks, s))) return st;
   }
   {
     StageScope sc(MOE_STAGE_FC1, s);
-    if (int st = hip_status(launch_fc1(dm->dtype, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
+    if (int st = hip_status(launch_fc1(dm->dtype, regime, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
                                        fw.n_mblocks, fw.max_mb, dm->d, dm->f, s))) return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
-  return hip_status(launch_fc2(dm->dtype, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb, dm->d, dm->f, s));
+  return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb, dm->d, dm->f, s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
@@ -188,7 +190,12 @@ int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const fl
 }
 
 int ffn_shape_ok(const moe_dims_t* dm) {
-  return (dm->d % 64 == 0 && dm->f % 64 == 0) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+  if (dm->d % 64 != 0 || dm->f % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  // the GEMM addresses x, h rows and one expert's weights with 32-bit byte offsets
+  const int64_t lim = int64_t(1) << 32, eb = elt_bytes(dm);
+  if (dm->T * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || dm->T * dm->k * dm->f * eb >= lim)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -204,7 +211,7 @@ const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID: return "invalid argument (null or misaligned pointer, or shape outside the limits)";
-    case MOE_ERR_UNSUPPORTED: return "shape not supported by the GPU path (needs d % 64 == 0 and f % 64 == 0)";
+    case MOE_ERR_UNSUPPORTED: return "shape not supported by the GPU path (needs d % 64 == 0, f % 64 == 0, and x, h and one expert matrix under 4 GiB)";
     case MOE_ERR_WORKSPACE: return "workspace too small (see moe_workspace_bytes)";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     default: return "unknown status";

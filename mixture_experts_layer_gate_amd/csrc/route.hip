@@ -9,26 +9,40 @@
 // the 64 class sums are then combined by a butterfly with offsets
 // 32,16,8,4,2,1 (s_j += s_{j+off} for j < off); the bias is added last.
 //
-// Work mapping: a group of 8 threads owns a register tile of RT tokens x RE
-// experts; thread q of the group owns the 8 lane classes 8q..8q+7 and loads
-// them as one 16-byte vector per row per 64-element step. The butterfly's
-// first three levels (offsets 32, 16, 8) cross threads of the group
-// (lane distance 4, 2, 1); the last three stay inside a thread.
+// Work mapping: a group of 64/G lanes owns a register tile of RT tokens x RE
+// experts; lane q of the group owns the G consecutive lane classes
+// G*q .. G*q+G-1 and loads them as one vector per row per 64-element step.
+// Butterfly levels with offset >= G cross lanes of the group (lane distance
+// off/G); the smaller ones stay inside a thread. Small batches use G = 1 (64
+// lanes per logit) so that enough waves run; large ones use G = 8 and a
+// register tile.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <int kDtype>
-__device__ __forceinline__ void load8(const void* base, int64_t elem_off, float (&v)[8]) {
+// G consecutive elements as fp32 (G = 1, 2, 4 or 8; 2*G bytes for bf16, 4*G for fp32).
+template <int kDtype, int G>
+__device__ __forceinline__ void loadG(const void* base, int64_t elem_off, float (&v)[G]) {
   if constexpr (kDtype == 1) {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(base) + elem_off);
-    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+    const bf16_t* p = static_cast<const bf16_t*>(base) + elem_off;
+    if constexpr (G == 8) {
+      const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(u[i]); v[2 * i + 1] = bf16_hi(u[i]); }
+    } else if constexpr (G == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    } else if constexpr (G == 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = bf16_lo(u); v[1] = bf16_hi(u);
+    } else {
+      v[0] = __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const float* p = static_cast<const float*>(base) + elem_off;
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = p[i];
   }
 }
 
@@ -46,14 +60,20 @@ __device__ __forceinline__ float mac(float x, float w, float acc) {
   }
 }
 
-template <int kDtype, int RT, int RE>
+// A group of TPP = 64/G lanes owns a register tile of RT tokens x RE experts;
+// lane q of the group owns the G consecutive lane classes G*q .. G*q+G-1.
+// The K loop is unrolled by U steps of 64 elements so that U loads per row
+// are in flight before the (ordered) accumulation consumes them.
+template <int kDtype, int G, int RT, int RE>
 __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict__ x,
                                                           const void* __restrict__ wg,
                                                           const float* __restrict__ bias,
                                                           float* __restrict__ logits, int T, int d,
                                                           int E, int n_eb, int64_t n_pb) {
-  const int q = threadIdx.x & 7;
-  const int64_t pb = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 3);
+  constexpr int TPP = 64 / G;
+  constexpr int U = G == 8 ? 2 : 8;
+  const int q = threadIdx.x % TPP;
+  const int64_t pb = static_cast<int64_t>(blockIdx.x) * (256 / TPP) + threadIdx.x / TPP;
   const bool live = pb < n_pb;
   const int64_t pbc = live ? pb : 0;
   const int tb = static_cast<int>(pbc / n_eb), eb = static_cast<int>(pbc % n_eb);
@@ -64,70 +84,86 @@ __global__ __launch_bounds__(256) void gate_logits_kernel(const void* __restrict
 #pragma unroll
   for (int r = 0; r < RE; ++r) wrow[r] = static_cast<int64_t>(min(eb * RE + r, E - 1)) * d;
 
-  float acc[RT][RE][8];
+  float acc[RT][RE][G];
 #pragma unroll
   for (int a = 0; a < RT; ++a)
 #pragma unroll
     for (int b = 0; b < RE; ++b)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) acc[a][b][r] = 0.0f;
+      for (int r = 0; r < G; ++r) acc[a][b][r] = 0.0f;
 
-  for (int i0 = q * 8; i0 < d; i0 += 64) {
-    float xv[RT][8], wv[RE][8];
+  int i0 = q * G;
+  // full batches of U steps: all loads first, then the FMAs in order
+  for (; i0 + (U - 1) * 64 < d; i0 += U * 64) {
+    float xv[U][RT][G], wv[U][RE][G];
 #pragma unroll
-    for (int a = 0; a < RT; ++a) load8<kDtype>(x, xrow[a] + i0, xv[a]);
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-    for (int b = 0; b < RE; ++b) load8<kDtype>(wg, wrow[b] + i0, wv[b]);
+      for (int a = 0; a < RT; ++a) loadG<kDtype, G>(x, xrow[a] + i0 + u * 64, xv[u][a]);
+#pragma unroll
+      for (int b = 0; b < RE; ++b) loadG<kDtype, G>(wg, wrow[b] + i0 + u * 64, wv[u][b]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int b = 0; b < RE; ++b)
+#pragma unroll
+          for (int r = 0; r < G; ++r) acc[a][b][r] = mac<kDtype>(xv[u][a][r], wv[u][b][r], acc[a][b][r]);
+  }
+  for (; i0 < d; i0 += 64) {
+    float xv[RT][G], wv[RE][G];
+#pragma unroll
+    for (int a = 0; a < RT; ++a) loadG<kDtype, G>(x, xrow[a] + i0, xv[a]);
+#pragma unroll
+    for (int b = 0; b < RE; ++b) loadG<kDtype, G>(wg, wrow[b] + i0, wv[b]);
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
       for (int b = 0; b < RE; ++b)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) acc[a][b][r] = mac<kDtype>(xv[a][r], wv[b][r], acc[a][b][r]);
+        for (int r = 0; r < G; ++r) acc[a][b][r] = mac<kDtype>(xv[a][r], wv[b][r], acc[a][b][r]);
   }
 
-  // Butterfly. Class j = 8q + r. Offsets 32, 16, 8 pair thread q with q+4, q+2, q+1.
+  // Butterfly over class j = G*q + r: offsets >= G pair lane q with q + off/G,
+  // smaller offsets stay inside the thread.
 #pragma unroll
   for (int a = 0; a < RT; ++a)
 #pragma unroll
-    for (int b = 0; b < RE; ++b)
+    for (int b = 0; b < RE; ++b) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        float s = acc[a][b][r];
-        s = s + __shfl_down(s, 4, 8);
-        s = s + __shfl_down(s, 2, 8);
-        s = s + __shfl_down(s, 1, 8);
-        acc[a][b][r] = s;
-      }
+      for (int off = 32; off >= G; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < G; ++r) acc[a][b][r] = acc[a][b][r] + __shfl_down(acc[a][b][r], off / G, TPP);
+#pragma unroll
+      for (int off = G / 2; off >= 1; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < off; ++r) acc[a][b][r] = acc[a][b][r] + acc[a][b][r + off];
+    }
   if (!live || q != 0) return;
 #pragma unroll
   for (int a = 0; a < RT; ++a)
 #pragma unroll
     for (int b = 0; b < RE; ++b) {
-      float s[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) s[r] = acc[a][b][r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] = s[r] + s[r + 4];
-      s[0] = s[0] + s[2];
-      s[1] = s[1] + s[3];
-      s[0] = s[0] + s[1];
       const int t = tb * RT + a, e = eb * RE + b;
       if (t < T && e < E) {
         const float bv = bias ? bias[e] : 0.0f;
-        logits[static_cast<int64_t>(t) * E + e] = s[0] + bv;
+        logits[static_cast<int64_t>(t) * E + e] = acc[a][b][0] + bv;
       }
     }
 }
 
-template <int kDtype, int RT, int RE>
+template <int kDtype, int G, int RT, int RE>
 static hipError_t gate_launch(const void* x, const void* wg, const float* bias, float* logits,
                               int64_t T, int64_t d, int E, hipStream_t s) {
+  constexpr int TPP = 64 / G;
   const int n_tb = static_cast<int>((T + RT - 1) / RT);
   const int n_eb = (E + RE - 1) / RE;
   const int64_t n_pb = static_cast<int64_t>(n_tb) * n_eb;
-  const int64_t blocks = (n_pb + 31) / 32;
-  hipLaunchKernelGGL((gate_logits_kernel<kDtype, RT, RE>), dim3(static_cast<unsigned>(blocks)),
+  const int64_t per_block = 256 / TPP;
+  const int64_t blocks = (n_pb + per_block - 1) / per_block;
+  hipLaunchKernelGGL((gate_logits_kernel<kDtype, G, RT, RE>), dim3(static_cast<unsigned>(blocks)),
                      dim3(256), 0, s, x, wg, bias, logits, static_cast<int>(T), static_cast<int>(d),
                      E, n_eb, n_pb);
   return hipGetLastError();
@@ -136,17 +172,20 @@ static hipError_t gate_launch(const void* x, const void* wg, const float* bias, 
 template <int kDtype>
 static hipError_t gate_dispatch(const void* x, const void* wg, const float* bias, float* logits,
                                 int64_t T, int64_t d, int E, hipStream_t s) {
-  // Largest register tile that still gives >= 2048 waves (8 per CU); tiles no
-  // wider than E in the expert direction.
-  auto waves = [&](int rt, int re) {
+  // Most work per thread (wide loads, big register tile) that still gives
+  // >= 2048 waves (8 per CU); otherwise the narrowest mapping.
+  auto waves = [&](int g, int rt, int re) {
     const int64_t pbs = ((T + rt - 1) / rt) * ((E + re - 1) / re);
-    return pbs * 8 / kWave;
+    return pbs * (64 / g) / kWave;
   };
   const int64_t want = 2048;
-  if (E >= 4 && waves(2, 4) >= want) return gate_launch<kDtype, 2, 4>(x, wg, bias, logits, T, d, E, s);
-  if (E >= 2 && waves(2, 2) >= want) return gate_launch<kDtype, 2, 2>(x, wg, bias, logits, T, d, E, s);
-  if (E >= 2 && waves(1, 2) >= want) return gate_launch<kDtype, 1, 2>(x, wg, bias, logits, T, d, E, s);
-  return gate_launch<kDtype, 1, 1>(x, wg, bias, logits, T, d, E, s);
+  if (E >= 4 && waves(8, 2, 4) >= want) return gate_launch<kDtype, 8, 2, 4>(x, wg, bias, logits, T, d, E, s);
+  if (E >= 2 && waves(8, 2, 2) >= want) return gate_launch<kDtype, 8, 2, 2>(x, wg, bias, logits, T, d, E, s);
+  if (E >= 2 && waves(8, 1, 2) >= want) return gate_launch<kDtype, 8, 1, 2>(x, wg, bias, logits, T, d, E, s);
+  if (waves(8, 1, 1) >= want) return gate_launch<kDtype, 8, 1, 1>(x, wg, bias, logits, T, d, E, s);
+  if (waves(4, 1, 1) >= want) return gate_launch<kDtype, 4, 1, 1>(x, wg, bias, logits, T, d, E, s);
+  if (waves(2, 1, 1) >= want) return gate_launch<kDtype, 2, 1, 1>(x, wg, bias, logits, T, d, E, s);
+  return gate_launch<kDtype, 1, 1, 1>(x, wg, bias, logits, T, d, E, s);
 }
 
 hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const float* bias,

@@ -148,6 +148,26 @@ def test_grouped_ffn_round_robin_routing():
     assert rel_err(gpu_float(y), ref) <= OUT_TOL
 
 
+REGIME_SHAPES = [
+    # T, d, f, E, k, bias scale
+    (600, 256, 384, 4, 2, 1.5),   # hot expert spans several 256-row blocks, ragged tails
+    (300, 320, 192, 8, 3, 0.0),   # column tails in FC1 (f=192) and FC2 (d=320)
+    (64, 128, 128, 2, 1, 0.0),    # one block per expert
+]
+
+
+@pytest.mark.parametrize("regime", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", REGIME_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
+def test_each_gemm_tile_regime(monkeypatch, regime, shape):
+    """Every grouped-GEMM tile configuration (forced through MOE_GEMM_REGIME) matches the oracle."""
+    T, d, f, E, k, s = shape
+    _say(f"case regime {regime} {shape}")
+    monkeypatch.setenv("MOE_GEMM_REGIME", str(regime))
+    cfg = moe_inputs.LayerConfig("regime", T, d, f, E, k, "bf16", s)
+    inp = moe_inputs.make_layer_inputs(cfg, 6, "cuda")
+    _full_oracle_check(cfg, inp)
+
+
 # ---------------- full-size workloads ----------------
 FULL = ["mixtral_decode", "dbrx_bal", "dbrx_zipf", "mixtral_prefill_skew", "mixtral_prefill_bal",
         "deepseek_skew", "deepseek_bal"]
