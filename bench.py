@@ -143,7 +143,9 @@ def main():
     counts = r["counts"].cpu().tolist()
     torch.cuda.synchronize()
 
-    moe.timing_enable(args.steps)
+    # Timed region: events only around the dominant kernel (FC1), on the
+    # stream it is launched on.
+    moe.timing_enable(args.steps, stages=["fc1"])
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -154,7 +156,16 @@ def main():
     moe.timing_disable()
     total_ms = ev0.elapsed_time(ev1)
     ms = total_ms / args.steps
+    fc1_rec = moe.timing_read("fc1")
+    # Per-stage breakdown from a separate, untimed pass with every stage recorded.
+    nbreak = min(args.steps, 5)
+    moe.timing_enable(nbreak)
+    for _ in range(nbreak):
+        step()
+    torch.cuda.synchronize()
+    moe.timing_disable()
     stages = {s: moe.timing_read(s) for s in moe.STAGES}
+    stages["fc1"] = fc1_rec
 
     elt = 2 if cfg.dtype == "bf16" else 4
     n = cfg.T * cfg.k
@@ -197,7 +208,7 @@ def main():
                   "bound": rf.classify(layer_flops, layer_bytes).bound,
                   "floor_ms": round(rf.classify(layer_flops, layer_bytes).floor_s * 1e3, 4),
                   "kappa": round(rf.kappa(counts), 3), "active_experts": rf.active_experts(counts)},
-        "stages_ms": {s: round(v[0] / max(v[1], 1), 4) for s, v in stages.items()},
+        "stages_ms": {s: round(v[0] / max(v[1], 1), 4) for s, v in stages.items() if v[1] > 0},
     }
     if not args.no_cpu_baseline:
         ntok = cfg.T if args.cpu_sample_tokens <= 0 else min(cfg.T, args.cpu_sample_tokens)

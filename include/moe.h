@@ -154,11 +154,13 @@ enum {
   MOE_STAGE_FC1 = 6,      /* grouped FC1 + SiLU*mul */
   MOE_STAGE_FC2 = 7,      /* grouped FC2 */
   MOE_STAGE_COMBINE = 8,  /* weighted combine */
-  MOE_NUM_STAGES = 9
+  MOE_STAGE_DISPATCH = 9, /* single-workgroup histogram + scan + scatter (+ tile plan) */
+  MOE_NUM_STAGES = 10
 };
-/* Start recording; `capacity` = launches per stage to keep (host memory only).
- * Discards earlier records. */
-int moe_timing_enable(int capacity);
+/* Start recording; `capacity` = launches per stage to keep (host memory only);
+ * `stage_mask` = bit s set records stage s (0 = every stage). Discards
+ * earlier records. */
+int moe_timing_enable(int capacity, unsigned stage_mask);
 /* Stop recording (records are kept until the next enable). */
 int moe_timing_disable(void);
 /* Synchronises on the recorded events of `stage` and returns the summed

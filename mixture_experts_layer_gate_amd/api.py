@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmoe_amd.so"
 
-STAGES = ["gate", "topk", "hist", "scan", "scatter", "plan", "fc1", "fc2", "combine"]
+STAGES = ["gate", "topk", "hist", "scan", "scatter", "plan", "fc1", "fc2", "combine", "dispatch"]
 MOE_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 # Every symbol include/moe.h declares.
@@ -79,7 +79,7 @@ def load_library():
     lib.moe_grouped_ffn.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P]
     lib.moe_layer_forward.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
-    lib.moe_timing_enable.argtypes = [ctypes.c_int]
+    lib.moe_timing_enable.argtypes = [ctypes.c_int, ctypes.c_uint]
     lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read"):
@@ -225,8 +225,10 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
     return (out, r) if return_routing else out
 
 
-def timing_enable(capacity: int):
-    _check("moe_timing_enable", load_library().moe_timing_enable(capacity))
+def timing_enable(capacity: int, stages=None):
+    """Record HIP events around the library's kernel launches (stages: names, None = all)."""
+    mask = 0 if stages is None else sum(1 << STAGES.index(st) for st in stages)
+    _check("moe_timing_enable", load_library().moe_timing_enable(capacity, mask))
 
 
 def timing_disable():

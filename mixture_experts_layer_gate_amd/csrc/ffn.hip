@@ -262,6 +262,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            static_cast<int>(bytes), 0x00020000);
 }
 
+// Scheduling pattern for M MFMAs, R LDS reads and V global loads in one basic
+// block: R groups of about M/R MFMAs, each followed by one LDS read, with the
+// V loads spread over the first V groups.
+template <int M, int R, int V, int... I>
+__device__ __forceinline__ void interleave_mfma_ds_vmem(std::integer_sequence<int, I...>) {
+  static_assert(M >= R && R >= V, "at least one MFMA per LDS read, one LDS read per load");
+  ((__builtin_amdgcn_sched_group_barrier(0x008, ((I + 1) * M) / R - (I * M) / R, 0),
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0),
+    __builtin_amdgcn_sched_group_barrier(0x020, ((I + 1) * V) / R - (I * V) / R, 0)),
+   ...);
+}
+
 // Scheduling pattern for M MFMAs and R LDS reads in one basic block: groups of
 // about M/R MFMAs, each followed by one LDS read.
 template <int M, int R, int... I>
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
   constexpr int MI = TM / 32, NJ = TN / 32;
   constexpr int KS = BK / 16;              // MFMA sub-steps per stage
   static_assert(WM * WN == 4, "four waves");
-  static_assert(NST >= 3, "stage kt+1 must be in flight before step kt starts");
+  static_assert(NST >= 2, "at least double buffering");
   static_assert(!kGated || (NJ % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(AI * 4 * RPI == BM && BI * 4 * RPI == BN, "load tiling");
   __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
@@ -400,20 +412,27 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    // Loads of K step kt into LDS slot `stage`. Steps past the end load from an
+    // empty descriptor (zeros, no memory access) into a slot nobody reads
+    // again, so every step issues the same number of loads and the issue can
+    // sit in the same basic block as the MFMAs.
+    const __amdgpu_buffer_rsrc_t nul = make_rsrc(g.B0, 0u);
     auto issue = [&](int stage, int kt) {
+      const bool real = kt < nk;
       char* sa = lds + stage * STAGE;
       char* sb = sa + BM * RB;
-      const uint32_t koff = static_cast<uint32_t>(kt) * RB;
+      const uint32_t koff = real ? static_cast<uint32_t>(kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < AI; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ars, (__attribute__((address_space(3))) void*)(sa + (wv * AI + i) * 1024), 16, aoff[i], koff, 0, 0);
+            real ? ars : nul, (__attribute__((address_space(3))) void*)(sa + (wv * AI + i) * 1024), 16, aoff[i],
+            koff, 0, 0);
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
         const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            second ? brs1 : brs0, (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024), 16,
-            boff[i], koff, 0, 0);
+            real ? (second ? brs1 : brs0) : nul, (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024),
+            16, boff[i], koff, 0, 0);
       }
     };
 
@@ -440,44 +459,57 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
       }
     };
 
+    if constexpr (NST >= 3) {
 #pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
-      if (st < nk) issue(st, st);
-    // stage 0 landed (later prologue stages may still be in flight)
-    if (nk - 1 >= NST - 2) wait_vmcnt<(NST - 2) * LPS>();
-    else if (NST > 3 && nk - 1 == 1) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
-    lds_barrier();
+      for (int st = 0; st < NST - 1; ++st) issue(st, st);
+      wait_vmcnt<(NST - 2) * LPS>();  // stage 0 landed; NST-2 later stages may be in flight
+      lds_barrier();
 #pragma unroll
-    for (int s = 0; s < KS; ++s) read_sub(s, 0);
+      for (int s = 0; s < KS; ++s) read_sub(s, 0);
 
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) {
-        // stage kt+1 landed: at most min(NST-3, nk-2-kt) later stages may be outstanding
-        const int later = nk - 2 - kt;
-        if constexpr (NST >= 4) {
-          if (later >= NST - 3) wait_vmcnt<(NST - 3) * LPS>();
-          else wait_vmcnt<0>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        // every wave's copy of stage kt+1 is in LDS, and every wave's MFMAs have
-        // consumed stage kt-1 (its slot is refilled next)
+      for (int kt = 0; kt < nk; ++kt) {
+        // Stage kt+1 landed (exactly NST-3 later stages, real or empty, are
+        // issued after it); every wave has consumed stage kt-1 in its MFMAs.
+        wait_vmcnt<(NST - 3 >= 0 ? NST - 3 : 0) * LPS>();
         lds_barrier();
-        if (kt + NST - 1 < nk) issue((kt + NST - 1) % NST, kt + NST - 1);
+        issue((kt + NST - 1) % NST, kt + NST - 1);
+        const int nxt = (kt + 1) % NST;  // read on the last step too (unused), to keep one block
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+          read_sub(s, nxt);
+        }
+        interleave_mfma_ds_vmem<KS * MI * NJ, KS * (MI + NJ), LPS>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const int nxt = (kt + 1) % NST;  // read on the last step too (unused), to keep one block
+    } else {
+      // Double buffering: stage kt+1 loads while stage kt computes; fragments
+      // are read within the step, one sub-step ahead of its MFMAs.
+      issue(0, 0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        wait_vmcnt<0>();  // this wave's loads of stage kt landed
+        // every wave's copy of stage kt is in LDS and every wave is done with
+        // stage kt-1, whose slot is refilled next
+        lds_barrier();
+        issue(cur ^ 1, kt + 1);
+        read_sub(0, cur);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KS; ++s) {
+          if (s + 1 < KS) read_sub(s + 1, cur);
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+          for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-        read_sub(s, nxt);
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+        }
+        interleave_mfma_ds_vmem<KS * MI * NJ, KS * (MI + NJ), LPS>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
+        __builtin_amdgcn_sched_barrier(0);
       }
-      interleave_mfma_ds<KS * MI * NJ, KS * (MI + NJ)>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     // Epilogue through LDS: every wave writes its fragment values (bf16) into a
@@ -532,15 +564,15 @@ static int persistent_grid(int64_t max_tiles) {
 constexpr int kBigBK = 32, kBigNST = 4;  // 256 x 256 tiles: 4 stages of 32 KB
 constexpr int kMidBK = 32, kMidNST = 4;  // 128 x 256 tiles: 4 stages of 24 KB
 constexpr int kTallBK = 32, kTallNST = 3; // 256 x 128 tiles: 3 stages of 24 KB, two workgroups per CU
+constexpr int kWideBK = 64, kWideNST = 2; // 256 x 256 tiles: 2 stages of 64 KB (full 128-byte rows)
 
 int choose_gemm_regime(int64_t T, int k, int E) {
   if (const char* env = getenv("MOE_GEMM_REGIME")) {
     const int r = atoi(env);
-    if (r >= 0 && r <= 3) return r;
+    if (r >= 0 && r <= 4) return r;
   }
   const int64_t mean_rows = (T * k) / E;
-  if (mean_rows >= 256) return 2;
-  if (mean_rows >= 96) return 1;
+  if (mean_rows >= 96) return 2;
   return 0;
 }
 
@@ -553,6 +585,11 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
   if (dtype == 1 && regime == 2) {
     const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
     hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 256, 2, 2, kBigBK, kBigNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && regime == 4) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 256, 2, 2, kWideBK, kWideNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (dtype == 1 && regime == 3) {
@@ -579,6 +616,11 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
   if (dtype == 1 && regime == 2) {
     const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
     hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 256, 2, 2, kBigBK, kBigNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (dtype == 1 && regime == 4) {
+    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
+    hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 256, 2, 2, kWideBK, kWideNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   if (dtype == 1 && regime == 3) {

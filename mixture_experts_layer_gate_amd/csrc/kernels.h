@@ -25,6 +25,13 @@ hipError_t launch_scan(int32_t* block_hist, int n_chunks, int E, int32_t* counts
 hipError_t launch_scatter(const int32_t* idx, int64_t n, int E, int chunk, int n_chunks,
                           const int32_t* block_base, int32_t* perm, int32_t* inv_perm, hipStream_t s);
 
+// Single-workgroup dispatch (+ tile plan when mblocks != nullptr) for
+// n <= kFusedMaxAssign assignments.
+constexpr int64_t kFusedMaxAssign = 65536;
+hipError_t launch_dispatch_fused(const int32_t* idx, int64_t n, int E, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv_perm, int block_rows, int64_t max_mb,
+                                 int4* mblocks, int32_t* n_mblocks, hipStream_t s);
+
 // Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most block_rows rows.
 int64_t max_mblocks(int64_t n_assign, int E);
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,

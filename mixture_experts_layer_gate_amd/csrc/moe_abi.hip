@@ -35,6 +35,7 @@ struct Timing {
   std::mutex mu;
   bool on = false;
   int cap = 0;
+  unsigned mask = 0xffffffffu;
   std::vector<hipEvent_t> ev[MOE_NUM_STAGES][2];
   int n[MOE_NUM_STAGES] = {0};
 } g_timing;
@@ -44,7 +45,7 @@ struct StageScope {
   hipStream_t s;
   int slot = -1;
   StageScope(int st, hipStream_t stream) : stage(st), s(stream) {
-    if (!g_timing.on) return;
+    if (!g_timing.on || !((g_timing.mask >> stage) & 1u)) return;
     if (g_timing.n[stage] < g_timing.cap) {
       slot = g_timing.n[stage]++;
       (void)hipEventRecord(g_timing.ev[stage][0][slot], s);
@@ -153,6 +154,10 @@ int do_route(const moe_dims_t* dm, const void* x, const void* wg, const float* b
 int do_permute(const moe_dims_t* dm, const int32_t* idx, int32_t* counts, int32_t* offsets,
                int32_t* perm, int32_t* inv, const PermuteWs& pw, hipStream_t s) {
   const int64_t n = dm->T * dm->k;
+  if (n <= kFusedMaxAssign) {
+    StageScope sc(MOE_STAGE_DISPATCH, s);
+    return hip_status(launch_dispatch_fused(idx, n, dm->E, counts, offsets, perm, inv, 0, 0, nullptr, nullptr, s));
+  }
   {
     StageScope sc(MOE_STAGE_HIST, s);
     if (int st = hip_status(launch_hist(idx, n, dm->E, pw.chunk, pw.n_chunks, pw.block_hist, s))) return st;
@@ -165,11 +170,15 @@ int do_permute(const moe_dims_t* dm, const int32_t* idx, int32_t* counts, int32_
   return hip_status(launch_scatter(idx, n, dm->E, pw.chunk, pw.n_chunks, pw.block_hist, perm, inv, s));
 }
 
+int gemm_regime(const moe_dims_t* dm) {
+  return dm->dtype == MOE_DTYPE_BF16 ? choose_gemm_regime(dm->T, dm->k, dm->E) : 0;
+}
+
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
-           const FfnWs& fw, hipStream_t s) {
-  const int regime = dm->dtype == MOE_DTYPE_BF16 ? choose_gemm_regime(dm->T, dm->k, dm->E) : 0;
-  {
+           const FfnWs& fw, hipStream_t s, bool planned = false) {
+  const int regime = gemm_regime(dm);
+  if (!planned) {
     StageScope sc(MOE_STAGE_PLAN, s);
     if (int st = hip_status(launch_plan(counts, offsets, dm->E, dm->T * dm->k, fw.max_mb, regime_block_rows(regime),
                                         fw.mblocks, fw.n_mblocks, s))) return st;
@@ -308,16 +317,29 @@ int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const
   if (!inv_perm) inv_perm = lw.inv;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
-  PermuteWs pw{};
-  permute_ws(dm, lw.sub, &pw);
-  if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
+  const int64_t n = dm->T * dm->k;
   FfnWs fw{};
   ffn_ws(dm, lw.sub, &fw);
-  if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s)) return st;
+  if (n <= kFusedMaxAssign) {
+    // histogram, scan, scatter and tile plan in one launch
+    {
+      StageScope sc(MOE_STAGE_DISPATCH, s);
+      if (int st = hip_status(launch_dispatch_fused(topk_idx, n, dm->E, counts, offsets, perm, inv_perm,
+                                                    regime_block_rows(gemm_regime(dm)), fw.max_mb, fw.mblocks,
+                                                    fw.n_mblocks, s)))
+        return st;
+    }
+    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, true)) return st;
+  } else {
+    PermuteWs pw{};
+    permute_ws(dm, lw.sub, &pw);
+    if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
+    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s)) return st;
+  }
   return do_combine(dm, lw.y, inv_perm, topk_w, out, s);
 }
 
-int moe_timing_enable(int capacity) {
+int moe_timing_enable(int capacity, unsigned stage_mask) {
   if (capacity < 1 || capacity > (1 << 20)) return MOE_ERR_INVALID;
   std::lock_guard<std::mutex> lk(g_timing.mu);
   for (int st = 0; st < MOE_NUM_STAGES; ++st)
@@ -330,6 +352,7 @@ int moe_timing_enable(int capacity) {
       }
     }
   g_timing.cap = capacity;
+  g_timing.mask = stage_mask ? stage_mask : 0xffffffffu;
   for (int st = 0; st < MOE_NUM_STAGES; ++st) g_timing.n[st] = 0;
   g_timing.on = true;
   return MOE_OK;

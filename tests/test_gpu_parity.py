@@ -66,6 +66,7 @@ SMALL = [
     (1000, 128, 256, 256, 8, "bf16", 2.0),  # fine-grained, strong skew: idle experts
     (700, 256, 320, 8, 8, "bf16", 0.0),     # k = E: every expert gets every token
     (96, 128, 256, 8, 2, "f32", 1.5),       # fp32 path with skew
+    (9000, 128, 128, 64, 8, "bf16", 1.0),   # > 65536 assignments: multi-kernel dispatch + plan
 ]
 
 
@@ -119,12 +120,14 @@ def test_stage_calls_match_layer_forward():
 
 def test_permute_on_given_indices():
     """moe_permute on hand-made routing: all assignments to one expert, and a random one."""
-    T, E, k = 1500, 64, 4
     _say("case permute given idx")
-    dims = moe.Dims(T, 128, 128, E, k)
     rng = np.random.default_rng(7)
-    for idx_np in (np.tile(np.array([[5, 9, 0, 63]], np.int32), (T, 1)),
-                   np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)):
+    cases = []
+    for T, E, k in ((1500, 64, 4), (20000, 64, 4)):  # single-workgroup path and multi-kernel path
+        cases.append((T, E, k, np.tile(np.array([[5, 9, 0, 63]], np.int32), (T, 1))))
+        cases.append((T, E, k, np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)))
+    for T, E, k, idx_np in cases:
+        dims = moe.Dims(T, 128, 128, E, k)
         counts, offsets, perm, inv = moe.permute(dims, torch.from_numpy(idx_np).cuda())
         torch.cuda.synchronize()
         rc, ro, rp, ri = oracle.dispatch(idx_np, E)
@@ -156,7 +159,7 @@ REGIME_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("regime", [0, 1, 2, 3])
+@pytest.mark.parametrize("regime", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("shape", REGIME_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
 def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     """Every grouped-GEMM tile configuration (forced through MOE_GEMM_REGIME) matches the oracle."""
