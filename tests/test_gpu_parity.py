@@ -67,6 +67,7 @@ SMALL = [
     (700, 256, 320, 8, 8, "bf16", 0.0),     # k = E: every expert gets every token
     (96, 128, 256, 8, 2, "f32", 1.5),       # fp32 path with skew
     (9000, 128, 128, 64, 8, "bf16", 1.0),   # > 65536 assignments: multi-kernel dispatch + plan
+    (64, 4096, 2048, 8, 2, "bf16", 0.0),    # decode-shaped: wide d and f, few rows per expert
 ]
 
 
@@ -159,7 +160,7 @@ REGIME_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("regime", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("regime", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("shape", REGIME_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
 def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     """Every grouped-GEMM tile configuration (forced through MOE_GEMM_REGIME) matches the oracle."""
