@@ -160,7 +160,7 @@ REGIME_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("regime", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("regime", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("shape", REGIME_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
 def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     """Every grouped-GEMM tile configuration (forced through MOE_GEMM_REGIME) matches the oracle."""
