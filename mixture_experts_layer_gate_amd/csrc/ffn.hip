@@ -242,11 +242,16 @@ __global__ __launch_bounds__(kThreads, kDtype == 1 ? 2 : 1) void grouped_gemm_ke
 
 // ---------------------------------------------------------------------------
 // Large-tile variant for experts with many rows: tile BM x BN, K step BK,
-// NST LDS stages filled by buffer loads straight into LDS
+// a ring of NST LDS stages filled by buffer loads straight into LDS
 // (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at M0 + 16 * i), one
-// barrier per K step, loads for step kt + NST - 1 issued while step kt
-// computes. 4 waves as WM x WN, each (BM/WM) x (BN/WN) with 32x32x16 bf16
-// MFMAs; fragments are double-buffered across the 16-wide K sub-steps.
+// barrier per K step, the loads of step kt + NST - 1 issued during step kt.
+// WM x WN waves (4 or 8), each (BM/WM) x (BN/WN) with 32x32x16 bf16 MFMAs.
+// A step's MFMAs run on fragments read during the previous step; the reads
+// of the next stage and the step's loads are interleaved with the MFMAs in
+// one scheduling block, so neither an LDS read nor a load issue stalls the
+// MFMA stream. Measured on the Mixtral-8x22B prefill FC1: with the global
+// loads switched off the same loop runs at the MFMA ceiling; with them on,
+// the L1-to-L2 request rate (64-byte row segments) is what limits it.
 // LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits in slot
 // c ^ f(r), f(r) = (r / R256) mod CPR with R256 = rows per 256 bytes. gfx950's
 // LDS has 64 four-byte banks, so a 16-byte-per-lane read is conflict-free when
@@ -274,16 +279,6 @@ __device__ __forceinline__ void interleave_mfma_ds_vmem(std::integer_sequence<in
    ...);
 }
 
-// Scheduling pattern for M MFMAs and R LDS reads in one basic block: groups of
-// about M/R MFMAs, each followed by one LDS read.
-template <int M, int R, int... I>
-__device__ __forceinline__ void interleave_mfma_ds(std::integer_sequence<int, I...>) {
-  static_assert(M >= R, "at least one MFMA per LDS read");
-  ((__builtin_amdgcn_sched_group_barrier(0x008, ((I + 1) * M) / R - (I * M) / R, 0),
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0)),
-   ...);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -302,7 +297,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <bool kGated, int BM, int BN, int WM, int WN, int BK, int NST, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) {
   // device-only body: the buffer-resource builtins have no host form, and the
   // host pass only needs the kernel's launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -312,16 +307,18 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
   constexpr int R256 = 16 / CPR;           // rows per 256 bytes
   static_assert(CPR == 4 || CPR == 8, "BK of 32 or 64");
   constexpr int STAGE = (BM + BN) * RB;
-  constexpr int AI = BM / (4 * RPI);       // A load instructions per wave per stage
-  constexpr int BI = BN / (4 * RPI);       // B load instructions per wave per stage
+  constexpr int NW = WM * WN;              // waves per workgroup
+  constexpr int NT = 64 * NW;              // threads per workgroup
+  constexpr int AI = BM / (NW * RPI);      // A load instructions per wave per stage
+  constexpr int BI = BN / (NW * RPI);      // B load instructions per wave per stage
   constexpr int LPS = AI + BI;             // loads per thread per stage
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MI = TM / 32, NJ = TN / 32;
   constexpr int KS = BK / 16;              // MFMA sub-steps per stage
-  static_assert(WM * WN == 4, "four waves");
-  static_assert(NST >= 2, "at least double buffering");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NST >= 3, "stage kt+1 must be in flight before step kt starts");
   static_assert(!kGated || (NJ % 2 == 0), "gated tiles pair gate and up blocks");
-  static_assert(AI * 4 * RPI == BM && BI * 4 * RPI == BN, "load tiling");
+  static_assert(AI * NW * RPI == BM && BI * NW * RPI == BN, "load tiling");
   __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -459,57 +456,31 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
       }
     };
 
-    if constexpr (NST >= 3) {
 #pragma unroll
-      for (int st = 0; st < NST - 1; ++st) issue(st, st);
-      wait_vmcnt<(NST - 2) * LPS>();  // stage 0 landed; NST-2 later stages may be in flight
-      lds_barrier();
+    for (int st = 0; st < NST - 1; ++st) issue(st, st);
+    wait_vmcnt<(NST - 2) * LPS>();  // stage 0 landed; NST-2 later stages may be in flight
+    lds_barrier();
 #pragma unroll
-      for (int s = 0; s < KS; ++s) read_sub(s, 0);
+    for (int s = 0; s < KS; ++s) read_sub(s, 0);
 
-      for (int kt = 0; kt < nk; ++kt) {
-        // Stage kt+1 landed (exactly NST-3 later stages, real or empty, are
-        // issued after it); every wave has consumed stage kt-1 in its MFMAs.
-        wait_vmcnt<(NST - 3 >= 0 ? NST - 3 : 0) * LPS>();
-        lds_barrier();
-        issue((kt + NST - 1) % NST, kt + NST - 1);
-        const int nxt = (kt + 1) % NST;  // read on the last step too (unused), to keep one block
+    for (int kt = 0; kt < nk; ++kt) {
+      // Stage kt+1 landed (exactly NST-3 later stages, real or empty, are
+      // issued after it); every wave has consumed stage kt-1 in its MFMAs.
+      wait_vmcnt<(NST - 3) * LPS>();
+      lds_barrier();
+      issue((kt + NST - 1) % NST, kt + NST - 1);
+      const int nxt = (kt + 1) % NST;  // read on the last step too (unused), to keep one block
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+      for (int s = 0; s < KS; ++s) {
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-          read_sub(s, nxt);
-        }
-        interleave_mfma_ds_vmem<KS * MI * NJ, KS * (MI + NJ), LPS>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
-        __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+        read_sub(s, nxt);
       }
-    } else {
-      // Double buffering: stage kt+1 loads while stage kt computes; fragments
-      // are read within the step, one sub-step ahead of its MFMAs.
-      issue(0, 0);
-      for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        wait_vmcnt<0>();  // this wave's loads of stage kt landed
-        // every wave's copy of stage kt is in LDS and every wave is done with
-        // stage kt-1, whose slot is refilled next
-        lds_barrier();
-        issue(cur ^ 1, kt + 1);
-        read_sub(0, cur);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          if (s + 1 < KS) read_sub(s + 1, cur);
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-        }
-        interleave_mfma_ds_vmem<KS * MI * NJ, KS * (MI + NJ), LPS>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      interleave_mfma_ds_vmem<KS * MI * NJ, KS * (MI + NJ), LPS>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // Epilogue through LDS: every wave writes its fragment values (bf16) into a
@@ -543,7 +514,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dl_kernel(GemmArgs g) {
       bf16_t* C = static_cast<bf16_t*>(g.C);
       const int64_t col0 = static_cast<int64_t>(nb) * CW;
       constexpr int VPR = CW / 8;  // 16-byte vectors per tile row
-      for (int q = tid; q < rows * VPR; q += kThreads) {
+      for (int q = tid; q < rows * VPR; q += NT) {
         const int r = q / VPR, c8 = (q % VPR) * 8;
         if (col0 + c8 < N)
           *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
@@ -561,47 +532,36 @@ static int persistent_grid(int64_t max_tiles) {
   return static_cast<int>(g < 1 ? 1 : g);
 }
 
-constexpr int kBigBK = 32, kBigNST = 4;  // 256 x 256 tiles: 4 stages of 32 KB
-constexpr int kMidBK = 32, kMidNST = 4;  // 128 x 256 tiles: 4 stages of 24 KB
-constexpr int kTallBK = 32, kTallNST = 3; // 256 x 128 tiles: 3 stages of 24 KB, two workgroups per CU
-constexpr int kWideBK = 64, kWideNST = 2; // 256 x 256 tiles: 2 stages of 64 KB (full 128-byte rows)
+constexpr int kBigBK = 32, kBigNST = 4;  // 256 x 256 tiles: 4 stages of 32 KB (128 KB of LDS)
 
 int choose_gemm_regime(int64_t T, int k, int E) {
   if (const char* env = getenv("MOE_GEMM_REGIME")) {
     const int r = atoi(env);
-    if (r >= 0 && r <= 4) return r;
+    if (r >= 0 && r <= 2) return r;
   }
   const int64_t mean_rows = (T * k) / E;
-  if (mean_rows >= 96) return 2;
-  return 0;
+  return mean_rows >= 96 ? 2 : 0;
 }
 
-int regime_block_rows(int regime) { return regime >= 2 ? 256 : 128; }
+int regime_block_rows(int regime) { return regime >= 1 ? 256 : 128; }
+
+// Large-tile launch: one workgroup per CU (the four 32 KB stages take 128 KB
+// of the CU's 160 KB LDS), persistent over the tile list.
+template <bool kGated, int WM, int WN>
+static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, hipStream_t s) {
+  const int64_t nb = kGated ? (ncols + 127) / 128 : (ncols + 255) / 256;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, device_cu_count())));
+  hipLaunchKernelGGL((gemm_dl_kernel<kGated, 256, 256, WM, WN, kBigBK, kBigNST, 1>), dim3(grid), dim3(64 * WM * WN),
+                     0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f};
-  if (dtype == 1 && regime == 2) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 256, 2, 2, kBigBK, kBigNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (dtype == 1 && regime == 4) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 256, 2, 2, kWideBK, kWideNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (dtype == 1 && regime == 3) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 63) / 64), 2 * device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<true, 256, 128, 2, 2, kTallBK, kTallNST, 2>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (dtype == 1 && regime == 1) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((f + 127) / 128), device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<true, 128, 256, 1, 4, kMidBK, kMidNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
+  if (dtype == 1 && regime == 2) return launch_big<true, 2, 4>(a, max_mb, f, s);
+  if (dtype == 1 && regime == 1) return launch_big<true, 2, 2>(a, max_mb, f, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -613,26 +573,8 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d};
-  if (dtype == 1 && regime == 2) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 256, 2, 2, kBigBK, kBigNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (dtype == 1 && regime == 4) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 256, 2, 2, kWideBK, kWideNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (dtype == 1 && regime == 3) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 127) / 128), 2 * device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<false, 256, 128, 2, 2, kTallBK, kTallNST, 2>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  if (dtype == 1 && regime == 1) {
-    const int grid = static_cast<int>(std::min<int64_t>(max_mb * ((d + 255) / 256), device_cu_count()));
-    hipLaunchKernelGGL((gemm_dl_kernel<false, 128, 256, 1, 4, kMidBK, kMidNST, 1>), dim3(std::max(grid, 1)), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-  }
+  if (dtype == 1 && regime == 2) return launch_big<false, 2, 4>(a, max_mb, d, s);
+  if (dtype == 1 && regime == 1) return launch_big<false, 2, 2>(a, max_mb, d, s);
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);

@@ -16,6 +16,9 @@
 // off/G); the smaller ones stay inside a thread. Small batches use G = 1 (64
 // lanes per logit) so that enough waves run; large ones use G = 8 and a
 // register tile.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -172,13 +175,24 @@ static hipError_t gate_launch(const void* x, const void* wg, const float* bias, 
 template <int kDtype>
 static hipError_t gate_dispatch(const void* x, const void* wg, const float* bias, float* logits,
                                 int64_t T, int64_t d, int E, hipStream_t s) {
-  // Most work per thread (wide loads, big register tile) that still gives
-  // >= 2048 waves (8 per CU); otherwise the narrowest mapping.
+  // Most work per thread (big register tile, few conversions per FMA) that
+  // still gives >= 2048 waves (8 per CU); otherwise the narrowest mapping.
+  // On the 4096 x 7168 x 256 gate, tiles of 2 classes x 4 tokens x 8 experts
+  // measured fastest; tiles that force one wave per SIMD were slower.
   auto waves = [&](int g, int rt, int re) {
     const int64_t pbs = ((T + rt - 1) / rt) * ((E + re - 1) / re);
     return pbs * (64 / g) / kWave;
   };
   const int64_t want = 2048;
+  if (const char* env = getenv("MOE_GATE_CFG")) {  // tuning: "G,RT,RE" among the instantiated tiles
+    int g = 0, rt = 0, re = 0;
+    if (sscanf(env, "%d,%d,%d", &g, &rt, &re) == 3) {
+      if (g == 4 && rt == 4 && re == 4) return gate_launch<kDtype, 4, 4, 4>(x, wg, bias, logits, T, d, E, s);
+      if (g == 2 && rt == 4 && re == 8) return gate_launch<kDtype, 2, 4, 8>(x, wg, bias, logits, T, d, E, s);
+      if (g == 8 && rt == 2 && re == 4) return gate_launch<kDtype, 8, 2, 4>(x, wg, bias, logits, T, d, E, s);
+    }
+  }
+  if (E >= 8 && waves(2, 4, 8) >= want) return gate_launch<kDtype, 2, 4, 8>(x, wg, bias, logits, T, d, E, s);
   if (E >= 4 && waves(8, 2, 4) >= want) return gate_launch<kDtype, 8, 2, 4>(x, wg, bias, logits, T, d, E, s);
   if (E >= 2 && waves(8, 2, 2) >= want) return gate_launch<kDtype, 8, 2, 2>(x, wg, bias, logits, T, d, E, s);
   if (E >= 2 && waves(8, 1, 2) >= want) return gate_launch<kDtype, 8, 1, 2>(x, wg, bias, logits, T, d, E, s);

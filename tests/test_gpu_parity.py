@@ -160,7 +160,7 @@ REGIME_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("regime", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("regime", [0, 1, 2])
 @pytest.mark.parametrize("shape", REGIME_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
 def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     """Every grouped-GEMM tile configuration (forced through MOE_GEMM_REGIME) matches the oracle."""
@@ -170,6 +170,24 @@ def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     cfg = moe_inputs.LayerConfig("regime", T, d, f, E, k, "bf16", s)
     inp = moe_inputs.make_layer_inputs(cfg, 6, "cuda")
     _full_oracle_check(cfg, inp)
+
+
+@pytest.mark.parametrize("gate_cfg", ["8,2,4", "4,4,4", "2,4,8", ""])
+@pytest.mark.parametrize("shape", [(300, 200, 24), (77, 512, 8), (1000, 1024, 64)], ids=lambda s: "T{}_d{}_E{}".format(*s))
+def test_gate_tile_configs_bit_exact(monkeypatch, gate_cfg, shape):
+    """Every gate register-tile configuration (forced via MOE_GATE_CFG) gives the oracle's logits bit for bit."""
+    T, d, E = shape
+    _say(f"case gate cfg {gate_cfg} {shape}")
+    monkeypatch.setenv("MOE_GATE_CFG", gate_cfg)
+    cfg = moe_inputs.LayerConfig("gate", T, d, 64, E, 2, "bf16", 1.0)
+    inp = moe_inputs.make_layer_inputs(cfg, 8, "cuda")
+    dims = moe.Dims(T, d, 64, E, 2)
+    logits, idx, w = moe.route(dims, inp["x"], inp["wg"], inp["bias"])
+    torch.cuda.synchronize()
+    h = {n: to_numpy(inp[n], "bf16") for n in ("x", "wg", "bias")}
+    ref = oracle.gate_logits(h["x"], h["wg"], h["bias"], "bf16")
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(idx.cpu().numpy(), oracle.topk_select(ref, 2))
 
 
 # ---------------- full-size workloads ----------------
