@@ -241,17 +241,22 @@ __global__ __launch_bounds__(kThreads, kDtype == 1 ? 2 : 1) void grouped_gemm_ke
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile variant for experts with many rows: tile BM x BN, K step BK,
-// a ring of NST LDS stages filled by buffer loads straight into LDS
-// (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at M0 + 16 * i), one
-// barrier per K step, the loads of step kt + NST - 1 issued during step kt.
-// WM x WN waves (4 or 8), each (BM/WM) x (BN/WN) with 32x32x16 bf16 MFMAs.
-// A step's MFMAs run on fragments read during the previous step; the reads
-// of the next stage and the step's loads are interleaved with the MFMAs in
-// one scheduling block, so neither an LDS read nor a load issue stalls the
-// MFMA stream. Measured on the Mixtral-8x22B prefill FC1: with the global
-// loads switched off the same loop runs at the MFMA ceiling; with them on,
-// the L1-to-L2 request rate (64-byte row segments) is what limits it.
+// Large-tile variant for experts with many rows: tile BM x BN, K step 64,
+// LDS buffers filled by buffer loads straight into LDS (buffer_load_dwordx4
+// ... lds: lane i's 16 bytes land at M0 + 16 * i), 128-byte row segments.
+// WM x WN waves, each (BM/WM) x (BN/WN) with 32x32x16 bf16 MFMAs. A has two
+// LDS buffers, B three (2 x 32 + 3 x 32 KB: the CU's whole 160 KB). After
+// the third of the four 16-wide sub-steps of step kt every wave waits for
+// the loads of step kt+1 and meets at the one barrier of the step; step
+// kt's buffers are then free, and the loads of A for step kt+2 and of B for
+// step kt+3 go out at once (weights, mostly first touches from HBM, get the
+// longer lead). The last sub-step's MFMAs hide the LDS reads of step kt+1's
+// first sub-step. Fragments alternate between two register sets, one
+// sub-step ahead of the MFMAs, and scheduling groups interleave the reads
+// and the load issue with the MFMAs.
+// On the Mixtral-8x22B prefill FC1 the loop is power-bound: with the loads
+// on, the clock settles near 1.6 GHz (2.3 GHz without them), and in cycles
+// the kernel runs within about 15 % of the load-free loop.
 // LDS rows are BK*2 bytes; the 16-byte chunk c of row r sits in slot
 // c ^ f(r), f(r) = (r / R256) mod CPR with R256 = rows per 256 bytes. gfx950's
 // LDS has 64 four-byte banks, so a 16-byte-per-lane read is conflict-free when
@@ -268,14 +273,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // Scheduling pattern for M MFMAs, R LDS reads and V global loads in one basic
-// block: R groups of about M/R MFMAs, each followed by one LDS read, with the
-// V loads spread over the first V groups.
-template <int M, int R, int V, int... I>
+// block: max(M, R) groups, MFMAs and reads each spread evenly over them, the
+// loads spread over the first VG groups, MFMAs first in every group.
+template <int Msk, int Cnt>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (Cnt > 0) __builtin_amdgcn_sched_group_barrier(Msk, Cnt, 0);
+}
+template <int M, int R, int V, int VG, int... I>
 __device__ __forceinline__ void interleave_mfma_ds_vmem(std::integer_sequence<int, I...>) {
-  static_assert(M >= R && R >= V, "at least one MFMA per LDS read, one LDS read per load");
-  ((__builtin_amdgcn_sched_group_barrier(0x008, ((I + 1) * M) / R - (I * M) / R, 0),
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0),
-    __builtin_amdgcn_sched_group_barrier(0x020, ((I + 1) * V) / R - (I * V) / R, 0)),
+  constexpr int G = sizeof...(I);
+  static_assert(G == (M > R ? M : R) && VG >= 1 && VG <= G, "one group per MFMA or LDS read");
+  ((sched_group<0x008, ((I + 1) * M) / G - (I * M) / G>(), sched_group<0x100, ((I + 1) * R) / G - (I * R) / G>(),
+    sched_group<0x020, (I < VG ? ((I + 1) * V) / VG - (I * V) / VG : 0)>()),
    ...);
 }
 
@@ -284,6 +293,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+
+// Every LDS read of this wave has returned (lgkmcnt 0; vmcnt and expcnt left alone).
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Workgroup barrier without the memory fence __syncthreads() carries: that fence
 // makes the compiler wait for every outstanding load, including the LDS stages
@@ -296,17 +308,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kGated, int BM, int BN, int WM, int WN, int BK, int NST, int OCC>
-__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) {
+template <bool kGated, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   // device-only body: the buffer-resource builtins have no host form, and the
   // host pass only needs the kernel's launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BK = 64;                   // K per step
   constexpr int RB = BK * 2;               // bytes per LDS row
   constexpr int CPR = RB / 16;             // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;            // rows per load instruction
   constexpr int R256 = 16 / CPR;           // rows per 256 bytes
-  static_assert(CPR == 4 || CPR == 8, "BK of 32 or 64");
-  constexpr int STAGE = (BM + BN) * RB;
   constexpr int NW = WM * WN;              // waves per workgroup
   constexpr int NT = 64 * NW;              // threads per workgroup
   constexpr int AI = BM / (NW * RPI);      // A load instructions per wave per stage
@@ -316,10 +327,15 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) 
   constexpr int MI = TM / 32, NJ = TN / 32;
   constexpr int KS = BK / 16;              // MFMA sub-steps per stage
   static_assert(NW == 4 || NW == 8, "four or eight waves");
-  static_assert(NST >= 3, "stage kt+1 must be in flight before step kt starts");
   static_assert(!kGated || (NJ % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(AI * NW * RPI == BM && BI * NW * RPI == BN, "load tiling");
-  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+  // LDS: NBA A buffers, then NBB B buffers (a third B buffer when it fits
+  // in the CU's 160 KB, so weight loads run two steps ahead)
+  constexpr int A_ST = BM * RB, B_ST = BN * RB;
+  constexpr int NBA = 2;
+  constexpr int NBB = 2 * A_ST + 3 * B_ST <= 160 * 1024 ? 3 : 2;
+  constexpr int LDS_BYTES = NBA * A_ST + NBB * B_ST;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
@@ -359,7 +375,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) 
     const int row0 = __builtin_amdgcn_readfirstlane(blk.y);
     const int rows = __builtin_amdgcn_readfirstlane(blk.z);
 
-    // A: FC1 gathers token rows of x; FC2 reads rows row0.. of h.
+    // A: FC1 gathers token rows of x; FC2 reads rows row0.. of h. Rows past the
+    // block's end get an offset at the descriptor's size: the load returns zeros
+    // and makes no memory request.
     __amdgpu_buffer_rsrc_t ars;
     uint32_t aoff[AI];
     if constexpr (kGated) {
@@ -367,18 +385,21 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) 
 #pragma unroll
       for (int i = 0; i < AI; ++i) {
         const int r = (wv * AI + i) * RPI + lrow;
-        const int rr = row0 + (r < rows ? r : 0);
-        int64_t tok = g.perm[rr] / g.ktop;
-        tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
-        aoff[i] = static_cast<uint32_t>(tok * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
+        if (r < rows) {
+          int64_t tok = g.perm[row0 + r] / g.ktop;
+          tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
+          aoff[i] = static_cast<uint32_t>(tok * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
+        } else {
+          aoff[i] = a_bytes;
+        }
       }
     } else {
-      ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(row0) * K * 2,
-                      static_cast<uint32_t>(static_cast<int64_t>(rows) * K * 2));
+      const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * K * 2);
+      ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(row0) * K * 2, hb);
 #pragma unroll
       for (int i = 0; i < AI; ++i) {
         const int r = (wv * AI + i) * RPI + lrow;
-        aoff[i] = static_cast<uint32_t>((r < rows ? r : 0) * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
+        aoff[i] = r < rows ? static_cast<uint32_t>(r * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR) : hb;
       }
     }
     // B: weight rows of expert e (gated: first half W1, second half W3, same columns).
@@ -414,16 +435,20 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) 
     // again, so every step issues the same number of loads and the issue can
     // sit in the same basic block as the MFMAs.
     const __amdgpu_buffer_rsrc_t nul = make_rsrc(g.B0, 0u);
-    auto issue = [&](int stage, int kt) {
+    auto issue_a = [&](int slot, int kt) {
       const bool real = kt < nk;
-      char* sa = lds + stage * STAGE;
-      char* sb = sa + BM * RB;
+      char* sa = lds + slot * A_ST;
       const uint32_t koff = real ? static_cast<uint32_t>(kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < AI; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             real ? ars : nul, (__attribute__((address_space(3))) void*)(sa + (wv * AI + i) * 1024), 16, aoff[i],
             koff, 0, 0);
+    };
+    auto issue_b = [&](int slot, int kt) {
+      const bool real = kt < nk;
+      char* sb = lds + NBA * A_ST + slot * B_ST;
+      const uint32_t koff = real ? static_cast<uint32_t>(kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
         const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
@@ -432,19 +457,16 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) 
             16, boff[i], koff, 0, 0);
       }
     };
-
-    // Fragments of one stage live in registers, one set per 16-wide sub-step.
-    // Sub-step s of stage kt runs its MFMAs, then the same registers are
-    // refilled with sub-step s of stage kt+1, overlapping the MFMAs of the
-    // next sub-step; the MFMA stream never waits on an LDS read of its own stage.
-    bf16x8_t fa[KS][MI], fb[KS][NJ];
-    auto read_sub = [&](int s, int stage) {
-      const char* sa = lds + stage * STAGE;
-      const char* sb = sa + BM * RB;
+    // Only the wave's first MA 32-row blocks hold rows of the m-block; the
+    // others are padding, so their fragments are neither read nor multiplied
+    // (their accumulators stay zero and are never stored).
+    bf16x8_t fa[2][MI], fb[2][NJ];  // two fragment register sets
+    auto read_sub = [&](auto ma_c, int set, int s, int a_slot, int b_slot) {
+      constexpr int MA = decltype(ma_c)::value;
+      const char* sa = lds + a_slot * A_ST;
+      const char* sb = lds + NBA * A_ST + b_slot * B_ST;
       const int ck = (((2 * s + (lane >> 5)) ^ fsw) % CPR) * 16;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[s][i] = *reinterpret_cast<const bf16x8_t*>(sa + (wm * TM + 32 * i + (lane & 31)) * RB + ck);
+      // B first: the first MFMA of a sub-step needs fb[0] and fa[0]
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         int brow;
@@ -452,41 +474,88 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dl_kernel(GemmArgs g) 
           brow = (j < NJ / 2 ? 0 : BN / 2) + wn * (TN / 2) + 32 * (j % (NJ / 2)) + (lane & 31);
         else
           brow = wn * TN + 32 * j + (lane & 31);
-        fb[s][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow * RB + ck);
+        fb[set][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow * RB + ck);
       }
+#pragma unroll
+      for (int i = 0; i < MA; ++i)
+        fa[set][i] = *reinterpret_cast<const bf16x8_t*>(sa + (wm * TM + 32 * i + (lane & 31)) * RB + ck);
     };
 
+    auto mfmas = [&](auto ma_c, int set) {
+      constexpr int MA = decltype(ma_c)::value;
 #pragma unroll
-    for (int st = 0; st < NST - 1; ++st) issue(st, st);
-    wait_vmcnt<(NST - 2) * LPS>();  // stage 0 landed; NST-2 later stages may be in flight
-    lds_barrier();
+      for (int i = 0; i < MA; ++i)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) read_sub(s, 0);
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+    };
 
-    for (int kt = 0; kt < nk; ++kt) {
-      // Stage kt+1 landed (exactly NST-3 later stages, real or empty, are
-      // issued after it); every wave has consumed stage kt-1 in its MFMAs.
-      wait_vmcnt<(NST - 3) * LPS>();
+    auto kloop = [&](auto ma_c) {
+      constexpr int MA = decltype(ma_c)::value;
+      // fa/fb[set]: set s & 1 holds sub-step s of the current stage. Step j
+      // uses A buffer j & 1 and B buffer j % NBB; both are free once every
+      // wave passed step j's barrier (its reads are done by then), so the
+      // loads of A for step j+2 and of B for step j+NBB are issued right
+      // there. Issue order (vmcnt counts in order): B0 A0 [B1] A1 B(NBB-1),
+      // then A(j+2) B(j+NBB) at each step j.
+      issue_b(0, 0);
+      issue_a(0, 0);
+      if constexpr (NBB == 3) issue_b(1, 1);
+      issue_a(1, 1);
+      issue_b(NBB - 1, NBB - 1);
+      wait_vmcnt<(NBB == 3 ? AI + 2 * BI : AI + BI)>();  // A0 and B0 landed
       lds_barrier();
-      issue((kt + NST - 1) % NST, kt + NST - 1);
-      const int nxt = (kt + 1) % NST;  // read on the last step too (unused), to keep one block
+      if constexpr (MA > 0) read_sub(ma_c, 0, 0, 0, 0);
+      int bsl = 0;  // B buffer of step kt
+      for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const int bnx = bsl + 1 == NBB ? 0 : bsl + 1;
+        if constexpr (MA > 0) {
+          // one scheduling region per sub-step: its MFMAs (set s & 1) with
+          // the reads of sub-step s+1 (the other set)
+          constexpr int M = MA * NJ, R = MA + NJ, G = M > R ? M : R;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-        read_sub(s, nxt);
+          for (int s = 0; s < KS - 1; ++s) {
+            mfmas(ma_c, s & 1);
+            read_sub(ma_c, (s + 1) & 1, s + 1, cur, bsl);
+            interleave_mfma_ds_vmem<M, R, 0, 1>(std::make_integer_sequence<int, G>{});
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        wait_vmcnt<(NBB == 3 ? BI : 0)>();  // this thread's loads of step kt+1 landed
+        wait_lds_reads();  // and its reads of step kt's buffers are done: they may be refilled after the barrier
+        lds_barrier();
+        issue_a(cur, kt + 2);
+        issue_b(bsl, kt + NBB);
+        if constexpr (MA > 0) {
+          mfmas(ma_c, (KS - 1) & 1);
+          read_sub(ma_c, 0, 0, cur ^ 1, bnx);  // on the last step: zeros, unused
+          constexpr int M = MA * NJ, R = MA + NJ, G = M > R ? M : R;
+          interleave_mfma_ds_vmem<M, R, LPS, G>(std::make_integer_sequence<int, G>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bsl = bnx;
       }
-      interleave_mfma_ds_vmem<KS * MI * NJ, KS * (MI + NJ), LPS>(std::make_integer_sequence<int, KS * (MI + NJ)>{});
-      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();  // the empty loads of the last steps still write LDS the epilogue reuses
+    };
+
+    const int ma = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * TM + 31) / 32)));
+    if (ma >= MI) {
+      kloop(std::integral_constant<int, MI>{});
+    } else {
+      static_assert(MI <= 4, "active-block dispatch covers up to four 32-row blocks per wave");
+      switch (ma) {
+        case 0: kloop(std::integral_constant<int, 0>{}); break;
+        case 1: kloop(std::integral_constant<int, (MI > 1 ? 1 : MI)>{}); break;
+        case 2: kloop(std::integral_constant<int, (MI > 2 ? 2 : MI)>{}); break;
+        default: kloop(std::integral_constant<int, (MI > 3 ? 3 : MI)>{}); break;
+      }
     }
 
     // Epilogue through LDS: every wave writes its fragment values (bf16) into a
     // row-major [BM][CW] tile, then all threads store whole 16-byte row chunks.
     constexpr int CW = kGated ? BN / 2 : BN;  // output columns of the tile
-    static_assert(BM * CW * 2 <= NST * STAGE, "epilogue tile fits in the stage buffers");
+    static_assert(BM * CW * 2 <= LDS_BYTES, "epilogue tile fits in the stage buffers");
     lds_barrier();
     bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
 #pragma unroll
@@ -532,27 +601,24 @@ static int persistent_grid(int64_t max_tiles) {
   return static_cast<int>(g < 1 ? 1 : g);
 }
 
-constexpr int kBigBK = 32, kBigNST = 4;  // 256 x 256 tiles: 4 stages of 32 KB (128 KB of LDS)
-
 int choose_gemm_regime(int64_t T, int k, int E) {
   if (const char* env = getenv("MOE_GEMM_REGIME")) {
     const int r = atoi(env);
-    if (r >= 0 && r <= 2) return r;
+    if (r == 0 || r == 1) return r;
   }
   const int64_t mean_rows = (T * k) / E;
-  return mean_rows >= 96 ? 2 : 0;
+  return mean_rows >= 96 ? 1 : 0;
 }
 
-int regime_block_rows(int regime) { return regime >= 1 ? 256 : 128; }
+int regime_block_rows(int regime) { return regime == 1 ? 256 : 128; }
 
-// Large-tile launch: one workgroup per CU (the four 32 KB stages take 128 KB
-// of the CU's 160 KB LDS), persistent over the tile list.
-template <bool kGated, int WM, int WN>
+// Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take the
+// CU's 160 KB), persistent over the tile list.
+template <bool kGated>
 static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, hipStream_t s) {
   const int64_t nb = kGated ? (ncols + 127) / 128 : (ncols + 255) / 256;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, device_cu_count())));
-  hipLaunchKernelGGL((gemm_dl_kernel<kGated, 256, 256, WM, WN, kBigBK, kBigNST, 1>), dim3(grid), dim3(64 * WM * WN),
-                     0, s, a);
+  hipLaunchKernelGGL((gemm_dl_kernel<kGated, 256, 256, 2, 4>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -560,8 +626,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f};
-  if (dtype == 1 && regime == 2) return launch_big<true, 2, 4>(a, max_mb, f, s);
-  if (dtype == 1 && regime == 1) return launch_big<true, 2, 2>(a, max_mb, f, s);
+  if (dtype == 1 && regime == 1) return launch_big<true>(a, max_mb, f, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -573,8 +638,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d};
-  if (dtype == 1 && regime == 2) return launch_big<false, 2, 4>(a, max_mb, d, s);
-  if (dtype == 1 && regime == 1) return launch_big<false, 2, 2>(a, max_mb, d, s);
+  if (dtype == 1 && regime == 1) return launch_big<false>(a, max_mb, d, s);
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);

@@ -39,9 +39,8 @@ hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int
 
 // Grouped GEMMs over the m-block list. regime 0: 128 x 128 tiles, register-
 // staged, two workgroups per CU (few rows per expert: weight streaming; also
-// the fp32 path); 1: 256 x 256 tiles fed by buffer loads into a 4-stage LDS
-// ring, 4 waves; 2: the same with 8 waves, two per SIMD (the default from 96
-// mean rows per expert).
+// the fp32 path); 1: 256 x 256 tiles fed by buffer loads into LDS, 8 waves,
+// one workgroup per CU (bf16, from 96 mean rows per expert).
 int choose_gemm_regime(int64_t T, int k, int E);
 int regime_block_rows(int regime);
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,

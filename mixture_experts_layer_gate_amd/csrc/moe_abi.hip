@@ -200,9 +200,12 @@ int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const fl
 
 int ffn_shape_ok(const moe_dims_t* dm) {
   if (dm->d % 64 != 0 || dm->f % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  // the GEMM addresses x, h rows and one expert's weights with 32-bit byte offsets
+  // the GEMM addresses x, h rows and one expert's weights with 32-bit byte
+  // offsets, and points padding rows one row past the end of x (or of a
+  // 256-row block of h), so those ends plus one row must stay below 4 GiB too
   const int64_t lim = int64_t(1) << 32, eb = elt_bytes(dm);
-  if (dm->T * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || dm->T * dm->k * dm->f * eb >= lim)
+  if ((dm->T + 1) * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || dm->T * dm->k * dm->f * eb >= lim ||
+      257 * dm->f * eb >= lim)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -160,7 +160,10 @@ REGIME_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("regime", [0, 1, 2])
+GEMM_REGIMES = [0, 1]
+
+
+@pytest.mark.parametrize("regime", GEMM_REGIMES)
 @pytest.mark.parametrize("shape", REGIME_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
 def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     """Every grouped-GEMM tile configuration (forced through MOE_GEMM_REGIME) matches the oracle."""
@@ -170,6 +173,33 @@ def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     cfg = moe_inputs.LayerConfig("regime", T, d, f, E, k, "bf16", s)
     inp = moe_inputs.make_layer_inputs(cfg, 6, "cuda")
     _full_oracle_check(cfg, inp)
+
+
+# Rows per expert chosen so that, in 256-row blocks, the upper and lower 128-row
+# halves of a block hold every number (0..4) of non-empty 32-row sub-blocks.
+PARTIAL_COUNTS = [1, 40, 70, 100, 128, 129, 170, 200, 255, 256, 300]
+
+
+@pytest.mark.parametrize("regime", GEMM_REGIMES)
+def test_grouped_ffn_partial_blocks(monkeypatch, regime):
+    """moe_grouped_ffn on shuffled top-1 routing with the counts above, against the oracle."""
+    _say(f"case partial blocks regime {regime}")
+    monkeypatch.setenv("MOE_GEMM_REGIME", str(regime))
+    E, T = len(PARTIAL_COUNTS), sum(PARTIAL_COUNTS)
+    cfg = moe_inputs.LayerConfig("partial", T, 256, 192, E, 1, "bf16", 0.0)
+    inp = moe_inputs.make_layer_inputs(cfg, 8, "cuda")
+    rng = np.random.default_rng(8)
+    idx_np = rng.permutation(np.repeat(np.arange(E), PARTIAL_COUNTS)).astype(np.int32).reshape(T, 1)
+    counts, offsets, perm, inv = oracle.dispatch(idx_np, E)
+    assert list(counts) == PARTIAL_COUNTS
+    y = moe.grouped_ffn(_dims(cfg), inp["x"], torch.from_numpy(perm).cuda(), torch.from_numpy(counts).cuda(),
+                        torch.from_numpy(offsets).cuda(), inp["w1"], inp["w3"], inp["w2"])
+    torch.cuda.synchronize()
+    h = {n: to_numpy(v, cfg.dtype) for n, v in inp.items()}
+    ref = oracle.expert_ffn_sorted(h["x"], perm, offsets, h["w1"], h["w3"], h["w2"], cfg.k, cfg.dtype)
+    err = rel_err(gpu_float(y), ref)
+    _say(f"  rel_err={err:.3e}")
+    assert err <= OUT_TOL
 
 
 @pytest.mark.parametrize("gate_cfg", ["8,2,4", "4,4,4", "2,4,8", ""])
