@@ -329,11 +329,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(!kGated || (NJ % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(AI * NW * RPI == BM && BI * NW * RPI == BN, "load tiling");
-  // LDS: NBA A buffers, then NBB B buffers (a third B buffer when it fits
-  // in the CU's 160 KB, so weight loads run two steps ahead)
+  // LDS: two A buffers, then as many B buffers (up to 8) as fit in the CU's
+  // 160 KB, so weight loads run NBB-1 steps ahead
   constexpr int A_ST = BM * RB, B_ST = BN * RB;
   constexpr int NBA = 2;
-  constexpr int NBB = 2 * A_ST + 3 * B_ST <= 160 * 1024 ? 3 : 2;
+  constexpr int NBB_FIT = (160 * 1024 - NBA * A_ST) / B_ST;
+  constexpr int NBB = NBB_FIT > 8 ? 8 : NBB_FIT;
+  static_assert(NBB >= 2, "two A and two B buffers fit in LDS");
   constexpr int LDS_BYTES = NBA * A_ST + NBB * B_ST;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
@@ -496,14 +498,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       // uses A buffer j & 1 and B buffer j % NBB; both are free once every
       // wave passed step j's barrier (its reads are done by then), so the
       // loads of A for step j+2 and of B for step j+NBB are issued right
-      // there. Issue order (vmcnt counts in order): B0 A0 [B1] A1 B(NBB-1),
-      // then A(j+2) B(j+NBB) at each step j.
-      issue_b(0, 0);
-      issue_a(0, 0);
-      if constexpr (NBB == 3) issue_b(1, 1);
-      issue_a(1, 1);
-      issue_b(NBB - 1, NBB - 1);
-      wait_vmcnt<(NBB == 3 ? AI + 2 * BI : AI + BI)>();  // A0 and B0 landed
+      // there, in that order. vmcnt counts in issue order, so the prologue
+      // issues as the steps before step 0 would have: B0 .. B(NBB-3), A0,
+      // B(NBB-2), A1, B(NBB-1) (two buffers: B0 A0 A1 B1). At step kt's
+      // barrier only the newest B batch, B(kt+NBB-1), may then be in flight.
+      if constexpr (NBB == 2) {
+        issue_b(0, 0);
+        issue_a(0, 0);
+        issue_a(1, 1);
+        issue_b(1, 1);
+      } else {
+        issue_b(0, 0);
+#pragma unroll
+        for (int j = 1; j <= NBB - 3; ++j) issue_b(j, j);
+        issue_a(0, 0);
+        issue_b(NBB - 2, NBB - 2);
+        issue_a(1, 1);
+        issue_b(NBB - 1, NBB - 1);
+      }
+      wait_vmcnt<(NBB == 2 ? AI + BI : AI + 2 * BI)>();  // A0 and B0 landed
       lds_barrier();
       if constexpr (MA > 0) read_sub(ma_c, 0, 0, 0, 0);
       int bsl = 0;  // B buffer of step kt
@@ -522,7 +535,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        wait_vmcnt<(NBB == 3 ? BI : 0)>();  // this thread's loads of step kt+1 landed
+        wait_vmcnt<(NBB == 2 ? 0 : BI)>();  // this thread's loads of step kt+1 landed
         wait_lds_reads();  // and its reads of step kt's buffers are done: they may be refilled after the barrier
         lds_barrier();
         issue_a(cur, kt + 2);
@@ -602,23 +615,24 @@ static int persistent_grid(int64_t max_tiles) {
 }
 
 int choose_gemm_regime(int64_t T, int k, int E) {
+  (void)T, (void)k, (void)E;
   if (const char* env = getenv("MOE_GEMM_REGIME")) {
     const int r = atoi(env);
-    if (r == 0 || r == 1) return r;
+    if (r >= 0 && r <= 2) return r;
   }
-  const int64_t mean_rows = (T * k) / E;
-  return mean_rows >= 96 ? 1 : 0;
+  return 1;
 }
 
-int regime_block_rows(int regime) { return regime == 1 ? 256 : 128; }
+int regime_block_rows(int regime) { return regime >= 1 ? 256 : 128; }
 
-// Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take the
-// CU's 160 KB), persistent over the tile list.
-template <bool kGated>
+// Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take up
+// to the CU's 160 KB), persistent over the tile list.
+template <bool kGated, int BN, int WM, int WN>
 static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, hipStream_t s) {
-  const int64_t nb = kGated ? (ncols + 127) / 128 : (ncols + 255) / 256;
+  const int64_t cols = kGated ? BN / 2 : BN;
+  const int64_t nb = (ncols + cols - 1) / cols;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, device_cu_count())));
-  hipLaunchKernelGGL((gemm_dl_kernel<kGated, 256, 256, 2, 4>), dim3(grid), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((gemm_dl_kernel<kGated, 256, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -626,7 +640,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f};
-  if (dtype == 1 && regime == 1) return launch_big<true>(a, max_mb, f, s);
+  if (dtype == 1 && regime >= 1) return launch_big<true, 256, 2, 4>(a, max_mb, f, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -638,7 +652,19 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d};
-  if (dtype == 1 && regime == 1) return launch_big<false>(a, max_mb, d, s);
+  if (dtype == 1 && regime >= 1) {
+    // Few m-blocks (decode-sized batches, weight streaming): 256-column tiles
+    // can leave CUs idle (Mixtral-8x22B decode: 8 x 24 tiles for 256 CUs);
+    // 192-column tiles (8 x 32 there, one per CU) are taken when their rounds
+    // of tiles cost less. Regime 2 keeps 256.
+    const int64_t cus = device_cu_count();
+    if (regime == 1 && max_mb * ((d + 255) / 256) < 2 * cus) {
+      const int64_t t256 = (max_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
+      const int64_t t192 = (max_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
+      if (t192 < t256) return launch_big<false, 192, 4, 2>(a, max_mb, d, s);
+    }
+    return launch_big<false, 256, 2, 4>(a, max_mb, d, s);
+  }
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);

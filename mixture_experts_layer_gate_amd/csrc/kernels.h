@@ -38,9 +38,10 @@ hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int
                        int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s);
 
 // Grouped GEMMs over the m-block list. regime 0: 128 x 128 tiles, register-
-// staged, two workgroups per CU (few rows per expert: weight streaming; also
-// the fp32 path); 1: 256 x 256 tiles fed by buffer loads into LDS, 8 waves,
-// one workgroup per CU (bf16, from 96 mean rows per expert).
+// staged, two workgroups per CU (the fp32 path); 1: 256-row tiles fed by
+// buffer loads into LDS, 8 waves, one workgroup per CU (bf16), FC1 256 weight
+// rows wide, FC2 256 or, when few m-blocks would leave CUs idle, 192 columns;
+// 2: as 1 with FC2 always 256 columns. MOE_GEMM_REGIME overrides the choice.
 int choose_gemm_regime(int64_t T, int k, int E);
 int regime_block_rows(int regime);
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,

@@ -160,7 +160,7 @@ REGIME_SHAPES = [
 ]
 
 
-GEMM_REGIMES = [0, 1]
+GEMM_REGIMES = [0, 1, 2]
 
 
 @pytest.mark.parametrize("regime", GEMM_REGIMES)
