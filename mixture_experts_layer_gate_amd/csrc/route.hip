@@ -18,6 +18,7 @@
 // register tile.
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "common.h"
 #include "kernels.h"
@@ -172,6 +173,121 @@ static hipError_t gate_launch(const void* x, const void* wg, const float* bias, 
   return hipGetLastError();
 }
 
+// LDS-staged variant for bf16 gates with many experts (d % 64 == 0). A
+// workgroup owns 16 tokens x 32 experts; K is walked in chunks of 128 that
+// are loaded as bf16, converted to fp32 once and stored in LDS (two
+// buffers), so the inner loop is LDS reads and FMAs only. Lane mapping and
+// summation order are those of gate_logits_kernel with G = 4, RT = 4, RE = 8:
+// 16 lane groups of 16 lanes, group (tg, eg) = tokens 4tg..4tg+3 x experts
+// 8eg..8eg+7, lane q holding classes 4q..4q+3, each class summed in
+// increasing element order, then the same butterfly and bias add.
+constexpr int kLdsTT = 16, kLdsTE = 32, kLdsKC = 128;
+
+__global__ __launch_bounds__(256, 2) void gate_lds_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                                                       const float* __restrict__ bias, float* __restrict__ logits,
+                                                       int T, int d, int E) {
+  constexpr int G = 4, RT = 4, RE = 8, TPP = 16;
+  constexpr int XS = kLdsTT * kLdsKC, WS = kLdsTE * kLdsKC;  // floats per buffer
+  __shared__ __attribute__((aligned(16))) float lx[2][XS];
+  __shared__ __attribute__((aligned(16))) float lw[2][WS];
+  const int tid = threadIdx.x, q = tid % TPP, grp = tid / TPP;
+  const int tg = grp / 4, eg = grp % 4;
+  const int t0 = blockIdx.y * kLdsTT, e0 = blockIdx.x * kLdsTE;
+
+  // staging: 16-byte (8-element) pieces; x tile 16 x 128 = 256 pieces (one
+  // per thread), w tile 32 x 128 = 512 pieces (two per thread)
+  const int xr = tid / 16, xc = (tid % 16) * 8;
+  const bf16_t* xsrc = x + static_cast<int64_t>(min(t0 + xr, T - 1)) * d + xc;
+  const bf16_t* wsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) wsrc[h] = wg + static_cast<int64_t>(min(e0 + xr + 16 * h, E - 1)) * d + xc;
+  u32x4_t rx, rw[2];
+  const int nch = (d + kLdsKC - 1) / kLdsKC;
+  auto gload = [&](int c) {  // chunk c, clamped to the row: a short last chunk reads valid memory, never used
+    const int k0 = min(c * kLdsKC, d - kLdsKC < 0 ? 0 : d - kLdsKC);
+    const int off = c * kLdsKC + xc < d ? c * kLdsKC : k0;
+    rx = *reinterpret_cast<const u32x4_t*>(xsrc + off);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) rw[h] = *reinterpret_cast<const u32x4_t*>(wsrc[h] + off);
+  };
+  auto lstore = [&](int b) {
+    float* px = &lx[b][xr * kLdsKC + xc];
+    reinterpret_cast<f32x4_t*>(px)[0] = f32x4_t{bf16_lo(rx[0]), bf16_hi(rx[0]), bf16_lo(rx[1]), bf16_hi(rx[1])};
+    reinterpret_cast<f32x4_t*>(px)[1] = f32x4_t{bf16_lo(rx[2]), bf16_hi(rx[2]), bf16_lo(rx[3]), bf16_hi(rx[3])};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float* pw = &lw[b][(xr + 16 * h) * kLdsKC + xc];
+      reinterpret_cast<f32x4_t*>(pw)[0] =
+          f32x4_t{bf16_lo(rw[h][0]), bf16_hi(rw[h][0]), bf16_lo(rw[h][1]), bf16_hi(rw[h][1])};
+      reinterpret_cast<f32x4_t*>(pw)[1] =
+          f32x4_t{bf16_lo(rw[h][2]), bf16_hi(rw[h][2]), bf16_lo(rw[h][3]), bf16_hi(rw[h][3])};
+    }
+  };
+
+  float acc[RT][RE][G];
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b = 0; b < RE; ++b)
+#pragma unroll
+      for (int r = 0; r < G; ++r) acc[a][b][r] = 0.0f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nch) gload(c + 1);
+    const int steps = min(kLdsKC, d - c * kLdsKC) / 64;  // d % 64 == 0
+#pragma unroll 1
+    for (int st = 0; st < steps; ++st) {
+      f32x4_t xv[RT], wv[RE];
+#pragma unroll
+      for (int a = 0; a < RT; ++a) xv[a] = *reinterpret_cast<const f32x4_t*>(&lx[b][(4 * tg + a) * kLdsKC + st * 64 + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < RE; ++e) wv[e] = *reinterpret_cast<const f32x4_t*>(&lw[b][(8 * eg + e) * kLdsKC + st * 64 + 4 * q]);
+#pragma unroll
+      for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int e = 0; e < RE; ++e)
+#pragma unroll
+          for (int r = 0; r < G; ++r) acc[a][e][r] = __builtin_fmaf(xv[a][r], wv[e][r], acc[a][e][r]);
+    }
+    if (c + 1 < nch) lstore(b ^ 1);  // buffer b^1 was last read in step c-1, before the barrier below it
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int e = 0; e < RE; ++e) {
+#pragma unroll
+      for (int off = 32; off >= G; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < G; ++r) acc[a][e][r] = acc[a][e][r] + __shfl_down(acc[a][e][r], off / G, TPP);
+#pragma unroll
+      for (int off = G / 2; off >= 1; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < off; ++r) acc[a][e][r] = acc[a][e][r] + acc[a][e][r + off];
+    }
+  if (q != 0) return;
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int e = 0; e < RE; ++e) {
+      const int t = t0 + 4 * tg + a, ex = e0 + 8 * eg + e;
+      if (t < T && ex < E) logits[static_cast<int64_t>(t) * E + ex] = acc[a][e][0] + (bias ? bias[ex] : 0.0f);
+    }
+}
+
+static hipError_t gate_lds_launch(const void* x, const void* wg, const float* bias, float* logits, int64_t T,
+                                  int64_t d, int E, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((E + kLdsTE - 1) / kLdsTE), static_cast<unsigned>((T + kLdsTT - 1) / kLdsTT));
+  hipLaunchKernelGGL(gate_lds_kernel, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                     static_cast<const bf16_t*>(wg), bias, logits, static_cast<int>(T), static_cast<int>(d), E);
+  return hipGetLastError();
+}
+
 template <int kDtype>
 static hipError_t gate_dispatch(const void* x, const void* wg, const float* bias, float* logits,
                                 int64_t T, int64_t d, int E, hipStream_t s) {
@@ -184,7 +300,9 @@ static hipError_t gate_dispatch(const void* x, const void* wg, const float* bias
     return pbs * (64 / g) / kWave;
   };
   const int64_t want = 2048;
-  if (const char* env = getenv("MOE_GATE_CFG")) {  // tuning: "G,RT,RE" among the instantiated tiles
+  const bool lds_ok = kDtype == 1 && d % 64 == 0 && d >= kLdsKC && T <= 65535 * static_cast<int64_t>(kLdsTT);
+  if (const char* env = getenv("MOE_GATE_CFG")) {  // tuning: "lds" or "G,RT,RE" among the instantiated tiles
+    if (lds_ok && strcmp(env, "lds") == 0) return gate_lds_launch(x, wg, bias, logits, T, d, E, s);
     int g = 0, rt = 0, re = 0;
     if (sscanf(env, "%d,%d,%d", &g, &rt, &re) == 3) {
       if (g == 4 && rt == 4 && re == 4) return gate_launch<kDtype, 4, 4, 4>(x, wg, bias, logits, T, d, E, s);
@@ -192,6 +310,9 @@ static hipError_t gate_dispatch(const void* x, const void* wg, const float* bias
       if (g == 8 && rt == 2 && re == 4) return gate_launch<kDtype, 8, 2, 4>(x, wg, bias, logits, T, d, E, s);
     }
   }
+  // many experts: the LDS-staged tile (16 tokens x 32 experts per workgroup)
+  if (lds_ok && E >= kLdsTE && ((T + kLdsTT - 1) / kLdsTT) * ((E + kLdsTE - 1) / kLdsTE) >= 1024)
+    return gate_lds_launch(x, wg, bias, logits, T, d, E, s);
   if (E >= 8 && waves(2, 4, 8) >= want) return gate_launch<kDtype, 2, 4, 8>(x, wg, bias, logits, T, d, E, s);
   if (E >= 4 && waves(8, 2, 4) >= want) return gate_launch<kDtype, 8, 2, 4>(x, wg, bias, logits, T, d, E, s);
   if (E >= 2 && waves(8, 2, 2) >= want) return gate_launch<kDtype, 8, 2, 2>(x, wg, bias, logits, T, d, E, s);
