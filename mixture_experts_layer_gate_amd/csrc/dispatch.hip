@@ -54,12 +54,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_
   __shared__ int32_t tot[kMaxExperts];
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
+  constexpr int kBatch = 16;  // chunk counts loaded together, then rewritten
   int32_t run = 0;
   if (e < E) {
-    for (int b = 0; b < n_chunks; ++b) {
-      const int32_t c = block_hist[static_cast<int64_t>(b) * E + e];
-      block_hist[static_cast<int64_t>(b) * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < n_chunks; b0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        c[j] = b0 + j < n_chunks ? block_hist[static_cast<int64_t>(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (b0 + j < n_chunks) {
+          block_hist[static_cast<int64_t>(b0 + j) * E + e] = run;
+          run += c[j];
+        }
     }
     counts[e] = run;
   }

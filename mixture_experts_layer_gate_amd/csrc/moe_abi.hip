@@ -3,6 +3,7 @@
 // entry point are in include/moe.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -151,10 +152,21 @@ int do_route(const moe_dims_t* dm, const void* x, const void* wg, const float* b
   return hip_status(launch_topk(logits, dm->T, dm->E, dm->k, idx, w, s));
 }
 
+// One-workgroup dispatch (histogram, scan, scatter and plan in one launch)
+// up to kFusedMaxAssign assignments; MOE_DISPATCH=split or =fused overrides.
+bool use_fused_dispatch(int64_t n) {
+  if (n > kFusedMaxAssign) return false;
+  if (const char* env = getenv("MOE_DISPATCH")) {
+    if (strcmp(env, "split") == 0) return false;
+    if (strcmp(env, "fused") == 0) return true;
+  }
+  return true;
+}
+
 int do_permute(const moe_dims_t* dm, const int32_t* idx, int32_t* counts, int32_t* offsets,
                int32_t* perm, int32_t* inv, const PermuteWs& pw, hipStream_t s) {
   const int64_t n = dm->T * dm->k;
-  if (n <= kFusedMaxAssign) {
+  if (use_fused_dispatch(n)) {
     StageScope sc(MOE_STAGE_DISPATCH, s);
     return hip_status(launch_dispatch_fused(idx, n, dm->E, counts, offsets, perm, inv, 0, 0, nullptr, nullptr, s));
   }
@@ -323,7 +335,7 @@ int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const
   const int64_t n = dm->T * dm->k;
   FfnWs fw{};
   ffn_ws(dm, lw.sub, &fw);
-  if (n <= kFusedMaxAssign) {
+  if (use_fused_dispatch(n)) {
     // histogram, scan, scatter and tile plan in one launch
     {
       StageScope sc(MOE_STAGE_DISPATCH, s);

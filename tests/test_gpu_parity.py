@@ -136,6 +136,23 @@ def test_permute_on_given_indices():
         assert np.array_equal(perm.cpu().numpy(), rp) and np.array_equal(inv.cpu().numpy(), ri)
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_dispatch_paths_bit_exact(monkeypatch, path):
+    """Both dispatch implementations (one workgroup, or histogram/scan/scatter kernels) on the
+    same skewed routing, 32768 assignments over 256 experts, against the oracle."""
+    _say(f"case dispatch path {path}")
+    monkeypatch.setenv("MOE_DISPATCH", path)
+    rng = np.random.default_rng(11)
+    T, E, k = 4096, 256, 8
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    idx_np = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm, inv = moe.permute(moe.Dims(T, 128, 128, E, k), torch.from_numpy(idx_np).cuda())
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = oracle.dispatch(idx_np, E)
+    assert np.array_equal(counts.cpu().numpy(), rc) and np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp) and np.array_equal(inv.cpu().numpy(), ri)
+
+
 def test_grouped_ffn_round_robin_routing():
     """Exactly balanced synthetic routing e = (t*k + j) mod E fed to moe_grouped_ffn."""
     cfg = moe_inputs.LayerConfig("rr", 256, 256, 320, 8, 2, "bf16", 0.0)
