@@ -182,7 +182,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(cfg.name, "fc1")
-    roof["kernel"] = "grouped_gemm_kernel (FC1 + SiLU*mul)"
+    big_tile = cfg.dtype == "bf16" and os.environ.get("MOE_GEMM_REGIME", "1") != "0"
+    roof["kernel"] = ("gemm_dl_kernel<gated, 256x256> (FC1 + SiLU*mul)" if big_tile
+                      else "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)")
     roof["kernel_ms"] = round(fc1_ms, 4)
 
     layer_flops = rf.layer_flops(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k)
