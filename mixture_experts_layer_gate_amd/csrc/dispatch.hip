@@ -142,6 +142,16 @@ __global__ __launch_bounds__(kDispThreads) void scatter_kernel(const int32_t* __
   }
 }
 
+// Tile group of an expert's i-th m-block (of nb, the first at list index
+// start): runs of up to kTileGroup consecutive m-blocks of one expert, packed
+// as (index of the group's first m-block) << 4 | (group size). The grouped
+// GEMM walks a group's tiles m-block-fastest, so the CUs that run them at the
+// same time share weight and activation panels.
+__device__ __forceinline__ int tile_group(int start, int i, int nb) {
+  const int g0 = (i / kTileGroup) * kTileGroup;
+  return ((start + g0) << 4) | min(kTileGroup, nb - g0);
+}
+
 // ---------------------------------------------------------------------------
 // Single-workgroup dispatch for small batches (n <= kFusedMaxAssign): the
 // histogram, the exclusive scan, the stable scatter and (optionally) the tile
@@ -212,7 +222,8 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
     const int start = bbefore + bi - nb;
     if (tid < E)
       for (int i = 0; i < nb && start + i < max_mb; ++i)
-        mblocks[start + i] = make_int4(tid, excl + i * block_rows, min(block_rows, c - i * block_rows), 0);
+        mblocks[start + i] = make_int4(tid, excl + i * block_rows, min(block_rows, c - i * block_rows),
+                                       tile_group(start, i, nb));
     if (tid == kFusedThreads - 1) n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(bbefore + bi), max_mb));
   }
   __syncthreads();
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (e < E) {
     for (int i = 0; i < nb && start + i < max_mb; ++i) {
       const int r = min(block_rows, c - i * block_rows);
-      mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * block_rows, r, 0);
+      mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * block_rows, r, tile_group(start, i, nb));
     }
   }
   if (e == 1023) n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(before + incl), max_mb));

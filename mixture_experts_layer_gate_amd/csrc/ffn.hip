@@ -347,7 +347,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
   const int64_t ntiles = static_cast<int64_t>(nmb) * nbc;
   const int nk = static_cast<int>(K / BK);
-  constexpr int GM = 8;  // m-blocks per group in the tile order
   const int lrow = lane / CPR;                                          // row within a load instruction
   // Chunk this lane fetches for a load instruction whose first row is R0.
   // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
@@ -367,11 +366,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
   for (int64_t tile = slot; tile < ntiles; tile += G) {
-    const int64_t grp = tile / (static_cast<int64_t>(GM) * nbc);
-    const int64_t o = tile % (static_cast<int64_t>(GM) * nbc);
-    const int gm_n = static_cast<int>(min(static_cast<int64_t>(GM), nmb - grp * GM));
-    const int mb = static_cast<int>(grp * GM + o % gm_n);
-    const int nb = static_cast<int>(o / gm_n);
+    // Tiles run group by group (the plan's runs of up to kTileGroup m-blocks
+    // of one expert), m-block-fastest inside a group; a malformed group entry
+    // falls back to a group of one.
+    const int row = static_cast<int>(tile / nbc);
+    const int info = g.mblocks[row].w;
+    int m0 = info >> 4, gs = info & 15;
+    if (gs < 1 || gs > kTileGroup || m0 > row || row >= m0 + gs || m0 + gs > nmb) m0 = row, gs = 1;
+    const int64_t o = tile - static_cast<int64_t>(m0) * nbc;
+    const int mb = m0 + static_cast<int>(o % gs);
+    const int nb = static_cast<int>(o / gs);
     const int4 blk = g.mblocks[mb];
     const int e = __builtin_amdgcn_readfirstlane(blk.x);
     const int row0 = __builtin_amdgcn_readfirstlane(blk.y);

@@ -8,6 +8,8 @@ namespace moe {
 // Smallest rows per m-block of the grouped GEMM (tile-aligned token blocks);
 // the large-tile regime uses 256.
 constexpr int kBlockRows = 128;
+// Largest tile group (m-blocks of one expert walked together by the GEMM).
+constexpr int kTileGroup = 8;
 
 // Gate logits l[t][e] in the fixed fp32 order. Requires d % 8 == 0.
 hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const float* bias,
