@@ -624,6 +624,8 @@ int choose_gemm_regime(int64_t T, int k, int E) {
     const int r = atoi(env);
     if (r >= 0 && r <= 2) return r;
   }
+  // 256-row m-blocks for every batch size: weights are streamed once per
+  // m-block, so few large blocks suit weight-bound (decode) batches too
   return 1;
 }
 
@@ -631,12 +633,12 @@ int regime_block_rows(int regime) { return regime >= 1 ? 256 : 128; }
 
 // Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take up
 // to the CU's 160 KB), persistent over the tile list.
-template <bool kGated, int BN, int WM, int WN>
+template <bool kGated, int BM, int BN, int WM, int WN>
 static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, hipStream_t s) {
   const int64_t cols = kGated ? BN / 2 : BN;
   const int64_t nb = (ncols + cols - 1) / cols;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, device_cu_count())));
-  hipLaunchKernelGGL((gemm_dl_kernel<kGated, 256, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
+  hipLaunchKernelGGL((gemm_dl_kernel<kGated, BM, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -644,7 +646,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f};
-  if (dtype == 1 && regime >= 1) return launch_big<true, 256, 2, 4>(a, max_mb, f, s);
+  if (dtype == 1 && regime >= 1) return launch_big<true, 256, 256, 2, 4>(a, max_mb, f, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -654,20 +656,23 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 }
 
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
-                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
+                      const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                      hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d};
   if (dtype == 1 && regime >= 1) {
     // Few m-blocks (decode-sized batches, weight streaming): 256-column tiles
     // can leave CUs idle (Mixtral-8x22B decode: 8 x 24 tiles for 256 CUs);
     // 192-column tiles (8 x 32 there, one per CU) are taken when their rounds
-    // of tiles cost less. Regime 2 keeps 256.
+    // of tiles cost less for the expected number of m-blocks. Regime 2 keeps 256.
     const int64_t cus = device_cu_count();
-    if (regime == 1 && max_mb * ((d + 255) / 256) < 2 * cus) {
-      const int64_t t256 = (max_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
-      const int64_t t192 = (max_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
-      if (t192 < t256) return launch_big<false, 192, 4, 2>(a, max_mb, d, s);
+    bool narrow = false;
+    if (regime != 2 && est_mb * ((d + 255) / 256) < 2 * cus) {
+      const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
+      const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
+      narrow = t192 < t256;
     }
-    return launch_big<false, 256, 2, 4>(a, max_mb, d, s);
+    return narrow ? launch_big<false, 256, 192, 4, 2>(a, max_mb, d, s)
+                  : launch_big<false, 256, 256, 2, 4>(a, max_mb, d, s);
   }
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)

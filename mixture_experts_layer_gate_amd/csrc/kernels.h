@@ -42,15 +42,17 @@ hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int
 // Grouped GEMMs over the m-block list. regime 0: 128 x 128 tiles, register-
 // staged, two workgroups per CU (the fp32 path); 1: 256-row tiles fed by
 // buffer loads into LDS, 8 waves, one workgroup per CU (bf16), FC1 256 weight
-// rows wide, FC2 256 or, when few m-blocks would leave CUs idle, 192 columns;
-// 2: as 1 with FC2 always 256 columns. MOE_GEMM_REGIME overrides the choice.
+// rows wide, FC2 256 or, when few m-blocks would leave CUs idle, 192
+// columns; 2: as 1 with FC2 always 256 columns. MOE_GEMM_REGIME overrides
+// the choice.
 int choose_gemm_regime(int64_t T, int k, int E);
 int regime_block_rows(int regime);
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
-                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
+                      const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                      hipStream_t s);
 
 // Weighted combine.
 hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, const float* w,

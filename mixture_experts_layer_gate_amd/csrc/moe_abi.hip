@@ -201,7 +201,11 @@ int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32
                                        fw.n_mblocks, fw.max_mb, dm->d, dm->f, s))) return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
-  return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb, dm->d, dm->f, s));
+  // expected m-blocks under even routing (the list holds at most max_mb)
+  const int64_t n = dm->T * dm->k, active = n < dm->E ? n : dm->E, br = regime_block_rows(regime);
+  const int64_t est_mb = active > 0 ? active * (((n + active - 1) / active + br - 1) / br) : 1;
+  return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
+                               est_mb < fw.max_mb ? est_mb : fw.max_mb, dm->d, dm->f, s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
