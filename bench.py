@@ -4,7 +4,7 @@ One step = one moe_layer_forward call (gate GEMM + top-k, dispatch, tile plan,
 grouped FC1 + SiLU*mul, grouped FC2, combine) on one batch of synthetic
 inputs already resident in HBM. Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceilings]
 
 The default workload is the Mixtral-8x22B-shaped decode layer (T=256, d=6144,
 f=16384, E=8, top-2, bf16, balanced routing). The roofline object covers the
@@ -33,9 +33,80 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = whole batch")
+    p.add_argument("--expert-curve", choices=sorted(EXPERT_SHAPES), default=None,
+                   help="instead of the layer: time one expert's FC1 + FC2 against rows per expert")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured HBM-read and MFMA ceilings (diagnostic, about a second)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run 5 device copies of 1 GiB (reference kernel for HBM byte counters)")
     return p.parse_args()
+
+
+# Expert shapes (d, f) of the workloads: Mixtral 8x22B, DBRX, DeepSeek-V3 routed expert.
+EXPERT_SHAPES = {"mixtral": (6144, 16384), "dbrx": (6144, 10752), "deepseek": (7168, 2048)}
+
+
+def expert_curve(shape: str, seed: int):
+    """Time T_e(c), the per-expert cost of the grouped FC1 + FC2 at c rows per
+    expert, c = 1, 2, 4, ..., 4096: 8 experts of the shape each get exactly c
+    rows (round-robin routing, k = 1) in one moe_grouped_ffn call, as experts
+    run together in a layer, and T_e = call time / 8. The 8 experts' weights
+    exceed the 256 MB last-level cache for every shape, so they stream from
+    HBM. Prints one JSON line per c, then the fit T_e = k3 * c + k4 over the
+    points with c >= 512 and the floor (mean of c = 1..8)."""
+    import numpy as np
+    import torch
+    import moe_inputs
+    import mixture_experts_layer_gate_amd as moe
+    from mixture_experts_layer_gate_amd import roofline as rf
+
+    d, f = EXPERT_SHAPES[shape]
+    E, cmax = 8, 4096
+    cfg = moe_inputs.LayerConfig(f"curve_{shape}", E * cmax, d, f, E, 1, "bf16", 0.0)
+    inp = moe_inputs.make_layer_inputs(cfg, seed, torch.device("cuda:0"))
+    points = []
+    c = 1
+    while c <= cmax:
+        T = E * c
+        dims = moe.Dims(T, d, f, E, 1)
+        ws = moe.make_workspace(dims)
+        x = inp["x"][:T].contiguous()
+        counts = torch.full((E,), c, dtype=torch.int32, device="cuda")
+        offsets = torch.arange(0, T + 1, c, dtype=torch.int32, device="cuda")
+        # sorted row p = e * c + i holds token i * E + e (routing e = t mod E)
+        perm = torch.arange(T, dtype=torch.int32, device="cuda").view(c, E).t().contiguous().view(-1)
+        y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        reps = 10
+        for _ in range(2):  # warm-up
+            moe.grouped_ffn(dims, x, perm, counts, offsets, inp["w1"], inp["w3"], inp["w2"], y, ws)
+        torch.cuda.synchronize()
+        moe.timing_enable(reps, stages=["fc1", "fc2"])
+        for _ in range(reps):
+            moe.grouped_ffn(dims, x, perm, counts, offsets, inp["w1"], inp["w3"], inp["w2"], y, ws)
+        torch.cuda.synchronize()
+        moe.timing_disable()
+        fc1 = moe.timing_read("fc1")[0] / reps
+        fc2 = moe.timing_read("fc2")[0] / reps
+        ms = fc1 + fc2
+        flops = rf.ffn_flops(T, d, f)
+        wbytes = E * 3 * d * f * 2
+        pt = {"shape": shape, "d": d, "f": f, "rows_per_expert": c, "experts": E, "fc1_ms": round(fc1, 4),
+              "fc2_ms": round(fc2, 4), "t_e_ms": round(ms / E, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+              "weight_gbps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+              "util_e": round(min(c * rf.PEAK_HBM_BYTES_PER_S / rf.PEAK_MFMA_BF16_FLOPS, 1.0), 4)}
+        points.append(pt)
+        print(json.dumps(pt), flush=True)
+        c *= 2
+    rows = np.array([p["rows_per_expert"] for p in points], dtype=np.float64)
+    t = np.array([p["t_e_ms"] for p in points], dtype=np.float64)
+    floor = float(t[:4].mean())  # 1..8 rows per expert: weight streaming
+    big = rows >= 512
+    k3, k4 = np.polyfit(rows[big], t[big], 1)
+    ridge = (floor - k4) / k3 if k3 > 0 else float("nan")
+    print(json.dumps({"shape": shape, "fit": "T_e = k3 * rows + k4 over rows >= 512", "k3_ms_per_row": k3,
+                      "k4_ms": k4, "floor_ms": floor, "ridge_rows": round(ridge, 1),
+                      "datasheet_ridge_rows": round(rf.PEAK_MFMA_BF16_FLOPS / rf.PEAK_HBM_BYTES_PER_S, 1)}),
+          flush=True)
 
 
 def copy_probe():
@@ -115,6 +186,9 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
+    if args.expert_curve:
+        expert_curve(args.expert_curve, args.seed)
+        return
     import torch
     import moe_inputs
     import mixture_experts_layer_gate_amd as moe
@@ -187,6 +261,17 @@ def main():
                       else "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)")
     roof["kernel_ms"] = round(fc1_ms, 4)
 
+    ceilings = None
+    if not args.no_ceilings:
+        # measured ceilings of this GPU (diagnostic): the fraction above is against
+        # the datasheet peak; this one is against what the library's probes sustain
+        hbm = moe.probe_hbm_read_gbps()
+        mfma = moe.probe_mfma_tflops()
+        ceil = hbm if roof["unit"] == "GB/s" else mfma
+        ceilings = {"hbm_read_GBps": round(hbm, 1), "mfma_bf16_TFLOPs": round(mfma, 1),
+                    "frac_of_measured": round(roof["achieved"] / ceil, 4),
+                    "kind": "library probes: streaming read through LDS; register-only bf16 MFMA chains"}
+
     layer_flops = rf.layer_flops(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k)
     layer_bytes = rf.layer_bytes(cfg.T, cfg.d, cfg.f, cfg.E, counts, elt)
     res = {
@@ -209,7 +294,9 @@ def main():
                   "gbps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
                   "bound": rf.classify(layer_flops, layer_bytes).bound,
                   "floor_ms": round(rf.classify(layer_flops, layer_bytes).floor_s * 1e3, 4),
-                  "kappa": round(rf.kappa(counts), 3), "active_experts": rf.active_experts(counts)},
+                  "kappa": round(rf.kappa(counts), 3), "active_experts": rf.active_experts(counts),
+                  "util_pages": round(rf.util(cfg.k, cfg.E, rf.PEAK_HBM_BYTES_PER_S, rf.PEAK_MFMA_BF16_FLOPS, cfg.T), 4)},
+        "ceilings": ceilings,
         "stages_ms": {s: round(v[0] / max(v[1], 1), 4) for s, v in stages.items() if v[1] > 0},
     }
     if not args.no_cpu_baseline:

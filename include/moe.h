@@ -167,6 +167,25 @@ int moe_timing_disable(void);
  * kernel time in ms and the number of launches recorded. */
 int moe_timing_read(int stage, double* total_ms, int* launches);
 
+/* ---- measurement probes (diagnostic; not part of the layer) ----
+ * Kernels that measure what the GPU sustains, so that achieved fractions can be
+ * reported against measured ceilings next to the datasheet peaks. Asynchronous
+ * on `stream`; the caller times them (e.g. with events on that stream). */
+/* Compute units; the probes launch one workgroup of 8 waves on each. */
+int moe_probe_cus(void);
+/* Streams `bytes` (a multiple of 16, 16-byte aligned device buffer `src`)
+ * through LDS: each workgroup reads a contiguous slice of bytes / CUs (rounded
+ * down to 16 bytes; at most 2 GiB) with 16-byte buffer loads, three 32 KiB
+ * steps in flight. sink [CUs] int32 receives one loaded byte per workgroup.
+ * MOE_ERR_INVALID for a null or misaligned pointer or a bad size,
+ * MOE_ERR_UNSUPPORTED if a slice would be empty or too large. */
+int moe_probe_hbm_read(const void* src, size_t bytes, int32_t* sink, void* stream);
+/* `iters` rounds of 16 bf16 32x32x16 MFMAs (four independent accumulator
+ * chains) in each of 8 waves per CU, register operands only:
+ * FLOP = 2*32*32*16 * 16 * 8 * iters * CUs. sink [8 * CUs] fp32 receives each
+ * wave's accumulator sum. MOE_ERR_INVALID for a null sink or iters < 1. */
+int moe_probe_mfma(int iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ MOE_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 # Every symbol include/moe.h declares.
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
-           "moe_timing_disable", "moe_timing_read"]
+           "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma"]
 
 
 class MoeError(RuntimeError):
@@ -81,8 +81,11 @@ def load_library():
     lib.moe_layer_forward.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_timing_enable.argtypes = [ctypes.c_int, ctypes.c_uint]
     lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    lib.moe_probe_cus.restype = ctypes.c_int
+    lib.moe_probe_hbm_read.argtypes = [_P, _S, _P, _P]
+    lib.moe_probe_mfma.argtypes = [ctypes.c_int, _P, _P]
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-               "moe_timing_enable", "moe_timing_disable", "moe_timing_read"):
+               "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -240,3 +243,43 @@ def timing_read(stage: str):
     ms, n = ctypes.c_double(), ctypes.c_int()
     _check("moe_timing_read", load_library().moe_timing_read(STAGES.index(stage), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def probe_hbm_read_gbps(nbytes: int = 2 << 30, reps: int = 5, stream=None) -> float:
+    """Best-of-reps read rate (GB/s) of the library's streaming-read probe over a
+    fresh device buffer of nbytes (one warm-up launch first)."""
+    lib = load_library()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(lib.moe_probe_cus(), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream() if stream is None else stream
+    best = None
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        _check("moe_probe_hbm_read", lib.moe_probe_hbm_read(_ptr(buf), nbytes, _ptr(sink), st.cuda_stream))
+        e1.record(st)
+        e1.synchronize()
+        if i:
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    slice_bytes = nbytes // lib.moe_probe_cus() // 16 * 16
+    return slice_bytes * lib.moe_probe_cus() / (best * 1e-3) / 1e9
+
+
+def probe_mfma_tflops(iters: int = 20000, reps: int = 3, stream=None) -> float:
+    """Best-of-reps bf16 MFMA rate (TFLOP/s) of the library's register-only MFMA probe."""
+    lib = load_library()
+    cus = lib.moe_probe_cus()
+    sink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream() if stream is None else stream
+    best = None
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        _check("moe_probe_mfma", lib.moe_probe_mfma(iters, _ptr(sink), st.cuda_stream))
+        e1.record(st)
+        e1.synchronize()
+        if i:
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    return 2 * 32 * 32 * 16 * 16 * 8 * iters * cus / (best * 1e-3) / 1e12

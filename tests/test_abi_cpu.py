@@ -109,3 +109,15 @@ def test_permute_ffn_combine_validation():
     assert lib.moe_combine(ctypes.byref(dm), A, A, A, None, None) == 1
     assert lib.moe_combine(ctypes.byref(_dims(d=12)), A, A, A, A, None) == 2
     assert lib.moe_timing_read(99, None, None) == 1
+
+
+def test_probe_validation():
+    """The measurement probes reject null, misaligned and badly sized arguments on the host."""
+    lib = moe.load_library()
+    assert lib.moe_probe_hbm_read(None, 1 << 20, 16, None) == 1
+    assert lib.moe_probe_hbm_read(16, 1 << 20, None, None) == 1
+    assert lib.moe_probe_hbm_read(16, 0, 16, None) == 1
+    assert lib.moe_probe_hbm_read(16, 100, 16, None) == 1      # not a multiple of 16
+    assert lib.moe_probe_hbm_read(24, 1 << 20, 16, None) == 1  # misaligned
+    assert lib.moe_probe_mfma(10, None, None) == 1
+    assert lib.moe_probe_mfma(0, 16, None) == 1

@@ -268,3 +268,13 @@ def test_full_size_workload(name):
     _say(f"  sampled out rel_err={err:.3e} over {toks.size} tokens")
     assert err <= OUT_TOL
     assert torch.isfinite(out.float()).all()
+
+
+def test_measurement_probes_run():
+    """The ceilings the bench reports come from working probes: rates within physical bounds."""
+    _say("case probes")
+    gbps = moe.probe_hbm_read_gbps(nbytes=1 << 30, reps=2)
+    tflops = moe.probe_mfma_tflops(iters=2000, reps=2)
+    _say(f"  hbm read {gbps:.0f} GB/s, mfma {tflops:.0f} TFLOP/s")
+    assert 1000 < gbps < 8000 * 1.05
+    assert 300 < tflops < 2516.6 * 1.05
