@@ -33,6 +33,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = whole batch")
+    p.add_argument("--protocol", action="store_true",
+                   help="median of 2 fresh processes x seeds 0,1,2 per workload, and skew ratios of the twins")
+    p.add_argument("--workloads", default="",
+                   help="comma-separated workloads for --protocol (default: all)")
+    p.add_argument("--seeds", default="", help="comma-separated seeds measured one after another in this process")
     p.add_argument("--expert-curve", choices=sorted(EXPERT_SHAPES), default=None,
                    help="instead of the layer: time one expert's FC1 + FC2 against rows per expert")
     p.add_argument("--no-ceilings", action="store_true",
@@ -109,6 +114,40 @@ def expert_curve(shape: str, seed: int):
           flush=True)
 
 
+SKEW_TWINS = [("mixtral_prefill_skew", "mixtral_prefill_bal"), ("dbrx_zipf", "dbrx_bal"),
+              ("deepseek_skew", "deepseek_bal")]
+
+
+def protocol(args):
+    """For each workload, two fresh processes each measure seeds 0, 1 and 2 (the
+    usual warm-up and timed steps); prints one JSON line per workload with the
+    median of the six layer times, then one line with the skew ratios
+    t(skewed) / t(balanced twin). Runs children only: this process never
+    touches the GPU."""
+    import statistics
+    import subprocess
+    import moe_inputs
+    names = [w for w in args.workloads.split(",") if w] or list(moe_inputs.CONFIGS)
+    med = {}
+    for w in names:
+        runs = []
+        for _ in range(2):
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--seeds", "0,1,2",
+                   "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-ceilings"]
+            out = subprocess.run(cmd, check=True, capture_output=True, text=True).stdout
+            runs += [json.loads(l) for l in out.splitlines() if l.startswith("{")]
+        ms = [r["ms_per_step"] for r in runs]
+        m = statistics.median(ms)
+        med[w] = m
+        cfg = moe_inputs.config(w)
+        print(json.dumps({"workload": w, "median_ms": round(m, 4), "tokens_per_s": round(cfg.T / (m * 1e-3), 1),
+                          "runs_ms": ms, "seeds": [r["config"]["seed"] for r in runs],
+                          "fc1_roofline_frac_median": statistics.median(r["roofline"]["frac"] for r in runs),
+                          "bound": runs[0]["roofline"]["bound"]}), flush=True)
+    ratios = {f"{a}/{b}": round(med[a] / med[b], 3) for a, b in SKEW_TWINS if a in med and b in med}
+    print(json.dumps({"skew_ratios": ratios, "target": "<= 1.2"}), flush=True)
+
+
 def copy_probe():
     """Plain device-to-device copies of a known size; their FETCH_SIZE / WRITE_SIZE
     counter readings scale the counters taken on the layer's kernels."""
@@ -123,7 +162,7 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 5}), flush=True)
 
 
-def cpu_baseline(cfg, inp, ntok: int):
+def cpu_baseline(cfg, inp, ntok: int, seed: int = 0):
     """Time the CPU oracle (as it stands) on the first ntok tokens of the same inputs."""
     import numpy as np
     import torch
@@ -148,7 +187,7 @@ def cpu_baseline(cfg, inp, ntok: int):
         limiter.unregister() if hasattr(limiter, "unregister") else None
     return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"oracle layer_forward (numpy, fp64 FFN) on the first {ntok} of {cfg.T} tokens "
-                      f"of workload {cfg.name}, seed 0 inputs; {dt:.1f} s"}
+                      f"of workload {cfg.name}, seed {seed} inputs; {dt:.1f} s"}
 
 
 def kernel_source_sha256() -> str:
@@ -189,6 +228,16 @@ def main():
     if args.expert_curve:
         expert_curve(args.expert_curve, args.seed)
         return
+    if args.protocol:
+        protocol(args)
+        return
+    seeds = [int(v) for v in args.seeds.split(",") if v] or [args.seed]
+    for seed in seeds:
+        print(json.dumps(run_one(args, seed)), flush=True)
+
+
+def run_one(args, seed: int) -> dict:
+    """One measurement of the layer on the workload's inputs for `seed`."""
     import torch
     import moe_inputs
     import mixture_experts_layer_gate_amd as moe
@@ -197,7 +246,7 @@ def main():
     cfg = moe_inputs.config(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = moe_inputs.make_layer_inputs(cfg, args.seed, dev)
+    inp = moe_inputs.make_layer_inputs(cfg, seed, dev)
     dims = moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype)
     ws = moe.make_workspace(dims)
     out = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device=dev)
@@ -288,7 +337,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
-                   "bias_scale": cfg.bias_scale, "seed": args.seed, "parallelism": "none (1 GPU)"},
+                   "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "gbps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
@@ -301,10 +350,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         ntok = cfg.T if args.cpu_sample_tokens <= 0 else min(cfg.T, args.cpu_sample_tokens)
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, ntok)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, ntok, seed)
     else:
         res["cpu_baseline"] = None
-    print(json.dumps(res), flush=True)
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
