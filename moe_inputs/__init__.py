@@ -17,7 +17,8 @@ Recipe (one generator per tensor, in a fixed order, so every tensor is
 reproducible on its own):
 
 * ``torch.Generator(device)`` seeded with ``seed * 1000 + tensor_id``;
-  tensor ids: x=1, wg=2, w1=3, w3=4, w2=5.
+  tensor ids: x=1, wg=2, w1=3, w3=4, w2=5, and for shared experts sw1=6,
+  sw3=7, sw2=8.
 * expert weight tensors are drawn one expert at a time, expert 0 first;
 * each draw is fp32 ``torch.randn``, multiplied by fp32 ``1/sqrt(fan_in)``,
   then converted to the activation dtype (bf16 conversion rounds to nearest
@@ -34,6 +35,7 @@ Tensor layouts (row-major):
   w1 [E][f][d]    FC1 gate projection, [out][in] per expert
   w3 [E][f][d]    FC1 up projection,   [out][in] per expert
   w2 [E][d][f]    FC2 down projection, [out][in] per expert
+  sw1, sw3 [S][f][d], sw2 [S][d][f]   shared experts (only when S > 0)
   bias [E] fp32
 """
 from __future__ import annotations
@@ -46,7 +48,7 @@ import torch
 
 __all__ = ["LayerConfig", "CONFIGS", "TENSOR_IDS", "make_layer_inputs", "gate_bias", "config"]
 
-TENSOR_IDS = {"x": 1, "wg": 2, "w1": 3, "w3": 4, "w2": 5}
+TENSOR_IDS = {"x": 1, "wg": 2, "w1": 3, "w3": 4, "w2": 5, "sw1": 6, "sw3": 7, "sw2": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +62,7 @@ class LayerConfig:
     dtype: str        # "bf16" or "f32": x, weights, intermediate and output
     bias_scale: float  # s in bias[e] = -s * ln(e + 1); 0 = no skew
     description: str = ""
+    n_shared: int = 0  # shared (always-active) experts, same d and f as the routed ones
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -86,6 +89,9 @@ CONFIGS: Dict[str, LayerConfig] = {c.name: c for c in [
                 "DeepSeek-style fine-grained layer, 256 experts top-8, skew 2.0"),
     LayerConfig("deepseek_bal", 4096, 7168, 2048, 256, 8, "bf16", 0.0,
                 "balanced twin of deepseek_skew"),
+    LayerConfig("deepseek_shared", 4096, 7168, 2048, 256, 8, "bf16", 2.0,
+                "DeepSeek-V3-shaped layer: 256 routed experts top-8 plus 1 shared expert, skew 2.0",
+                n_shared=1),
 ]}
 
 
@@ -137,11 +143,17 @@ def make_layer_inputs(cfg: LayerConfig, seed: int = 0, device="cpu",
     w3 = _expert_tensor(cfg.E, cfg.f, cfg.d, 1.0 / math.sqrt(cfg.d), seed, TENSOR_IDS["w3"], dev, dt)
     w2 = _expert_tensor(cfg.E, cfg.d, cfg.f, 1.0 / math.sqrt(cfg.f), seed, TENSOR_IDS["w2"], dev, dt)
     bias = gate_bias(cfg.E, cfg.bias_scale).to(dev)
-    return {"x": x, "wg": wg, "bias": bias, "w1": w1, "w3": w3, "w2": w2}
+    out = {"x": x, "wg": wg, "bias": bias, "w1": w1, "w3": w3, "w2": w2}
+    if cfg.n_shared > 0:
+        S = cfg.n_shared
+        out["sw1"] = _expert_tensor(S, cfg.f, cfg.d, 1.0 / math.sqrt(cfg.d), seed, TENSOR_IDS["sw1"], dev, dt)
+        out["sw3"] = _expert_tensor(S, cfg.f, cfg.d, 1.0 / math.sqrt(cfg.d), seed, TENSOR_IDS["sw3"], dev, dt)
+        out["sw2"] = _expert_tensor(S, cfg.d, cfg.f, 1.0 / math.sqrt(cfg.f), seed, TENSOR_IDS["sw2"], dev, dt)
+    return out
 
 
 def random_inputs(T: int, d: int, f: int, E: int, k: int, dtype: str = "bf16", bias_scale: float = 0.0,
-                  seed: int = 0, device="cpu") -> Dict[str, torch.Tensor]:
+                  seed: int = 0, device="cpu", n_shared: int = 0) -> Dict[str, torch.Tensor]:
     """Inputs for an arbitrary small shape (edge-case and sweep tests)."""
-    cfg = LayerConfig("custom", T, d, f, E, k, dtype, bias_scale)
+    cfg = LayerConfig("custom", T, d, f, E, k, dtype, bias_scale, n_shared=n_shared)
     return make_layer_inputs(cfg, seed, device)

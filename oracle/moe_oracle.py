@@ -22,7 +22,9 @@ Sources on the pages:
   expert (MegaFlux, section 3.1);
 * SwiGLU expert with gate, up and down matrices (Piper, section III-A and
   Table III); FC1 then FC2 per expert and a separate final top-k sum (MegaFlux,
-  section 2.1).
+  section 2.1);
+* shared experts, always active besides the routed ones (Piper, Table III
+  notation; DeepSeek-V3: 256 routed + 1 shared, Piper Table I, note b).
 
 Readings where the pages are silent (each one is listed in the design notes):
 * logits are x . Wg_e plus a per-expert bias, added once after the dot product;
@@ -32,7 +34,10 @@ Readings where the pages are silent (each one is listed in the design notes):
 * weights: softmax over the k selected logits (bias included);
 * W1 is the gated (SiLU) projection, W3 the up projection;
 * SiLU(z) = z / (1 + exp(-z));
-* FFN and combine are computed in fp64 with no intermediate rounding.
+* FFN and combine are computed in fp64 with no intermediate rounding;
+* a shared expert is a SwiGLU expert of the same sizes that every token passes
+  through; its output is added with weight 1, outside the renormalised softmax
+  (shared experts in ascending order after the routed sum).
 
 Arrays: bf16 data is passed as its raw uint16 bit patterns and decoded exactly
 (fp32 bits = u16 << 16); fp32 data as float32.
@@ -44,7 +49,7 @@ import numpy as np
 __all__ = [
     "decode", "gate_logits", "topk_select", "topk_weights", "route", "dispatch",
     "block_plan", "expert_ffn_sorted", "combine", "layer_forward", "token_outputs",
-    "WAVE",
+    "shared_expert_ffn", "layer_forward_shared", "WAVE",
 ]
 
 WAVE = 64  # lane classes of the fixed logit summation order
@@ -241,3 +246,31 @@ def token_outputs(x, idx, w, w1, w3, w2, tokens, dtype: str) -> np.ndarray:
     for j in range(k):
         out += w[tokens, j:j + 1].astype(np.float64) * ys[:, j]
     return out
+
+
+def shared_expert_ffn(x, sw1, sw3, sw2, dtype: str) -> np.ndarray:
+    """y_s[t] = W2_s^T (SiLU(W1_s^T x_t) * W3_s^T x_t) for every shared expert s
+    and token t, fp64 (every token passes through every shared expert: Piper,
+    Table III notation). sw1, sw3: [S, f, d]; sw2: [S, d, f]. Returns [S, T, d]."""
+    xf = decode(x, dtype).astype(np.float64)
+    S = sw1.shape[0]
+    y = np.zeros((S, xf.shape[0], xf.shape[1]), np.float64)
+    for s in range(S):
+        g = xf @ decode(sw1[s], dtype).astype(np.float64).T
+        u = xf @ decode(sw3[s], dtype).astype(np.float64).T
+        y[s] = (_silu(g) * u) @ decode(sw2[s], dtype).astype(np.float64).T
+    return y
+
+
+def layer_forward_shared(x, wg, bias, w1, w3, w2, sw1, sw3, sw2, k: int, dtype: str) -> dict:
+    """The layer with shared experts: the routed layer's output plus, with weight
+    1 and in ascending order, every shared expert's output for the token."""
+    r = layer_forward(x, wg, bias, w1, w3, w2, k, dtype)
+    ys = shared_expert_ffn(x, sw1, sw3, sw2, dtype)
+    out = r["out"].copy()
+    for s in range(ys.shape[0]):
+        out += ys[s]
+    r["routed_out"] = r["out"]
+    r["y_shared"] = ys
+    r["out"] = out
+    return r

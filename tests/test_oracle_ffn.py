@@ -109,3 +109,61 @@ def test_combine_weights_each_slot():
         for j in range(k):
             assert out[t, inv[t * k + j]] == pytest.approx(float(w[t, j]))
     assert out.sum() == pytest.approx(float(w.sum()))
+
+
+def _small_shared(T, d, f, E, k, S, dtype="f32", seed=0, s=0.0):
+    inp = moe_inputs.random_inputs(T, d, f, E, k, dtype, s, seed, n_shared=S)
+    return {n: to_numpy(v, dtype) for n, v in inp.items()}
+
+
+def _direct_dense_python(x, w1, w3, w2):
+    """One SwiGLU expert applied to every token, scalar Python loops (tiny shapes only)."""
+    T, d = x.shape
+    f = w1.shape[0]
+    out = np.zeros((T, d))
+    for t in range(T):
+        h = []
+        for n in range(f):
+            g = sum(float(x[t, i]) * float(w1[n, i]) for i in range(d))
+            u = sum(float(x[t, i]) * float(w3[n, i]) for i in range(d))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        for o in range(d):
+            out[t, o] = sum(h[n] * float(w2[o, n]) for n in range(f))
+    return out
+
+
+@pytest.mark.parametrize("T,d,f,E,k,S", [(5, 6, 7, 4, 2, 1), (3, 4, 5, 3, 1, 2)])
+def test_shared_layer_matches_direct_python(T, d, f, E, k, S):
+    """Shared experts: every token's output gains each shared expert's SwiGLU output, weight 1."""
+    a = _small_shared(T, d, f, E, k, S, seed=4)
+    r = oracle.layer_forward_shared(a["x"], a["wg"], a["bias"], a["w1"], a["w3"], a["w2"],
+                                    a["sw1"], a["sw3"], a["sw2"], k, "f32")
+    ref = _direct_python(a["x"], r["topk_idx"], r["topk_w"], a["w1"], a["w3"], a["w2"])
+    for s in range(S):
+        ref = ref + _direct_dense_python(a["x"], a["sw1"][s], a["sw3"][s], a["sw2"][s])
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_shared_layer_with_zero_routed_output_is_dense_swiglu():
+    """Zero down projections for the routed experts leave the shared expert alone."""
+    T, d, f, E, k = 10, 32, 40, 8, 2
+    a = _small_shared(T, d, f, E, k, 1, dtype="bf16", seed=6)
+    a["w2"] = np.zeros_like(a["w2"])
+    r = oracle.layer_forward_shared(a["x"], a["wg"], a["bias"], a["w1"], a["w3"], a["w2"],
+                                    a["sw1"], a["sw3"], a["sw2"], k, "bf16")
+    dec = lambda v: torch.from_numpy(oracle.decode(v, "bf16")).double()  # noqa: E731
+    xt = dec(a["x"])
+    dense = (torch.nn.functional.silu(xt @ dec(a["sw1"][0]).T) * (xt @ dec(a["sw3"][0]).T)) @ dec(a["sw2"][0]).T
+    np.testing.assert_allclose(r["out"], dense.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_shared_expert_equals_a_single_routed_expert_layer():
+    """A shared expert's output equals a one-expert, top-1 layer with that expert's weights
+    (whose weight is exactly 1)."""
+    T, d, f = 7, 16, 24
+    a = _small_shared(T, d, f, 4, 2, 2, seed=8)
+    ys = oracle.shared_expert_ffn(a["x"], a["sw1"], a["sw3"], a["sw2"], "f32")
+    for s in range(2):
+        r1 = oracle.layer_forward(a["x"], a["wg"][:1], None, a["sw1"][s:s + 1], a["sw3"][s:s + 1],
+                                  a["sw2"][s:s + 1], 1, "f32")
+        np.testing.assert_array_equal(ys[s], r1["out"])
