@@ -181,12 +181,16 @@ def cpu_baseline(cfg, inp, ntok: int, seed: int = 0):
     h = {n: host(v) for n, v in inp.items()}
     x = h["x"][:ntok]
     t0 = time.perf_counter()
-    oracle.layer_forward(x, h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], cfg.k, cfg.dtype)
+    if cfg.n_shared:
+        oracle.layer_forward_shared(x, h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], h["sw1"], h["sw3"], h["sw2"],
+                                    cfg.k, cfg.dtype)
+    else:
+        oracle.layer_forward(x, h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], cfg.k, cfg.dtype)
     dt = time.perf_counter() - t0
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
     return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle layer_forward (numpy, fp64 FFN) on the first {ntok} of {cfg.T} tokens "
+            "sample": f"oracle layer forward (numpy, fp64 FFN) on the first {ntok} of {cfg.T} tokens "
                       f"of workload {cfg.name}, seed {seed} inputs; {dt:.1f} s"}
 
 
@@ -253,17 +257,31 @@ def run_one(args, seed: int) -> dict:
     counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    S = cfg.n_shared
+    if S:
+        ws = torch.empty(moe.workspace_bytes_shared(dims, S), dtype=torch.uint8, device=dev)
+
     def step():
-        moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], out=out,
-                          ws=ws, stream=stream)
+        if S:
+            moe.layer_forward_shared(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                     inp["sw1"], inp["sw3"], inp["sw2"], out=out, ws=ws, stream=stream)
+        else:
+            moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], out=out,
+                              ws=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     # routing counts of this batch (identical every step) for the work accounting
-    _, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
-                             ws=ws, return_routing=True)
-    counts = r["counts"].cpu().tolist()
+    if S:
+        _, r = moe.layer_forward_shared(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                        inp["sw1"], inp["sw3"], inp["sw2"], ws=ws, return_routing=True)
+    else:
+        _, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                 ws=ws, return_routing=True)
+    # shared experts count as S more experts with T rows each
+    counts = r["counts"].cpu().tolist() + [cfg.T] * S
+    kk = cfg.k + S
     torch.cuda.synchronize()
 
     # Timed region: events only around the dominant kernel (FC1), on the
@@ -291,10 +309,10 @@ def run_one(args, seed: int) -> dict:
     stages["fc1"] = fc1_rec
 
     elt = 2 if cfg.dtype == "bf16" else 4
-    n = cfg.T * cfg.k
+    n = cfg.T * kk
     fc1_ms = stages["fc1"][0] / max(stages["fc1"][1], 1)
     fc1_flops = rf.fc1_flops(n, cfg.d, cfg.f)
-    fc1_bytes = rf.fc1_bytes(cfg.T, cfg.d, cfg.f, cfg.k, counts, elt)
+    fc1_bytes = rf.fc1_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt)
     cls = rf.classify(fc1_flops, fc1_bytes)
     if cls.bound == "hbm":
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
@@ -321,7 +339,7 @@ def run_one(args, seed: int) -> dict:
                     "frac_of_measured": round(roof["achieved"] / ceil, 4),
                     "kind": "library probes: streaming read through LDS; register-only bf16 MFMA chains"}
 
-    layer_flops = rf.layer_flops(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k)
+    layer_flops = rf.layer_flops(cfg.T, cfg.d, cfg.f, cfg.E, kk)
     layer_bytes = rf.layer_bytes(cfg.T, cfg.d, cfg.f, cfg.E, counts, elt)
     res = {
         "metric": "MoE layer tokens/s at 1 GPU; % bf16 MFMA peak or % HBM peak (roofline)",
@@ -337,7 +355,7 @@ def run_one(args, seed: int) -> dict:
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
-                   "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
+                   "n_shared": S, "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "gbps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),

@@ -141,6 +141,24 @@ int moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg, con
                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Shared (always-active) experts: a layer whose tokens each also pass through
+ * n_shared SwiGLU experts of the same sizes outside the routing (Piper, Table III
+ * notation; DeepSeek-V3: 256 routed + 1 shared, Piper Table I, note b):
+ *   out[t] = sum_j w[t,j] * FFN_{S_t[j]}(x[t]) + sum_{s ascending} FFN^shared_s(x[t])
+ * with weight 1 for the shared experts (not part of the renormalised softmax).
+ *   sw1, sw3 [n_shared][f][d], sw2 [n_shared][d][f]: shared expert weights.
+ * The routed and shared rows run in one grouped FFN (shared rows after the
+ * T*k routed ones). Other arguments and outputs as moe_layer_forward (the
+ * routing outputs cover the routed experts only). 1 <= n_shared and
+ * E + n_shared <= 1024, else MOE_ERR_INVALID. */
+size_t moe_workspace_bytes_shared(const moe_dims_t* dims, int n_shared);
+int moe_layer_forward_shared(const moe_dims_t* dims, int n_shared, const void* x, const void* wg,
+                             const float* bias, const void* w1, const void* w3, const void* w2,
+                             const void* sw1, const void* sw3, const void* sw2, void* out,
+                             float* logits, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ---- stage timing (instrumentation; process-wide, not thread-safe) ----
  * While enabled, every kernel the library launches is bracketed by HIP events
  * recorded on the stream it is launched on. Stages: */

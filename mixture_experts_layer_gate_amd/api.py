@@ -23,7 +23,8 @@ MOE_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 # Every symbol include/moe.h declares.
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
-           "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma"]
+           "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
+           "moe_workspace_bytes_shared", "moe_layer_forward_shared"]
 
 
 class MoeError(RuntimeError):
@@ -79,12 +80,16 @@ def load_library():
     lib.moe_grouped_ffn.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P]
     lib.moe_layer_forward.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
+    lib.moe_workspace_bytes_shared.restype = _S
+    lib.moe_workspace_bytes_shared.argtypes = [_DP, ctypes.c_int]
+    lib.moe_layer_forward_shared.argtypes = [_DP, ctypes.c_int] + [_P] * 18 + [_S, _P]
     lib.moe_timing_enable.argtypes = [ctypes.c_int, ctypes.c_uint]
     lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.moe_probe_cus.restype = ctypes.c_int
     lib.moe_probe_hbm_read.argtypes = [_P, _S, _P, _P]
     lib.moe_probe_mfma.argtypes = [ctypes.c_int, _P, _P]
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+               "moe_layer_forward_shared",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -225,6 +230,47 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
         ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
         _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")), _ptr(g("counts")), _ptr(g("offsets")),
         _ptr(g("perm")), _ptr(g("inv_perm")), _ptr(ws), nws, _stream(stream)))
+    return (out, r) if return_routing else out
+
+
+def workspace_bytes_shared(dims: Dims, n_shared: int) -> int:
+    return int(load_library().moe_workspace_bytes_shared(ctypes.byref(dims.c()), n_shared))
+
+
+def layer_forward_shared(dims: Dims, x, wg, bias, w1, w3, w2, sw1, sw3, sw2, out=None, ws=None, stream=None,
+                         return_routing=False):
+    """The layer with shared (always-active) experts sw1, sw3 [S][f][d], sw2 [S][d][f]."""
+    lib = load_library()
+    dev = x.device
+    S = int(sw1.shape[0])
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    _need(wg, "wg", dims.dtype, (dims.E, dims.d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (dims.E,))
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f)), ("sw1", sw1, (S, dims.f, dims.d)),
+                         ("sw3", sw3, (S, dims.f, dims.d)), ("sw2", sw2, (S, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    if out is None:
+        out = torch.empty((dims.T, dims.d), dtype=dims.dtype, device=dev)
+    r = {}
+    if return_routing:
+        n = dims.T * dims.k
+        r = {"logits": torch.empty((dims.T, dims.E), dtype=torch.float32, device=dev),
+             "topk_idx": torch.empty((dims.T, dims.k), dtype=torch.int32, device=dev),
+             "topk_w": torch.empty((dims.T, dims.k), dtype=torch.float32, device=dev),
+             "counts": torch.empty(dims.E, dtype=torch.int32, device=dev),
+             "offsets": torch.empty(dims.E + 1, dtype=torch.int32, device=dev),
+             "perm": torch.empty(n, dtype=torch.int32, device=dev),
+             "inv_perm": torch.empty(n, dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = torch.empty(max(workspace_bytes_shared(dims, S), 256), dtype=torch.uint8, device=dev)
+    g = r.get
+    _check("moe_layer_forward_shared", lib.moe_layer_forward_shared(
+        ctypes.byref(dims.c()), S, _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(sw1),
+        _ptr(sw3), _ptr(sw2), _ptr(out), _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")),
+        _ptr(g("counts")), _ptr(g("offsets")), _ptr(g("perm")), _ptr(g("inv_perm")), _ptr(ws), ws.numel(),
+        _stream(stream)))
     return (out, r) if return_routing else out
 
 

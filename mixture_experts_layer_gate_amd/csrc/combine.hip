@@ -1,4 +1,5 @@
-// Weighted combine: out[t] = sum_{j ascending} w[t][j] * y_sorted[inv_perm[t*k + j]].
+// Weighted combine: out[t] = sum_{j ascending} w[t][j] * y_sorted[inv_perm[t*k + j]],
+// plus, for shared (always-active) experts, y[T*k + s*T + t] for s ascending.
 //
 // The final top-k sum is its own step after the expert FFN (MegaFlux,
 // section 2.1); token identity, slot and weight of every assignment are kept
@@ -17,7 +18,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* __res
                                                                const int32_t* __restrict__ inv_perm,
                                                                const float* __restrict__ w,
                                                                void* __restrict__ out, int64_t d,
-                                                               int k, int64_t n_assign) {
+                                                               int k, int64_t n_assign, int n_shared,
+                                                               int64_t T) {
   const int64_t t = blockIdx.x;
   const int64_t nvec = d / 8;
   for (int64_t c = threadIdx.x; c < nvec; c += kCombThreads) {
@@ -41,6 +43,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* __res
 #pragma unroll
       for (int r = 0; r < 8; ++r) acc[r] = __builtin_fmaf(wj, v[r], acc[r]);
     }
+    // shared experts: rows n_assign + s*T + t, weight 1, after the routed slots
+    for (int sh = 0; sh < n_shared; ++sh) {
+      const int64_t p = n_assign + static_cast<int64_t>(sh) * T + t;
+      if constexpr (kDtype == 1) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(y) + p * d + c * 8);
+        acc[0] += bf16_lo(u.x); acc[1] += bf16_hi(u.x); acc[2] += bf16_lo(u.y); acc[3] += bf16_hi(u.y);
+        acc[4] += bf16_lo(u.z); acc[5] += bf16_hi(u.z); acc[6] += bf16_lo(u.w); acc[7] += bf16_hi(u.w);
+      } else {
+        const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(y) + p * d + c * 8);
+        const float4 a = q[0], b = q[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      }
+    }
     if constexpr (kDtype == 1) {
       uint4 o;
       o.x = pack_bf16x2(acc[0], acc[1]);
@@ -57,14 +73,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* __res
 }
 
 hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, const float* w,
-                          void* out, int64_t T, int64_t d, int k, hipStream_t s) {
+                          void* out, int64_t T, int64_t d, int k, hipStream_t s, int n_shared) {
   const int64_t n_assign = T * k;
   if (dtype == 1)
     hipLaunchKernelGGL((combine_kernel<1>), dim3(static_cast<unsigned>(T)), dim3(kCombThreads), 0, s,
-                       y, inv_perm, w, out, d, k, n_assign);
+                       y, inv_perm, w, out, d, k, n_assign, n_shared, T);
   else
     hipLaunchKernelGGL((combine_kernel<0>), dim3(static_cast<unsigned>(T)), dim3(kCombThreads), 0, s,
-                       y, inv_perm, w, out, d, k, n_assign);
+                       y, inv_perm, w, out, d, k, n_assign, n_shared, T);
   return hipGetLastError();
 }
 

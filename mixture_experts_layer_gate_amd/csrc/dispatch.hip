@@ -293,15 +293,24 @@ int64_t max_mblocks(int64_t n_assign, int E) {
 // counts/offsets are clamped into [0, n_assign] and the list into max_mb
 // entries, so inconsistent caller-provided counts cannot send the GEMM out of
 // bounds (they give unspecified rows instead).
+// Shared experts (n_shared > 0) follow the E routed ones as experts E .. E+n_shared-1,
+// each with T rows starting at sorted row n_assign + s*T.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int64_t n_assign, int64_t max_mb, int block_rows,
                                                     int4* __restrict__ mblocks,
-                                                    int32_t* __restrict__ n_mblocks) {
+                                                    int32_t* __restrict__ n_mblocks, int n_shared, int64_t T) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
-  const int64_t row0 = e < E ? min(max(static_cast<int64_t>(offsets[e]), int64_t(0)), n_assign) : 0;
-  const int c = e < E ? static_cast<int>(min(max(static_cast<int64_t>(counts[e]), int64_t(0)), n_assign - row0)) : 0;
+  int64_t row0 = 0;
+  int c = 0;
+  if (e < E) {
+    row0 = min(max(static_cast<int64_t>(offsets[e]), int64_t(0)), n_assign);
+    c = static_cast<int>(min(max(static_cast<int64_t>(counts[e]), int64_t(0)), n_assign - row0));
+  } else if (e < E + n_shared) {
+    row0 = n_assign + static_cast<int64_t>(e - E) * T;
+    c = static_cast<int>(T);
+  }
   const int nb = (c + block_rows - 1) / block_rows;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int incl = nb;
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   int before = 0;
   for (int w = 0; w < wv; ++w) before += wsum[w];
   const int start = before + incl - nb;
-  if (e < E) {
+  if (e < E + n_shared) {
     for (int i = 0; i < nb && start + i < max_mb; ++i) {
       const int r = min(block_rows, c - i * block_rows);
       mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * block_rows, r, tile_group(start, i, nb));
@@ -325,9 +334,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,
-                       int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s) {
+                       int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s,
+                       int n_shared, int64_t T) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, n_assign, max_mb, block_rows,
-                     mblocks, n_mblocks);
+                     mblocks, n_mblocks, n_shared, T);
   return hipGetLastError();
 }
 

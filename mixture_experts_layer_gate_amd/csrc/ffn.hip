@@ -13,6 +13,7 @@
 // are gathered through perm (FC1) or read contiguously (FC2). Tiles are taken
 // from a persistent loop over (n-block, m-block) pairs; waves whose 32-row
 // sub-blocks lie entirely past the block's rows skip their MFMAs.
+#include <stdint.h>
 #include <stdlib.h>
 
 #include <algorithm>
@@ -30,17 +31,34 @@ constexpr int kThreads = 256;
 static_assert(kBM == kBlockRows, "small-tile rows must match the plan's smallest block rows");
 
 struct GemmArgs {
-  const void* A;          // FC1: x [T][K]; FC2: h [T*k][K]
-  const int32_t* perm;    // FC1: sorted row -> assignment
+  const void* A;          // FC1: x [T][K]; FC2: h [rows][K]
+  const int32_t* perm;    // FC1: sorted row -> assignment (routed rows)
   int ktop;               // FC1: token = perm[p] / ktop
-  int64_t T;              // FC1: token count (clamp)
+  int64_t T;              // FC1: token count (clamp; shared rows: token = (p - n_routed) % T)
   const void* B0;         // FC1: W1 [E][N][K]; FC2: W2 [E][N][K]
   const void* B1;         // FC1: W3 [E][N][K]
-  void* C;                // FC1: h [T*k][N]; FC2: y [T*k][N]
-  const int4* mblocks;    // (expert, first sorted row, rows, 0)
+  void* C;                // FC1: h [rows][N]; FC2: y [rows][N]
+  const int4* mblocks;    // (expert, first sorted row, rows, tile group)
   const int32_t* n_mblocks;
   int64_t K, N;
+  int64_t n_routed;       // sorted rows covered by perm; rows after them belong to shared experts
+  const void* S0;         // shared experts' W1 (FC1) or W2 (FC2), [S][N][K]
+  const void* S1;         // shared experts' W3 (FC1)
+  int E_routed;           // experts e >= E_routed are shared expert e - E_routed
 };
+
+// Token of sorted row p (FC1): routed rows through perm, shared rows directly.
+__device__ __forceinline__ int64_t row_token(const GemmArgs& g, int64_t p) {
+  int64_t tok = p < g.n_routed ? g.perm[p] / g.ktop : (p - g.n_routed) % (g.T > 0 ? g.T : 1);
+  return tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
+}
+
+// First weight byte of expert e in a routed tensor B or, for a shared expert, in S.
+__device__ __forceinline__ const char* expert_base(const GemmArgs& g, const void* B, const void* S, int e,
+                                                   int64_t ebytes) {
+  return e < g.E_routed ? static_cast<const char*>(B) + e * ebytes
+                        : static_cast<const char*>(S) + static_cast<int64_t>(e - g.E_routed) * ebytes;
+}
 
 template <int ACH, int BCH>
 __device__ __forceinline__ void gemm_gload(u32x4_t (&ra)[ACH], u32x4_t (&rb)[BCH], const char* const (&aptr)[ACH],
@@ -100,13 +118,10 @@ __global__ __launch_bounds__(kThreads, kDtype == 1 ? 2 : 1) void grouped_gemm_ke
       acol[i] = c % CPR;
       const int rr = row0 + (r < rows ? r : 0);
       int64_t arow;
-      if constexpr (kGated) {
-        int64_t tok = g.perm[rr] / g.ktop;
-        tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
-        arow = tok;
-      } else {
+      if constexpr (kGated)
+        arow = row_token(g, rr);
+      else
         arow = rr;
-      }
       aptr_[i] = static_cast<const char*>(g.A) + (arow * K) * EB + acol[i] * 16;
     }
     const char* bptr_[BCH];
@@ -119,14 +134,14 @@ __global__ __launch_bounds__(kThreads, kDtype == 1 ? 2 : 1) void grouped_gemm_ke
       const char* base;
       int64_t n;
       if constexpr (kGated) {
-        base = static_cast<const char*>(r < kBNW / 2 ? g.B0 : g.B1);
+        base = r < kBNW / 2 ? expert_base(g, g.B0, g.S0, e, N * K * EB) : expert_base(g, g.B1, g.S1, e, N * K * EB);
         n = static_cast<int64_t>(nb) * (kBNW / 2) + (r % (kBNW / 2));
       } else {
-        base = static_cast<const char*>(g.B0);
+        base = expert_base(g, g.B0, g.S0, e, N * K * EB);
         n = static_cast<int64_t>(nb) * kBNW + r;
         if (n >= N) n = N - 1;
       }
-      bptr_[i] = base + ((static_cast<int64_t>(e) * N + n) * K) * EB + bcol[i] * 16;
+      bptr_[i] = base + (n * K) * EB + bcol[i] * 16;
     }
 
     f32x16_t acc[2][2];
@@ -392,8 +407,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       for (int i = 0; i < AI; ++i) {
         const int r = (wv * AI + i) * RPI + lrow;
         if (r < rows) {
-          int64_t tok = g.perm[row0 + r] / g.ktop;
-          tok = tok < 0 ? 0 : (tok >= g.T ? g.T - 1 : tok);
+          const int64_t tok = row_token(g, row0 + r);
           aoff[i] = static_cast<uint32_t>(tok * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
         } else {
           aoff[i] = a_bytes;
@@ -413,8 +427,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
     uint32_t boff[BI];
     {
       const int64_t ebytes = N * K * 2;
-      brs0 = make_rsrc(static_cast<const char*>(g.B0) + e * ebytes, static_cast<uint32_t>(ebytes));
-      brs1 = kGated ? make_rsrc(static_cast<const char*>(g.B1) + e * ebytes, static_cast<uint32_t>(ebytes)) : brs0;
+      brs0 = make_rsrc(expert_base(g, g.B0, g.S0, e, ebytes), static_cast<uint32_t>(ebytes));
+      brs1 = kGated ? make_rsrc(expert_base(g, g.B1, g.S1, e, ebytes), static_cast<uint32_t>(ebytes)) : brs0;
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
         const int r = (wv * BI + i) * RPI + lrow;
@@ -644,8 +658,10 @@ static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, h
 
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
-                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
-  GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f};
+                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
+                      const SharedExperts& sh, hipStream_t s) {
+  GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f,
+             T * k, sh.w1, sh.w3, sh.n > 0 ? sh.E_routed : INT32_MAX};
   if (dtype == 1 && regime >= 1) return launch_big<true, 256, 256, 2, 4>(a, max_mb, f, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
@@ -657,8 +673,9 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      hipStream_t s) {
-  GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d};
+                      const SharedExperts& sh, hipStream_t s) {
+  GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d,
+             0, sh.w2, nullptr, sh.n > 0 ? sh.E_routed : INT32_MAX};
   if (dtype == 1 && regime >= 1) {
     // Few m-blocks (decode-sized batches, weight streaming): 256-column tiles
     // can leave CUs idle (Mixtral-8x22B decode: 8 x 24 tiles for 256 CUs);

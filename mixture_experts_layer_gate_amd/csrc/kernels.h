@@ -36,8 +36,11 @@ hipError_t launch_dispatch_fused(const int32_t* idx, int64_t n, int E, int32_t* 
 
 // Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most block_rows rows.
 int64_t max_mblocks(int64_t n_assign, int E);
+// With n_shared > 0, shared experts E .. E+n_shared-1 of T rows each follow the
+// routed rows (E + n_shared <= 1024).
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,
-                       int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s);
+                       int64_t max_mb, int block_rows, int4* mblocks, int32_t* n_mblocks, hipStream_t s,
+                       int n_shared = 0, int64_t T = 0);
 
 // Grouped GEMMs over the m-block list. regime 0: 128 x 128 tiles, register-
 // staged, two workgroups per CU (the fp32 path); 1: 256-row tiles fed by
@@ -45,18 +48,30 @@ hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int
 // rows wide, FC2 256 or, when few m-blocks would leave CUs idle, 192
 // columns; 2: as 1 with FC2 always 256 columns. MOE_GEMM_REGIME overrides
 // the choice.
+// Shared (always-active) experts appended to the routed ones: expert ids
+// E_routed .. E_routed + n - 1, each with T rows after the T*k routed rows.
+struct SharedExperts {
+  int n = 0;
+  const void* w1 = nullptr;  // [n][f][d]
+  const void* w3 = nullptr;  // [n][f][d]
+  const void* w2 = nullptr;  // [n][d][f]
+  int E_routed = 0;
+};
+
 int choose_gemm_regime(int64_t T, int k, int E);
 int regime_block_rows(int regime);
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
-                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
+                      const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
+                      const SharedExperts& sh, hipStream_t s);
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      hipStream_t s);
+                      const SharedExperts& sh, hipStream_t s);
 
 // Weighted combine.
+// With n_shared > 0, out[t] also adds y[T*k + s*T + t] for s ascending.
 hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, const float* w,
-                          void* out, int64_t T, int64_t d, int k, hipStream_t s);
+                          void* out, int64_t T, int64_t d, int k, hipStream_t s, int n_shared = 0);
 
 int device_cu_count();
 

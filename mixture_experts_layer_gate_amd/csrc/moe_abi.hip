@@ -104,14 +104,17 @@ size_t permute_ws(const moe_dims_t* dm, void* ws, PermuteWs* out) {
   return c.off;
 }
 
+// Sorted rows of the grouped FFN: T*k routed rows, then T rows per shared expert.
+int64_t ffn_rows(const moe_dims_t* dm, int n_shared) { return dm->T * dm->k + static_cast<int64_t>(n_shared) * dm->T; }
+
 struct FfnWs { int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; };
-size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out) {
+size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   Carver c(ws);
   FfnWs r{};
-  r.max_mb = max_mblocks(dm->T * dm->k, dm->E);
+  r.max_mb = max_mblocks(ffn_rows(dm, n_shared), dm->E + n_shared);
   r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
   r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
-  r.h = c.take<char>(size_t(elt_bytes(dm)) * dm->T * dm->k * dm->f);
+  r.h = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->f);
   if (out) *out = r;
   return c.off;
 }
@@ -120,7 +123,7 @@ struct LayerWs {
   float* logits; int32_t* idx; float* w; int32_t* counts; int32_t* offsets; int32_t* perm;
   int32_t* inv; void* y; void* sub;  // sub: start of the permute / ffn scratch (shared)
 };
-size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out) {
+size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out, int n_shared = 0) {
   Carver c(ws);
   LayerWs r{};
   const size_t n = size_t(dm->T) * dm->k;
@@ -131,9 +134,9 @@ size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out) {
   r.offsets = c.take<int32_t>(sizeof(int32_t) * (dm->E + 1));
   r.perm = c.take<int32_t>(sizeof(int32_t) * n);
   r.inv = c.take<int32_t>(sizeof(int32_t) * n);
-  r.y = c.take<char>(size_t(elt_bytes(dm)) * n * dm->d);
-  const size_t sub = permute_ws(dm, nullptr, nullptr) > ffn_ws(dm, nullptr, nullptr)
-                         ? permute_ws(dm, nullptr, nullptr) : ffn_ws(dm, nullptr, nullptr);
+  r.y = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->d);
+  const size_t pws = permute_ws(dm, nullptr, nullptr), fws = ffn_ws(dm, nullptr, nullptr, n_shared);
+  const size_t sub = pws > fws ? pws : fws;
   r.sub = c.take<char>(sub);
   if (out) *out = r;
   return c.off;
@@ -188,42 +191,92 @@ int gemm_regime(const moe_dims_t* dm) {
 
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
-           const FfnWs& fw, hipStream_t s, bool planned = false) {
+           const FfnWs& fw, hipStream_t s, bool planned = false, const SharedExperts& sh = SharedExperts{}) {
   const int regime = gemm_regime(dm);
   if (!planned) {
     StageScope sc(MOE_STAGE_PLAN, s);
     if (int st = hip_status(launch_plan(counts, offsets, dm->E, dm->T * dm->k, fw.max_mb, regime_block_rows(regime),
-                                        fw.mblocks, fw.n_mblocks, s))) return st;
+                                        fw.mblocks, fw.n_mblocks, s, sh.n, dm->T))) return st;
   }
   {
     StageScope sc(MOE_STAGE_FC1, s);
     if (int st = hip_status(launch_fc1(dm->dtype, regime, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
-                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, s))) return st;
+                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, s))) return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
   // expected m-blocks under even routing (the list holds at most max_mb)
   const int64_t n = dm->T * dm->k, active = n < dm->E ? n : dm->E, br = regime_block_rows(regime);
-  const int64_t est_mb = active > 0 ? active * (((n + active - 1) / active + br - 1) / br) : 1;
+  int64_t est_mb = active > 0 ? active * (((n + active - 1) / active + br - 1) / br) : 1;
+  est_mb += static_cast<int64_t>(sh.n) * ((dm->T + br - 1) / br);
   return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
-                               est_mb < fw.max_mb ? est_mb : fw.max_mb, dm->d, dm->f, s));
+                               est_mb < fw.max_mb ? est_mb : fw.max_mb, dm->d, dm->f, sh, s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
-               hipStream_t s) {
+               hipStream_t s, int n_shared = 0) {
   StageScope sc(MOE_STAGE_COMBINE, s);
-  return hip_status(launch_combine(dm->dtype, y, inv, w, out, dm->T, dm->d, dm->k, s));
+  return hip_status(launch_combine(dm->dtype, y, inv, w, out, dm->T, dm->d, dm->k, s, n_shared));
 }
 
-int ffn_shape_ok(const moe_dims_t* dm) {
+int ffn_shape_ok(const moe_dims_t* dm, int n_shared = 0) {
   if (dm->d % 64 != 0 || dm->f % 64 != 0) return MOE_ERR_UNSUPPORTED;
   // the GEMM addresses x, h rows and one expert's weights with 32-bit byte
   // offsets, and points padding rows one row past the end of x (or of a
   // 256-row block of h), so those ends plus one row must stay below 4 GiB too
   const int64_t lim = int64_t(1) << 32, eb = elt_bytes(dm);
-  if ((dm->T + 1) * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || dm->T * dm->k * dm->f * eb >= lim ||
+  if ((dm->T + 1) * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || ffn_rows(dm, n_shared) * dm->f * eb >= lim ||
       257 * dm->f * eb >= lim)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// The layer: route, dispatch, grouped FFN over the routed (and shared) rows, combine.
+int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, const void* wg, const float* bias,
+              const void* w1, const void* w3, const void* w2, void* out, float* logits, int32_t* topk_idx,
+              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+              size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(out) ||
+      !ok4_or_null(logits) || !ok4_or_null(topk_idx) || !ok4_or_null(topk_w) || !ok4_or_null(counts) ||
+      !ok4_or_null(offsets) || !ok4_or_null(perm) || !ok4_or_null(inv_perm))
+    return MOE_ERR_INVALID;
+  if (int st = ffn_shape_ok(dm, sh.n)) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < layer_ws(dm, nullptr, nullptr, sh.n)) return MOE_ERR_WORKSPACE;
+  LayerWs lw{};
+  layer_ws(dm, ws, &lw, sh.n);
+  if (!logits) logits = lw.logits;
+  if (!topk_idx) topk_idx = lw.idx;
+  if (!topk_w) topk_w = lw.w;
+  if (!counts) counts = lw.counts;
+  if (!offsets) offsets = lw.offsets;
+  if (!perm) perm = lw.perm;
+  if (!inv_perm) inv_perm = lw.inv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
+  const int64_t n = dm->T * dm->k;
+  FfnWs fw{};
+  ffn_ws(dm, lw.sub, &fw, sh.n);
+  if (use_fused_dispatch(n)) {
+    // histogram, scan, scatter (and, without shared experts, the tile plan) in one launch
+    const bool plan_inline = sh.n == 0;
+    {
+      StageScope sc(MOE_STAGE_DISPATCH, s);
+      if (int st = hip_status(launch_dispatch_fused(topk_idx, n, dm->E, counts, offsets, perm, inv_perm,
+                                                    regime_block_rows(gemm_regime(dm)), fw.max_mb,
+                                                    plan_inline ? fw.mblocks : nullptr,
+                                                    plan_inline ? fw.n_mblocks : nullptr, s)))
+        return st;
+    }
+    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, plan_inline, sh)) return st;
+  } else {
+    PermuteWs pw{};
+    permute_ws(dm, lw.sub, &pw);
+    if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
+    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, false, sh)) return st;
+  }
+  return do_combine(dm, lw.y, inv_perm, topk_w, out, s, sh.n);
 }
 
 }  // namespace
@@ -316,46 +369,32 @@ int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const
                       const void* w1, const void* w3, const void* w2, void* out, float* logits,
                       int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                       int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
+                   perm, inv_perm, ws, ws_bytes, stream);
+}
+
+size_t moe_workspace_bytes_shared(const moe_dims_t* dm, int n_shared) {
+  if (check_dims(dm) != MOE_OK || n_shared < 1 || dm->E + n_shared > 1024) return 0;
+  return layer_ws(dm, nullptr, nullptr, n_shared);
+}
+
+int moe_layer_forward_shared(const moe_dims_t* dm, int n_shared, const void* x, const void* wg, const float* bias,
+                             const void* w1, const void* w3, const void* w2, const void* sw1, const void* sw3,
+                             const void* sw2, void* out, float* logits, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                             size_t ws_bytes, void* stream) {
   if (int st = check_dims(dm)) return st;
-  if (dm->T == 0) return MOE_OK;
-  if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(out) ||
-      !ok4_or_null(logits) || !ok4_or_null(topk_idx) || !ok4_or_null(topk_w) || !ok4_or_null(counts) ||
-      !ok4_or_null(offsets) || !ok4_or_null(perm) || !ok4_or_null(inv_perm))
+  if (n_shared < 1 || dm->E + n_shared > 1024 || dm->T * (dm->k + int64_t(n_shared)) >= (int64_t(1) << 31))
     return MOE_ERR_INVALID;
-  if (int st = ffn_shape_ok(dm)) return st;
-  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
-  if (ws_bytes < layer_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
-  LayerWs lw{};
-  layer_ws(dm, ws, &lw);
-  if (!logits) logits = lw.logits;
-  if (!topk_idx) topk_idx = lw.idx;
-  if (!topk_w) topk_w = lw.w;
-  if (!counts) counts = lw.counts;
-  if (!offsets) offsets = lw.offsets;
-  if (!perm) perm = lw.perm;
-  if (!inv_perm) inv_perm = lw.inv;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
-  const int64_t n = dm->T * dm->k;
-  FfnWs fw{};
-  ffn_ws(dm, lw.sub, &fw);
-  if (use_fused_dispatch(n)) {
-    // histogram, scan, scatter and tile plan in one launch
-    {
-      StageScope sc(MOE_STAGE_DISPATCH, s);
-      if (int st = hip_status(launch_dispatch_fused(topk_idx, n, dm->E, counts, offsets, perm, inv_perm,
-                                                    regime_block_rows(gemm_regime(dm)), fw.max_mb, fw.mblocks,
-                                                    fw.n_mblocks, s)))
-        return st;
-    }
-    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, true)) return st;
-  } else {
-    PermuteWs pw{};
-    permute_ws(dm, lw.sub, &pw);
-    if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
-    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s)) return st;
-  }
-  return do_combine(dm, lw.y, inv_perm, topk_w, out, s);
+  if (dm->T > 0 && (!ok16(sw1) || !ok16(sw3) || !ok16(sw2))) return MOE_ERR_INVALID;
+  SharedExperts sh;
+  sh.n = n_shared;
+  sh.w1 = sw1;
+  sh.w3 = sw3;
+  sh.w2 = sw2;
+  sh.E_routed = dm->E;
+  return run_layer(dm, sh, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets, perm,
+                   inv_perm, ws, ws_bytes, stream);
 }
 
 int moe_timing_enable(int capacity, unsigned stage_mask) {

@@ -121,3 +121,24 @@ def test_probe_validation():
     assert lib.moe_probe_hbm_read(24, 1 << 20, 16, None) == 1  # misaligned
     assert lib.moe_probe_mfma(10, None, None) == 1
     assert lib.moe_probe_mfma(0, 16, None) == 1
+
+
+def test_layer_shared_validation():
+    """moe_layer_forward_shared rejects a bad shared-expert count or missing shared weights
+    before anything is launched; an empty batch is a no-op."""
+    lib = moe.load_library()
+
+    def call(n_shared=1, sw=A, dims=None):
+        return lib.moe_layer_forward_shared(ctypes.byref(_dims(**(dims or {}))), n_shared, A, A, None, A, A, A,
+                                            sw, sw, sw, A, None, None, None, None, None, None, None, A, 1 << 40,
+                                            None)
+    assert call(n_shared=0) == 1
+    assert call(n_shared=1017) == 1          # E + n_shared > 1024 with E = 8
+    assert call(sw=None) == 1
+    assert call(dims=dict(T=0)) == 0
+    base = lib.moe_workspace_bytes(ctypes.byref(_dims()))
+    assert lib.moe_workspace_bytes_shared(ctypes.byref(_dims()), 1) > 0
+    assert lib.moe_workspace_bytes_shared(ctypes.byref(_dims()), 2) > lib.moe_workspace_bytes_shared(
+        ctypes.byref(_dims()), 1)
+    assert lib.moe_workspace_bytes_shared(ctypes.byref(_dims()), 0) == 0
+    assert base > 0

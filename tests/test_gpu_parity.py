@@ -239,6 +239,35 @@ def test_gate_tile_configs_bit_exact(monkeypatch, gate_cfg, shape):
 
 
 # ---------------- full-size workloads ----------------
+SHARED_SHAPES = [
+    # T, d, f, E, k, shared experts, dtype
+    (300, 256, 192, 8, 2, 1, "bf16"),   # ragged m-blocks, FC2 column tail
+    (97, 128, 128, 16, 4, 2, "bf16"),   # two shared experts
+    (64, 128, 256, 8, 2, 1, "f32"),     # fp32 path
+]
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("shape", SHARED_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_S{}_{}".format(*s))
+def test_shared_experts_layer(monkeypatch, shape, path):
+    """moe_layer_forward_shared against the oracle: routing bit-exact, output within tolerance."""
+    T, d, f, E, k, S, dt = shape
+    _say(f"case shared {shape} {path}")
+    monkeypatch.setenv("MOE_DISPATCH", path)
+    inp = moe_inputs.random_inputs(T, d, f, E, k, dt, 1.0, seed=12, device="cuda", n_shared=S)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out, r = moe.layer_forward_shared(moe.Dims(T, d, f, E, k, tdt), inp["x"], inp["wg"], inp["bias"], inp["w1"],
+                                      inp["w3"], inp["w2"], inp["sw1"], inp["sw3"], inp["sw2"], return_routing=True)
+    torch.cuda.synchronize()
+    h = {n: to_numpy(v, dt) for n, v in inp.items()}
+    ref = oracle.layer_forward_shared(h["x"], h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], h["sw1"], h["sw3"],
+                                      h["sw2"], k, dt)
+    assert_routing_equal(r, ref)
+    err = rel_err(gpu_float(out), ref["out"])
+    _say(f"  out rel_err={err:.3e}")
+    assert err <= OUT_TOL
+
+
 FULL = ["mixtral_decode", "dbrx_bal", "dbrx_zipf", "mixtral_prefill_skew", "mixtral_prefill_bal",
         "deepseek_skew", "deepseek_bal"]
 
@@ -278,3 +307,27 @@ def test_measurement_probes_run():
     _say(f"  hbm read {gbps:.0f} GB/s, mfma {tflops:.0f} TFLOP/s")
     assert 1000 < gbps < 8000 * 1.05
     assert 300 < tflops < 2516.6 * 1.05
+
+
+@pytest.mark.timeout(600)
+def test_full_size_shared_workload():
+    """DeepSeek-V3-shaped layer with one shared expert: routing bit-exact, sampled rows."""
+    cfg = moe_inputs.config("deepseek_shared")
+    _say("case full deepseek_shared: generating inputs on the GPU")
+    inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    dims = _dims(cfg)
+    out, r = moe.layer_forward_shared(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                      inp["sw1"], inp["sw3"], inp["sw2"], return_routing=True)
+    torch.cuda.synchronize()
+    h = host_inputs(inp, cfg.dtype)
+    _say("  oracle routing")
+    ref = oracle_routing(h, cfg.k, cfg.dtype)
+    assert_routing_equal(r, ref)
+    toks = np.unique(np.linspace(0, cfg.T - 1, 8).astype(np.int64))
+    w1, w3, w2 = (LazyExperts(inp[n], cfg.dtype) for n in ("w1", "w3", "w2"))
+    routed = oracle.token_outputs(h["x"], ref["topk_idx"], ref["topk_w"], w1, w3, w2, toks, cfg.dtype)
+    sw = {n: to_numpy(inp[n], cfg.dtype) for n in ("sw1", "sw3", "sw2")}
+    shared = oracle.shared_expert_ffn(h["x"][toks], sw["sw1"], sw["sw3"], sw["sw2"], cfg.dtype).sum(axis=0)
+    err = rel_err(gpu_float(out[torch.from_numpy(toks).cuda()]), routed + shared)
+    _say(f"  sampled out rel_err={err:.3e} over {toks.size} tokens")
+    assert err <= OUT_TOL
