@@ -68,6 +68,8 @@ SMALL = [
     (96, 128, 256, 8, 2, "f32", 1.5),       # fp32 path with skew
     (9000, 128, 128, 64, 8, "bf16", 1.0),   # > 65536 assignments: multi-kernel dispatch + plan
     (64, 4096, 2048, 8, 2, "bf16", 0.0),    # decode-shaped: wide d and f, few rows per expert
+    (200, 64, 64, 1024, 4, "bf16", 1.0),    # the largest expert count
+    (40, 64, 128, 1024, 1024, "bf16", 0.0),  # k = E = 1024: every token to every expert
 ]
 
 
