@@ -339,10 +339,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   constexpr int BI = BN / (NW * RPI);      // B load instructions per wave per stage
   constexpr int LPS = AI + BI;             // loads per thread per stage
   constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MI = TM / 32, NJ = TN / 32;
-  constexpr int KS = BK / 16;              // MFMA sub-steps per stage
+  constexpr int MI = TM / 32;              // 32-row units of the wave's rows (padding granularity)
+  constexpr int MI16 = TM / 16, NJ16 = TN / 16;  // 16 x 16 MFMA blocks of the wave tile
+  constexpr int KS = BK / 32;              // MFMA sub-steps (K = 32) per stage
   static_assert(NW == 4 || NW == 8, "four or eight waves");
-  static_assert(!kGated || (NJ % 2 == 0), "gated tiles pair gate and up blocks");
+  static_assert(!kGated || (NJ16 % 2 == 0), "gated tiles pair gate and up blocks");
+  static_assert(KS == 2, "two 32-wide sub-steps per 64-wide stage");
   static_assert(AI * NW * RPI == BM && BI * NW * RPI == BN, "load tiling");
   // LDS: two A buffers, then as many B buffers (up to 8) as fit in the CU's
   // 160 KB, so weight loads run NBB-1 steps ahead
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
     return static_cast<uint32_t>(((lane % CPR) ^ ((r0_phase + lrow / R256) % CPR)) * 16);
   };
   constexpr int PH = (RPI / R256) % CPR;  // phase step per load instruction (0 or 4)
-  const int fsw = ((lane & 31) / R256) % CPR;                           // read-side swizzle of row (lane & 31)
+  const int fsw = ((lane & 15) / R256) % CPR;                           // read-side swizzle of row (lane & 15)
   // x spans T*K*2 bytes (< 2^32, checked on the host)
   const uint32_t a_bytes = kGated ? static_cast<uint32_t>(g.T * K * 2) : 0u;
 
@@ -442,13 +444,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       }
     }
 
-    f32x16_t acc[MI][NJ];
+    f32x4_t acc[MI16][NJ16];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI16; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < NJ16; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
     // Loads of K step kt into LDS slot `stage`. Steps past the end load from an
     // empty descriptor (zeros, no memory access) into a slot nobody reads
@@ -477,45 +479,51 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
             16, boff[i], koff, 0, 0);
       }
     };
-    // Only the wave's first MA 32-row blocks hold rows of the m-block; the
+    // bf16 MFMA 16x16x32 (under a sustained power limit it keeps a higher
+    // rate than 32x32x16: half the accumulator traffic per FLOP). Lane l holds
+    // row l % 16 and K elements 8 * (l / 16) .. +7 of an A or B fragment, and
+    // rows 4 * (l / 16) .. +3 of column l % 16 of the 16 x 16 result.
+    // Only the wave's first MA 32-row units hold rows of the m-block; the
     // others are padding, so their fragments are neither read nor multiplied
     // (their accumulators stay zero and are never stored).
-    bf16x8_t fa[2][MI], fb[2][NJ];  // two fragment register sets
-    auto read_sub = [&](auto ma_c, int set, int s, int a_slot, int b_slot) {
-      constexpr int MA = decltype(ma_c)::value;
+    // Fragments: fb[set] double-buffered per 32-wide sub-step; fa[i] refilled
+    // with the next sub-step's row block i as soon as block i's MFMAs are issued.
+    bf16x8_t fa[MI16], fb[2][NJ16];
+    auto ck_of = [&](int s) { return (((4 * s + (lane >> 4)) ^ fsw) % CPR) * 16; };
+    auto read_a = [&](int i, int s, int a_slot) {
       const char* sa = lds + a_slot * A_ST;
+      fa[i] = *reinterpret_cast<const bf16x8_t*>(sa + (wm * TM + 16 * i + (lane & 15)) * RB + ck_of(s));
+    };
+    auto read_b = [&](int set, int s, int b_slot) {
       const char* sb = lds + NBA * A_ST + b_slot * B_ST;
-      const int ck = (((2 * s + (lane >> 5)) ^ fsw) % CPR) * 16;
-      // B first: the first MFMA of a sub-step needs fb[0] and fa[0]
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < NJ16; ++j) {
         int brow;
         if constexpr (kGated)
-          brow = (j < NJ / 2 ? 0 : BN / 2) + wn * (TN / 2) + 32 * (j % (NJ / 2)) + (lane & 31);
+          brow = (j < NJ16 / 2 ? 0 : BN / 2) + wn * (TN / 2) + 16 * (j % (NJ16 / 2)) + (lane & 15);
         else
-          brow = wn * TN + 32 * j + (lane & 31);
-        fb[set][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow * RB + ck);
+          brow = wn * TN + 16 * j + (lane & 15);
+        fb[set][j] = *reinterpret_cast<const bf16x8_t*>(sb + brow * RB + ck_of(s));
       }
-#pragma unroll
-      for (int i = 0; i < MA; ++i)
-        fa[set][i] = *reinterpret_cast<const bf16x8_t*>(sa + (wm * TM + 32 * i + (lane & 31)) * RB + ck);
     };
-
-    auto mfmas = [&](auto ma_c, int set) {
-      constexpr int MA = decltype(ma_c)::value;
+    // MFMAs of sub-step `set` over the first MA16 row blocks, each block's A
+    // fragment then refilled with sub-step ns of A buffer a_slot
+    auto mfma_refill = [&](auto ma_c, int set, int ns, int a_slot) {
+      constexpr int MA16 = 2 * decltype(ma_c)::value < MI16 ? 2 * decltype(ma_c)::value : MI16;
 #pragma unroll
-      for (int i = 0; i < MA; ++i)
+      for (int i = 0; i < MA16; ++i) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ16; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[set][j], acc[i][j], 0, 0, 0);
+        read_a(i, ns, a_slot);
+      }
     };
 
     auto kloop = [&](auto ma_c) {
-      constexpr int MA = decltype(ma_c)::value;
-      // fa/fb[set]: set s & 1 holds sub-step s of the current stage. Step j
-      // uses A buffer j & 1 and B buffer j % NBB; both are free once every
-      // wave passed step j's barrier (its reads are done by then), so the
-      // loads of A for step j+2 and of B for step j+NBB are issued right
+      constexpr int MA16 = 2 * decltype(ma_c)::value < MI16 ? 2 * decltype(ma_c)::value : MI16;
+      // Step j uses A buffer j & 1 and B buffer j % NBB; both are free once
+      // every wave passed step j's barrier (its reads are done by then), so
+      // the loads of A for step j+2 and of B for step j+NBB are issued right
       // there, in that order. vmcnt counts in issue order, so the prologue
       // issues as the steps before step 0 would have: B0 .. B(NBB-3), A0,
       // B(NBB-2), A1, B(NBB-1) (two buffers: B0 A0 A1 B1). At step kt's
@@ -536,32 +544,33 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       }
       wait_vmcnt<(NBB == 2 ? AI + BI : AI + 2 * BI)>();  // A0 and B0 landed
       lds_barrier();
-      if constexpr (MA > 0) read_sub(ma_c, 0, 0, 0, 0);
+      if constexpr (MA16 > 0) {
+        read_b(0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < MA16; ++i) read_a(i, 0, 0);
+      }
       int bsl = 0;  // B buffer of step kt
       for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const int bnx = bsl + 1 == NBB ? 0 : bsl + 1;
-        if constexpr (MA > 0) {
-          // one scheduling region per sub-step: its MFMAs (set s & 1) with
-          // the reads of sub-step s+1 (the other set)
-          constexpr int M = MA * NJ, R = MA + NJ, G = M > R ? M : R;
-#pragma unroll
-          for (int s = 0; s < KS - 1; ++s) {
-            mfmas(ma_c, s & 1);
-            read_sub(ma_c, (s + 1) & 1, s + 1, cur, bsl);
-            interleave_mfma_ds_vmem<M, R, 0, 1>(std::make_integer_sequence<int, G>{});
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        constexpr int M = MA16 * NJ16, R = MA16 + NJ16, G = M > R ? M : R;
+        if constexpr (MA16 > 0) {
+          // sub-step 0: its MFMAs with the reads of sub-step 1 (same buffers)
+          read_b(1, 1, bsl);
+          mfma_refill(ma_c, 0, 1, cur);
+          interleave_mfma_ds_vmem<M, R, 0, 1>(std::make_integer_sequence<int, G>{});
+          __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmcnt<(NBB == 2 ? 0 : BI)>();  // this thread's loads of step kt+1 landed
         wait_lds_reads();  // and its reads of step kt's buffers are done: they may be refilled after the barrier
         lds_barrier();
         issue_a(cur, kt + 2);
         issue_b(bsl, kt + NBB);
-        if constexpr (MA > 0) {
-          mfmas(ma_c, (KS - 1) & 1);
-          read_sub(ma_c, 0, 0, cur ^ 1, bnx);  // on the last step: zeros, unused
-          constexpr int M = MA * NJ, R = MA + NJ, G = M > R ? M : R;
+        if constexpr (MA16 > 0) {
+          // sub-step 1: its MFMAs with the reads of step kt+1's sub-step 0
+          // (on the last step: zeros, unused)
+          read_b(0, 0, bnx);
+          mfma_refill(ma_c, 1, 0, cur ^ 1);
           interleave_mfma_ds_vmem<M, R, LPS, G>(std::make_integer_sequence<int, G>{});
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -590,20 +599,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
     lds_barrier();
     bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MI16; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * TM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      for (int v = 0; v < 4; ++v) {
+        const int r = wm * TM + 16 * i + 4 * (lane >> 4) + v;
         if constexpr (kGated) {
 #pragma unroll
-          for (int j = 0; j < NJ / 2; ++j) {
-            const int c = wn * (TN / 2) + 32 * j + (lane & 31);
-            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + NJ / 2][v])));
+          for (int j = 0; j < NJ16 / 2; ++j) {
+            const int c = wn * (TN / 2) + 16 * j + (lane & 15);
+            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + NJ16 / 2][v])));
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int c = wn * TN + 32 * j + (lane & 31);
+          for (int j = 0; j < NJ16; ++j) {
+            const int c = wn * TN + 16 * j + (lane & 15);
             ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
           }
         }
