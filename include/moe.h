@@ -198,9 +198,9 @@ int moe_probe_cus(void);
  * MOE_ERR_INVALID for a null or misaligned pointer or a bad size,
  * MOE_ERR_UNSUPPORTED if a slice would be empty or too large. */
 int moe_probe_hbm_read(const void* src, size_t bytes, int32_t* sink, void* stream);
-/* `iters` rounds of 16 bf16 32x32x16 MFMAs (four independent accumulator
- * chains) in each of 8 waves per CU, register operands only:
- * FLOP = 2*32*32*16 * 16 * 8 * iters * CUs. sink [8 * CUs] fp32 receives each
+/* `iters` rounds of 32 bf16 16x16x32 MFMAs (eight independent accumulator
+ * chains) in each of 8 waves per CU, register operands with varied bits only:
+ * FLOP = 2*16*16*32 * 32 * 8 * iters * CUs. sink [8 * CUs] fp32 receives each
  * wave's accumulator sum. MOE_ERR_INVALID for a null sink or iters < 1. */
 int moe_probe_mfma(int iters, float* sink, void* stream);
 

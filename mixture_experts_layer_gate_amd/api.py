@@ -312,8 +312,9 @@ def probe_hbm_read_gbps(nbytes: int = 2 << 30, reps: int = 5, stream=None) -> fl
     return slice_bytes * lib.moe_probe_cus() / (best * 1e-3) / 1e9
 
 
-def probe_mfma_tflops(iters: int = 20000, reps: int = 3, stream=None) -> float:
-    """Best-of-reps bf16 MFMA rate (TFLOP/s) of the library's register-only MFMA probe."""
+def probe_mfma_tflops(iters: int = 100000, reps: int = 3, stream=None) -> float:
+    """Best-of-reps bf16 MFMA rate (TFLOP/s) of the library's register-only MFMA probe
+    (about 50 ms per launch, long enough for the clock to settle at its power limit)."""
     lib = load_library()
     cus = lib.moe_probe_cus()
     sink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
@@ -328,4 +329,4 @@ def probe_mfma_tflops(iters: int = 20000, reps: int = 3, stream=None) -> float:
         if i:
             ms = e0.elapsed_time(e1)
             best = ms if best is None else min(best, ms)
-    return 2 * 32 * 32 * 16 * 16 * 8 * iters * cus / (best * 1e-3) / 1e12
+    return 524288 * 8 * iters * cus / (best * 1e-3) / 1e12

@@ -259,14 +259,14 @@ __global__ __launch_bounds__(kThreads, kDtype == 1 ? 2 : 1) void grouped_gemm_ke
 // Large-tile variant for experts with many rows: tile BM x BN, K step 64,
 // LDS buffers filled by buffer loads straight into LDS (buffer_load_dwordx4
 // ... lds: lane i's 16 bytes land at M0 + 16 * i), 128-byte row segments.
-// WM x WN waves, each (BM/WM) x (BN/WN) with 32x32x16 bf16 MFMAs. A has two
+// WM x WN waves, each (BM/WM) x (BN/WN) with 16x16x32 bf16 MFMAs. A has two
 // LDS buffers, B three (2 x 32 + 3 x 32 KB: the CU's whole 160 KB). After
-// the third of the four 16-wide sub-steps of step kt every wave waits for
+// the first of the two 32-wide sub-steps of step kt every wave waits for
 // the loads of step kt+1 and meets at the one barrier of the step; step
 // kt's buffers are then free, and the loads of A for step kt+2 and of B for
 // step kt+3 go out at once (weights, mostly first touches from HBM, get the
-// longer lead). The last sub-step's MFMAs hide the LDS reads of step kt+1's
-// first sub-step. Fragments alternate between two register sets, one
+// longer lead). The second sub-step's MFMAs hide the LDS reads of step kt+1's
+// first sub-step. B fragments alternate between two register sets, one
 // sub-step ahead of the MFMAs, and scheduling groups interleave the reads
 // and the load issue with the MFMAs.
 // On the Mixtral-8x22B prefill FC1 the loop is power-bound: with the loads

@@ -4,8 +4,9 @@
 // * hbm_read_probe: one workgroup of 8 waves per CU streams a contiguous slice
 //   of a device buffer into LDS with 16-byte buffer loads (the same load form
 //   the grouped GEMM uses), 32 KiB per step, three steps in flight.
-// * mfma_probe: 8 waves per CU each run four independent chains of bf16
-//   32x32x16 MFMAs on register operands; no memory traffic.
+// * mfma_probe: 8 waves per CU each run eight independent chains of bf16
+//   16x16x32 MFMAs (the GEMM's form) on register operands; no memory traffic.
+//   Each wave does 4 x 8 x 16384 = 524288 FLOP per iteration.
 #include <stdint.h>
 
 #include "common.h"
@@ -44,28 +45,30 @@ __global__ __launch_bounds__(kProbeThreads, 1) void hbm_read_probe(const char* s
 
 __global__ __launch_bounds__(kProbeThreads, 1) void mfma_probe(int iters, float* sink) {
   const int tid = threadIdx.x;
+  // operands with varied mantissa bits, as real activations and weights have: the
+  // MFMA pipes' power, and so the clock they sustain, depends on how many bits toggle
   bf16x8_t a, b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a[i] = static_cast<__bf16>(static_cast<float>((tid + i) & 7) * 0.125f);
-    b[i] = static_cast<__bf16>(static_cast<float>((tid * 3 + i) & 7) * 0.0625f);
+    a[i] = static_cast<__bf16>(static_cast<float>((tid * 7 + i) % 13) * 0.07f - 0.4f);
+    b[i] = static_cast<__bf16>(static_cast<float>((tid * 5 + i * 3) % 11) * 0.09f - 0.5f);
   }
-  f32x16_t acc[4];
+  f32x4_t acc[8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+    for (int v = 0; v < 4; ++v) acc[c][v] = 0.0f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
   }
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s += acc[c][v];
+    for (int v = 0; v < 4; ++v) s += acc[c][v];
   if ((tid & 63) == 0) sink[blockIdx.x * (kProbeThreads / 64) + (tid >> 6)] = s;
 }
 
