@@ -159,6 +159,43 @@ int moe_layer_forward_shared(const moe_dims_t* dims, int n_shared, const void* x
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward pass ----
+ * Gradients of the layer for a scalar loss whose gradient with respect to
+ * `out` is `dout`. The pages name the parts (MegaFlux, section 2.1: token
+ * blocks stream through DGrad and WGrad, and the final top-k sum is a step of
+ * its own; section 3.2 and Figure 2); the formulas are the chain rule of the
+ * forward: per assignment (t, j) of expert e with weight w,
+ *   dtopk_w[t][j] = dout_t . y,   dW2_e += (w dout_t) h^T,
+ *   dg = (W2_e^T w dout_t) * u * SiLU'(g),  du = (W2_e^T w dout_t) * SiLU(g),
+ *   dW1_e += dg x_t^T,  dW3_e += du x_t^T,  dx_t += W1_e^T dg + W3_e^T du,
+ * then the softmax over the k selected logits,
+ *   dlogits[t][e_j] = w_j (dtopk_w[t][j] - sum_i w_i dtopk_w[t][i]) (0 elsewhere),
+ * and the gate: dbias = column sums of dlogits, dwg = dlogits^T x,
+ * dx += dlogits wg. The selection itself is piecewise constant and gets no
+ * gradient.
+ *
+ * Inputs: the forward's inputs (bf16 only: dims->dtype must be MOE_DTYPE_BF16)
+ * and its routing outputs topk_idx, topk_w, counts, offsets, perm, inv_perm
+ * (exactly as moe_layer_forward or moe_route + moe_permute return them), and
+ * dout [T][d] bf16. Outputs (device, caller-allocated): dx [T][d] bf16;
+ * dwg [E][d], dbias [E], dw1 [E][f][d], dw3 [E][f][d], dw2 [E][d][f] fp32
+ * (every entry written, zero for experts that received no rows); optional
+ * (NULL to skip) dlogits [T][E] and dtopk_w [T][k] fp32.
+ * FC1 is recomputed (g and u are not kept by the forward); the weights are
+ * transposed into the workspace each call. Accumulation is fp32 throughout;
+ * dg, du, h and w*dout enter the matrix products as bf16. Every reduction
+ * has a fixed order: results are deterministic.
+ * Limits: d and f multiples of 256, else MOE_ERR_UNSUPPORTED; pointers
+ * 16-byte aligned (4 for the int32 / fp32 routing arrays); ws at least
+ * moe_backward_workspace_bytes(dims), 256-byte aligned. T == 0 writes zero
+ * weight gradients. Asynchronous on `stream`. */
+size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
+int moe_layer_backward(const moe_dims_t* dims, const void* x, const void* wg, const void* w1, const void* w3,
+                       const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
+                       void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2,
+                       float* dlogits, float* dtopk_w, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- stage timing (instrumentation; process-wide, not thread-safe) ----
  * While enabled, every kernel the library launches is bracketed by HIP events
  * recorded on the stream it is launched on. Stages: */
@@ -173,7 +210,18 @@ enum {
   MOE_STAGE_FC2 = 7,      /* grouped FC2 */
   MOE_STAGE_COMBINE = 8,  /* weighted combine */
   MOE_STAGE_DISPATCH = 9, /* single-workgroup histogram + scan + scatter (+ tile plan) */
-  MOE_NUM_STAGES = 10
+  MOE_STAGE_BWD_WT = 10,      /* backward: weight transposes */
+  MOE_STAGE_BWD_FC1 = 11,     /* backward: FC1 recompute (g | u) */
+  MOE_STAGE_BWD_DH = 12,      /* backward: DGrad of FC2 (q = dout W2) */
+  MOE_STAGE_BWD_SWIGLU = 13,  /* backward: dg | du and dtopk_w */
+  MOE_STAGE_BWD_ROUTE = 14,   /* backward: softmax over the selected logits */
+  MOE_STAGE_BWD_DX = 15,      /* backward: DGrad of FC1 */
+  MOE_STAGE_BWD_DXSUM = 16,   /* backward: per-token dx sum (+ gate part) */
+  MOE_STAGE_BWD_ACT_T = 17,   /* backward: activation transposes for WGrad */
+  MOE_STAGE_BWD_WG2 = 18,     /* backward: WGrad of W2 */
+  MOE_STAGE_BWD_WG13 = 19,    /* backward: WGrad of W1 and W3 */
+  MOE_STAGE_BWD_GATE = 20,    /* backward: gate weight and bias gradients */
+  MOE_NUM_STAGES = 21
 };
 /* Start recording; `capacity` = launches per stage to keep (host memory only);
  * `stage_mask` = bit s set records stage s (0 = every stage). Discards

@@ -17,14 +17,17 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmoe_amd.so"
 
-STAGES = ["gate", "topk", "hist", "scan", "scatter", "plan", "fc1", "fc2", "combine", "dispatch"]
+STAGES = ["gate", "topk", "hist", "scan", "scatter", "plan", "fc1", "fc2", "combine", "dispatch",
+          "bwd_wt", "bwd_fc1", "bwd_dh", "bwd_swiglu", "bwd_route", "bwd_dx", "bwd_dxsum", "bwd_act_t",
+          "bwd_wg2", "bwd_wg13", "bwd_gate"]
 MOE_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 # Every symbol include/moe.h declares.
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
-           "moe_workspace_bytes_shared", "moe_layer_forward_shared"]
+           "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
+           "moe_layer_backward"]
 
 
 class MoeError(RuntimeError):
@@ -83,13 +86,16 @@ def load_library():
     lib.moe_workspace_bytes_shared.restype = _S
     lib.moe_workspace_bytes_shared.argtypes = [_DP, ctypes.c_int]
     lib.moe_layer_forward_shared.argtypes = [_DP, ctypes.c_int] + [_P] * 18 + [_S, _P]
+    lib.moe_backward_workspace_bytes.restype = _S
+    lib.moe_backward_workspace_bytes.argtypes = [_DP]
+    lib.moe_layer_backward.argtypes = [_DP] + [_P] * 21 + [_S, _P]
     lib.moe_timing_enable.argtypes = [ctypes.c_int, ctypes.c_uint]
     lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.moe_probe_cus.restype = ctypes.c_int
     lib.moe_probe_hbm_read.argtypes = [_P, _S, _P, _P]
     lib.moe_probe_mfma.argtypes = [ctypes.c_int, _P, _P]
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-               "moe_layer_forward_shared",
+               "moe_layer_forward_shared", "moe_layer_backward",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -272,6 +278,56 @@ def layer_forward_shared(dims: Dims, x, wg, bias, w1, w3, w2, sw1, sw3, sw2, out
         _ptr(g("counts")), _ptr(g("offsets")), _ptr(g("perm")), _ptr(g("inv_perm")), _ptr(ws), ws.numel(),
         _stream(stream)))
     return (out, r) if return_routing else out
+
+
+def backward_workspace_bytes(dims: Dims) -> int:
+    return int(load_library().moe_backward_workspace_bytes(ctypes.byref(dims.c())))
+
+
+def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, stream=None,
+                   want_dlogits=False, want_dtopk_w=False, grads=None):
+    """Gradients of the layer for output gradient dout [T][d] (bf16).
+
+    routing: the forward's topk_idx, topk_w, counts, offsets, perm, inv_perm
+    (layer_forward(..., return_routing=True)). Returns a dict with dx [T][d]
+    (bf16), dwg [E][d], dbias [E], dw1, dw3 [E][f][d], dw2 [E][d][f] (fp32) and,
+    when asked for, dlogits [T][E] and dtopk_w [T][k]. ``grads`` may hold
+    preallocated output tensors under those names."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    _need(wg, "wg", dims.dtype, (dims.E, dims.d))
+    _need(dout, "dout", dims.dtype, (dims.T, dims.d))
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    n = dims.T * dims.k
+    for name, dt, shp in (("topk_idx", torch.int32, (dims.T, dims.k)), ("topk_w", torch.float32, (dims.T, dims.k)),
+                          ("counts", torch.int32, (dims.E,)), ("offsets", torch.int32, (dims.E + 1,)),
+                          ("perm", torch.int32, (n,)), ("inv_perm", torch.int32, (n,))):
+        _need(routing[name], name, dt, shp)
+    g = dict(grads or {})
+    f32 = torch.float32
+    shapes = {"dx": ((dims.T, dims.d), dims.dtype), "dwg": ((dims.E, dims.d), f32), "dbias": ((dims.E,), f32),
+              "dw1": ((dims.E, dims.f, dims.d), f32), "dw3": ((dims.E, dims.f, dims.d), f32),
+              "dw2": ((dims.E, dims.d, dims.f), f32)}
+    if want_dlogits:
+        shapes["dlogits"] = ((dims.T, dims.E), f32)
+    if want_dtopk_w:
+        shapes["dtopk_w"] = ((dims.T, dims.k), f32)
+    for name, (shp, dt) in shapes.items():
+        if name not in g:
+            g[name] = torch.empty(shp, dtype=dt, device=dev)
+        _need(g[name], name, dt, shp)
+    if ws is None:
+        ws = torch.empty(max(backward_workspace_bytes(dims), 256), dtype=torch.uint8, device=dev)
+    _check("moe_layer_backward", lib.moe_layer_backward(
+        ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(routing["topk_idx"]),
+        _ptr(routing["topk_w"]), _ptr(routing["counts"]), _ptr(routing["offsets"]), _ptr(routing["perm"]),
+        _ptr(routing["inv_perm"]), _ptr(dout), _ptr(g["dx"]), _ptr(g["dwg"]), _ptr(g["dbias"]), _ptr(g["dw1"]),
+        _ptr(g["dw3"]), _ptr(g["dw2"]), _ptr(g.get("dlogits")), _ptr(g.get("dtopk_w")), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return g
 
 
 def timing_enable(capacity: int, stages=None):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_amd.so")
 ARCH = "gfx950"
-SOURCES = ["route.hip", "dispatch.hip", "ffn.hip", "combine.hip", "moe_abi.hip", "probes.hip"]
+SOURCES = ["route.hip", "dispatch.hip", "ffn.hip", "combine.hip", "backward.hip", "moe_abi.hip", "probes.hip"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # no packed-fp32 instructions in any generated code

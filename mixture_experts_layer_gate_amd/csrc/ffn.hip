@@ -45,6 +45,13 @@ struct GemmArgs {
   const void* S0;         // shared experts' W1 (FC1) or W2 (FC2), [S][N][K]
   const void* S1;         // shared experts' W3 (FC1)
   int E_routed;           // experts e >= E_routed are shared expert e - E_routed
+  // weight gradients only (C[e] = A_e B_e^T with K = the expert's padded rows):
+  void* C2;               // second output tensor, for output rows >= split
+  const int32_t* kofs;    // [E+1] first padded column of each expert in A and B
+  int64_t pitch;          // row pitch (elements) of the transposed operands A and B
+  int64_t M;              // output rows per expert (rows of A)
+  int64_t split;          // output rows per output tensor (M, or M / 2 with C2)
+  int n_experts;
 };
 
 // Token of sorted row p (FC1): routed rows through perm, shared rows directly.
@@ -323,11 +330,28 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kGated, int BM, int BN, int WM, int WN>
+// What a large-tile launch computes. Every form is C = A B^T over 64-wide K
+// steps with both operands K-contiguous; they differ in where A rows come
+// from, which B rows pair up, and the epilogue.
+enum GemmMode : int {
+  kModeFc1 = 0,    // h = SiLU(x W1^T) * (x W3^T), A rows gathered by token, bf16 out
+  kModeFc2 = 1,    // y = h W2^T, A = the m-block's rows, bf16 out
+  kModeFc1GU = 2,  // g | u = x W1^T | x W3^T stored side by side ([rows][2N] bf16): the backward's recompute
+  kModeBwdQ = 3,   // q = dout W2 (B = W2 transposed), A rows gathered by token, fp32 out
+  kModeBwdDx = 4,  // dx rows = [dg | du] [W1 ; W3] (B = both transposed, K = 2f), fp32 out
+  kModeWgrad = 5,  // dW_e = A_e B_e^T, K = expert e's padded rows, fp32 out
+};
+__host__ __device__ constexpr bool mode_gated(int m) { return m == kModeFc1 || m == kModeFc1GU; }
+__host__ __device__ constexpr bool mode_gather(int m) { return m == kModeFc1 || m == kModeFc1GU || m == kModeBwdQ; }
+__host__ __device__ constexpr bool mode_f32_out(int m) { return m >= kModeBwdQ; }
+
+template <int kMode, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   // device-only body: the buffer-resource builtins have no host form, and the
   // host pass only needs the kernel's launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool kGated = mode_gated(kMode);
+  constexpr bool kWgrad = kMode == kModeWgrad;
   constexpr int BK = 64;                   // K per step
   constexpr int RB = BK * 2;               // bytes per LDS row
   constexpr int CPR = RB / 16;             // 16-byte chunks per row
@@ -360,10 +384,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   const int wm = wv / WN, wn = wv % WN;
   const int64_t K = g.K, N = g.N;
-  const int nmb = g.n_mblocks[0];
   const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
+  // weight gradients: every expert has M / BM m-blocks of output rows
+  const int mbe = kWgrad ? static_cast<int>(g.M / BM) : 0;
+  const int nmb = kWgrad ? g.n_experts * mbe : g.n_mblocks[0];
   const int64_t ntiles = static_cast<int64_t>(nmb) * nbc;
-  const int nk = static_cast<int>(K / BK);
+  int nk = static_cast<int>(K / BK);
   const int lrow = lane / CPR;                                          // row within a load instruction
   // Chunk this lane fetches for a load instruction whose first row is R0.
   // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
@@ -375,7 +401,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   constexpr int PH = (RPI / R256) % CPR;  // phase step per load instruction (0 or 4)
   const int fsw = ((lane & 15) / R256) % CPR;                           // read-side swizzle of row (lane & 15)
   // x spans T*K*2 bytes (< 2^32, checked on the host)
-  const uint32_t a_bytes = kGated ? static_cast<uint32_t>(g.T * K * 2) : 0u;
+  const uint32_t a_bytes = mode_gather(kMode) ? static_cast<uint32_t>(g.T * K * 2) : 0u;
 
   // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
   // b % 8). Renumber so that the gridDim/8 workgroups of one XCD take
@@ -383,51 +409,85 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
   for (int64_t tile = slot; tile < ntiles; tile += G) {
-    // Tiles run group by group (the plan's runs of up to kTileGroup m-blocks
-    // of one expert), m-block-fastest inside a group; a malformed group entry
-    // falls back to a group of one.
-    const int row = static_cast<int>(tile / nbc);
-    const int info = g.mblocks[row].w;
-    int m0 = info >> 4, gs = info & 15;
-    if (gs < 1 || gs > kTileGroup || m0 > row || row >= m0 + gs || m0 + gs > nmb) m0 = row, gs = 1;
-    const int64_t o = tile - static_cast<int64_t>(m0) * nbc;
-    const int mb = m0 + static_cast<int>(o % gs);
-    const int nb = static_cast<int>(o / gs);
-    const int4 blk = g.mblocks[mb];
-    const int e = __builtin_amdgcn_readfirstlane(blk.x);
-    const int row0 = __builtin_amdgcn_readfirstlane(blk.y);
-    const int rows = __builtin_amdgcn_readfirstlane(blk.z);
-
-    // A: FC1 gathers token rows of x; FC2 reads rows row0.. of h. Rows past the
-    // block's end get an offset at the descriptor's size: the load returns zeros
-    // and makes no memory request.
+    int mb, nb, e, row0, rows;
     __amdgpu_buffer_rsrc_t ars;
     uint32_t aoff[AI];
-    if constexpr (kGated) {
-      ars = make_rsrc(g.A, a_bytes);
+    if constexpr (kWgrad) {
+      // expert-major, m-block fastest: neighbouring tiles share a B panel
+      const int64_t per_e = static_cast<int64_t>(mbe) * nbc;
+      e = static_cast<int>(tile / per_e);
+      const int r = static_cast<int>(tile % per_e);
+      mb = r % mbe;
+      nb = r / mbe;
+      const int k0 = g.kofs[e], k1 = g.kofs[e + 1];
+      nk = (k1 - k0) / BK;
+      row0 = mb * BM;
+      rows = BM;
+      // A_e: rows row0.. of the transposed operand, K window from column k0
+      const uint32_t bytes = static_cast<uint32_t>((g.M * g.pitch - k0) * 2);
+      ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(k0) * 2, bytes);
 #pragma unroll
       for (int i = 0; i < AI; ++i) {
-        const int r = (wv * AI + i) * RPI + lrow;
-        if (r < rows) {
-          const int64_t tok = row_token(g, row0 + r);
-          aoff[i] = static_cast<uint32_t>(tok * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
-        } else {
-          aoff[i] = a_bytes;
-        }
+        const int r2 = (wv * AI + i) * RPI + lrow;
+        aoff[i] = static_cast<uint32_t>((row0 + r2) * g.pitch * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
       }
     } else {
-      const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * K * 2);
-      ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(row0) * K * 2, hb);
+      // Tiles run group by group (the plan's runs of up to kTileGroup m-blocks
+      // of one expert), m-block-fastest inside a group; a malformed group entry
+      // falls back to a group of one.
+      const int row = static_cast<int>(tile / nbc);
+      const int info = g.mblocks[row].w;
+      int m0 = info >> 4, gs = info & 15;
+      if (gs < 1 || gs > kTileGroup || m0 > row || row >= m0 + gs || m0 + gs > nmb) m0 = row, gs = 1;
+      const int64_t o = tile - static_cast<int64_t>(m0) * nbc;
+      mb = m0 + static_cast<int>(o % gs);
+      nb = static_cast<int>(o / gs);
+      const int4 blk = g.mblocks[mb];
+      e = __builtin_amdgcn_readfirstlane(blk.x);
+      row0 = __builtin_amdgcn_readfirstlane(blk.y);
+      rows = __builtin_amdgcn_readfirstlane(blk.z);
+
+      // A: FC1 gathers token rows of x; FC2 reads rows row0.. of h. Rows past the
+      // block's end get an offset at the descriptor's size: the load returns zeros
+      // and makes no memory request.
+      if constexpr (mode_gather(kMode)) {
+        ars = make_rsrc(g.A, a_bytes);
 #pragma unroll
-      for (int i = 0; i < AI; ++i) {
-        const int r = (wv * AI + i) * RPI + lrow;
-        aoff[i] = r < rows ? static_cast<uint32_t>(r * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR) : hb;
+        for (int i = 0; i < AI; ++i) {
+          const int r = (wv * AI + i) * RPI + lrow;
+          if (r < rows) {
+            const int64_t tok = row_token(g, row0 + r);
+            aoff[i] = static_cast<uint32_t>(tok * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
+          } else {
+            aoff[i] = a_bytes;
+          }
+        }
+      } else {
+        const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * K * 2);
+        ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(row0) * K * 2, hb);
+#pragma unroll
+        for (int i = 0; i < AI; ++i) {
+          const int r = (wv * AI + i) * RPI + lrow;
+          aoff[i] = r < rows ? static_cast<uint32_t>(r * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR) : hb;
+        }
       }
     }
-    // B: weight rows of expert e (gated: first half W1, second half W3, same columns).
+    // B: weight rows of expert e (gated: first half W1, second half W3, same
+    // columns); weight gradients: rows of the transposed operand, K window of expert e.
     __amdgpu_buffer_rsrc_t brs0, brs1;
     uint32_t boff[BI];
-    {
+    if constexpr (kWgrad) {
+      const int k0 = g.kofs[e];
+      brs0 = make_rsrc(static_cast<const char*>(g.B0) + static_cast<int64_t>(k0) * 2,
+                       static_cast<uint32_t>((N * g.pitch - k0) * 2));
+      brs1 = brs0;
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int r = (wv * BI + i) * RPI + lrow;
+        boff[i] = static_cast<uint32_t>((static_cast<int64_t>(nb) * BN + r) * g.pitch * 2) +
+                  chunk_off(((wv * BI + i) * PH) % CPR);
+      }
+    } else {
       const int64_t ebytes = N * K * 2;
       brs0 = make_rsrc(expert_base(g, g.B0, g.S0, e, ebytes), static_cast<uint32_t>(ebytes));
       brs1 = kGated ? make_rsrc(expert_base(g, g.B1, g.S1, e, ebytes), static_cast<uint32_t>(ebytes)) : brs0;
@@ -592,9 +652,50 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       }
     }
 
+    if constexpr (mode_f32_out(kMode)) {
+      // fp32 epilogue through LDS, one 16-row block i of every wave's rows at a
+      // time (so the accumulators of block i die as it is stored): the waves
+      // write acc[i] into a [WM * 16][BN + 4] tile (the 4-float pad spreads a
+      // fragment's 4-row steps over distinct banks), then all threads store
+      // 16-byte row chunks.
+      constexpr int CP = BN + 4;
+      constexpr int SR = WM * 16;  // rows per slice
+      static_assert(SR * CP * 4 <= LDS_BYTES, "slice fits in the stage buffers");
+      float* ct = reinterpret_cast<float*>(lds);
+      float* cbase;
+      if constexpr (kWgrad) {
+        const int64_t m0 = static_cast<int64_t>(row0);
+        const bool second = m0 >= g.split;
+        cbase = static_cast<float*>(second ? g.C2 : g.C) + static_cast<int64_t>(e) * g.split * N +
+                (second ? m0 - g.split : m0) * N;
+      } else {
+        cbase = static_cast<float*>(g.C) + static_cast<int64_t>(row0) * N;
+      }
+      const int64_t col0 = static_cast<int64_t>(nb) * BN;
+      constexpr int VPR = BN / 4;  // 16-byte vectors per tile row
+#pragma unroll
+      for (int i = 0; i < MI16; ++i) {
+        lds_barrier();
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < NJ16; ++j)
+            ct[(wm * 16 + 4 * (lane >> 4) + v) * CP + wn * TN + 16 * j + (lane & 15)] = acc[i][j][v];
+        __syncthreads();
+        for (int q = tid; q < SR * VPR; q += NT) {
+          const int rl = q / VPR, c4 = (q % VPR) * 4;
+          const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
+          if (r < rows && col0 + c4 < N)
+            *reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * N + col0 + c4) =
+                *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
+        }
+      }
+    } else {
     // Epilogue through LDS: every wave writes its fragment values (bf16) into a
     // row-major [BM][CW] tile, then all threads store whole 16-byte row chunks.
-    constexpr int CW = kGated ? BN / 2 : BN;  // output columns of the tile
+    // The recompute form keeps g and u apart: columns 0..BN/2-1 of the tile
+    // are g, the rest u, stored to the two halves of a [rows][2N] row.
+    constexpr int CW = (kGated && kMode != kModeFc1GU) ? BN / 2 : BN;  // output columns of the tile
     static_assert(BM * CW * 2 <= LDS_BYTES, "epilogue tile fits in the stage buffers");
     lds_barrier();
     bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
@@ -603,7 +704,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = wm * TM + 16 * i + 4 * (lane >> 4) + v;
-        if constexpr (kGated) {
+        if constexpr (kMode == kModeFc1GU) {
+#pragma unroll
+          for (int j = 0; j < NJ16 / 2; ++j) {
+            const int c = wn * (TN / 2) + 16 * j + (lane & 15);
+            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
+            ct[r * CW + BN / 2 + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j + NJ16 / 2][v]));
+          }
+        } else if constexpr (kGated) {
 #pragma unroll
           for (int j = 0; j < NJ16 / 2; ++j) {
             const int c = wn * (TN / 2) + 16 * j + (lane & 15);
@@ -621,14 +729,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
     __syncthreads();
     {
       bf16_t* C = static_cast<bf16_t*>(g.C);
-      const int64_t col0 = static_cast<int64_t>(nb) * CW;
       constexpr int VPR = CW / 8;  // 16-byte vectors per tile row
-      for (int q = tid; q < rows * VPR; q += NT) {
-        const int r = q / VPR, c8 = (q % VPR) * 8;
-        if (col0 + c8 < N)
-          *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
-              *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
+      if constexpr (kMode == kModeFc1GU) {
+        const int64_t col0 = static_cast<int64_t>(nb) * (BN / 2);
+        for (int q = tid; q < rows * VPR; q += NT) {
+          const int r = q / VPR, c8 = (q % VPR) * 8;
+          const int cc = c8 % (BN / 2);
+          if (col0 + cc < N)
+            *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * 2 * N + (c8 >= BN / 2 ? N : 0) + col0 + cc) =
+                *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
+        }
+      } else {
+        const int64_t col0 = static_cast<int64_t>(nb) * CW;
+        for (int q = tid; q < rows * VPR; q += NT) {
+          const int r = q / VPR, c8 = (q % VPR) * 8;
+          if (col0 + c8 < N)
+            *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
+                *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
+        }
       }
+    }
     }
     __syncthreads();  // the tile buffer is read out before the next tile's loads refill the stages
   }
@@ -656,12 +776,12 @@ int regime_block_rows(int regime) { return regime >= 1 ? 256 : 128; }
 
 // Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take up
 // to the CU's 160 KB), persistent over the tile list.
-template <bool kGated, int BM, int BN, int WM, int WN>
+template <int kMode, int BM, int BN, int WM, int WN>
 static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, hipStream_t s) {
-  const int64_t cols = kGated ? BN / 2 : BN;
+  const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
   const int64_t nb = (ncols + cols - 1) / cols;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, device_cu_count())));
-  hipLaunchKernelGGL((gemm_dl_kernel<kGated, BM, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
+  hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -671,7 +791,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
                       const SharedExperts& sh, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f,
              T * k, sh.w1, sh.w3, sh.n > 0 ? sh.E_routed : INT32_MAX};
-  if (dtype == 1 && regime >= 1) return launch_big<true, 256, 256, 2, 4>(a, max_mb, f, s);
+  if (dtype == 1 && regime >= 1) return launch_big<kModeFc1, 256, 256, 2, 4>(a, max_mb, f, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -697,14 +817,46 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
       const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
       narrow = t192 < t256;
     }
-    return narrow ? launch_big<false, 256, 192, 4, 2>(a, max_mb, d, s)
-                  : launch_big<false, 256, 256, 2, 4>(a, max_mb, d, s);
+    return narrow ? launch_big<kModeFc2, 256, 192, 4, 2>(a, max_mb, d, s)
+                  : launch_big<kModeFc2, 256, 256, 2, 4>(a, max_mb, d, s);
   }
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((grouped_gemm_kernel<0, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------- backward GEMMs (bf16, 256 x 256 tiles) ----------------
+
+hipError_t launch_fc1_gu(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
+                         void* gu, const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d,
+                         int64_t f, hipStream_t s) {
+  GemmArgs a{x, perm, k, T, w1, w3, gu, mblocks, n_mblocks, d, f, T * k, nullptr, nullptr, INT32_MAX};
+  return launch_big<kModeFc1GU, 256, 256, 2, 4>(a, max_mb, f, s);
+}
+
+hipError_t launch_bwd_q(const void* dout, const int32_t* perm, int k, int64_t T, const void* w2t, float* q,
+                        const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
+                        hipStream_t s) {
+  GemmArgs a{dout, perm, k, T, w2t, nullptr, q, mblocks, n_mblocks, d, f, T * k, nullptr, nullptr, INT32_MAX};
+  return launch_big<kModeBwdQ, 256, 256, 2, 4>(a, max_mb, f, s);
+}
+
+hipError_t launch_bwd_dx(const void* dgu, const void* w13t, float* dxs, const int4* mblocks,
+                         const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
+  GemmArgs a{dgu, nullptr, 1, 0, w13t, nullptr, dxs, mblocks, n_mblocks, 2 * f, d, 0, nullptr, nullptr, INT32_MAX};
+  return launch_big<kModeBwdDx, 256, 256, 2, 4>(a, max_mb, d, s);
+}
+
+hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, const int32_t* kofs, int64_t pitch,
+                        int E, int64_t M, int64_t N, int64_t split, hipStream_t s) {
+  GemmArgs a{at, nullptr, 1, 0, bt, nullptr, c, nullptr, nullptr, 0, N, 0, nullptr, nullptr, INT32_MAX,
+             c2, kofs, pitch, M, split, E};
+  const int64_t tiles = static_cast<int64_t>(E) * (M / 256) * (N / 256);
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(tiles, device_cu_count())));
+  hipLaunchKernelGGL((gemm_dl_kernel<kModeWgrad, 256, 256, 2, 4>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "moe.h"
@@ -144,6 +145,51 @@ size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out, int n_shared = 0) 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Backward scratch. P = T*k sorted rows; pp = padded columns of the transposed
+// activations (every expert's rows rounded up to a multiple of 64).
+struct BwdWs {
+  int4* mblocks; int32_t* n_mblocks; int64_t max_mb;
+  void* w2t; void* w13t;         // [E][f][d], [E][d][2f] bf16
+  void* gu; void* dgu;           // [P][2f] bf16
+  float* q;                      // [P][f]
+  float* dxs;                    // [P][d]
+  float* dwp; float* dl;         // [P]
+  int32_t* kofs; int32_t* colmap; int64_t pp;
+  void* xgt; void* dyt;          // x and dout rows by token, transposed: [d][pp] bf16
+  void* ht;                      // w * h, transposed: [f][pp] bf16
+  void* dgut;                    // [2f][pp] bf16
+  float* gpart; float* bpart;    // gate-gradient partials [parts][E][d], [parts][E]
+};
+size_t bwd_ws(const moe_dims_t* dm, void* ws, BwdWs* out) {
+  Carver c(ws);
+  BwdWs r{};
+  const int64_t P = dm->T * dm->k, d = dm->d, f = dm->f, E = dm->E;
+  r.max_mb = max_mblocks(P, dm->E);
+  r.pp = (P + 63) / 64 * 64 + 64 * E;
+  r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
+  r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
+  r.w2t = c.take<char>(size_t(2) * E * f * d);
+  r.w13t = c.take<char>(size_t(2) * E * d * 2 * f);
+  r.gu = c.take<char>(size_t(2) * P * 2 * f);
+  r.dgu = c.take<char>(size_t(2) * P * 2 * f);
+  r.q = c.take<float>(sizeof(float) * P * f);
+  r.dxs = c.take<float>(sizeof(float) * P * d);
+  r.dwp = c.take<float>(sizeof(float) * P);
+  r.dl = c.take<float>(sizeof(float) * P);
+  r.kofs = c.take<int32_t>(sizeof(int32_t) * (E + 1));
+  r.colmap = c.take<int32_t>(sizeof(int32_t) * r.pp);
+  r.xgt = c.take<char>(size_t(2) * d * r.pp);
+  r.dyt = c.take<char>(size_t(2) * d * r.pp);
+  r.ht = c.take<char>(size_t(2) * f * r.pp);
+  r.dgut = c.take<char>(size_t(2) * 2 * f * r.pp);
+  r.gpart = c.take<float>(sizeof(float) * gate_parts() * E * d);
+  r.bpart = c.take<float>(sizeof(float) * gate_parts() * E);
+  if (out) *out = r;
+  return c.off;
+}
+
+
+
 // ---------------- launch sequences (arguments already validated) ----------------
 int do_route(const moe_dims_t* dm, const void* x, const void* wg, const float* bias, float* logits,
              int32_t* idx, float* w, hipStream_t s) {
@@ -226,6 +272,20 @@ int ffn_shape_ok(const moe_dims_t* dm, int n_shared = 0) {
   const int64_t lim = int64_t(1) << 32, eb = elt_bytes(dm);
   if ((dm->T + 1) * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || ffn_rows(dm, n_shared) * dm->f * eb >= lim ||
       257 * dm->f * eb >= lim)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int bwd_shape_ok(const moe_dims_t* dm) {
+  if (dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (dm->d % 256 != 0 || dm->f % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (int st = ffn_shape_ok(dm)) return st;
+  // 32-bit byte offsets: one transposed-weight matrix per expert, the gathered
+  // operands (x and dout rows, g|u and dg|du rows of a block), and the
+  // transposed activations [2f][pp]
+  const int64_t lim = int64_t(1) << 32, P = dm->T * dm->k, pp = (P + 63) / 64 * 64 + 64 * int64_t(dm->E);
+  if (2 * dm->f * dm->d * 2 >= lim || 257 * 2 * dm->f * 2 >= lim || 2 * dm->f * pp * 2 >= lim ||
+      dm->d * pp * 2 >= lim)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -395,6 +455,104 @@ int moe_layer_forward_shared(const moe_dims_t* dm, int n_shared, const void* x, 
   sh.E_routed = dm->E;
   return run_layer(dm, sh, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets, perm,
                    inv_perm, ws, ws_bytes, stream);
+}
+
+size_t moe_backward_workspace_bytes(const moe_dims_t* dm) {
+  if (check_dims(dm) != MOE_OK) return 0;
+  return bwd_ws(dm, nullptr, nullptr);
+}
+
+int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
+                       const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
+                       void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits,
+                       float* dtopk_w, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (!ok16(wg) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(dwg) || !ok4(dbias) || !ok16(dw1) || !ok16(dw3) ||
+      !ok16(dw2) || !ok4(counts) || !ok4(offsets) || !ok4_or_null(dlogits) || !ok4_or_null(dtopk_w))
+    return MOE_ERR_INVALID;
+  if (dm->T > 0 && (!ok16(x) || !ok4(topk_idx) || !ok4(topk_w) || !ok4(perm) || !ok4(inv_perm) || !ok16(dout) ||
+                    !ok16(dx)))
+    return MOE_ERR_INVALID;
+  if (int st = bwd_shape_ok(dm)) return st;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < bwd_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  BwdWs b{};
+  bwd_ws(dm, ws, &b);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = dm->T, d = dm->d, f = dm->f, P = T * dm->k;
+  const int E = dm->E, k = dm->k;
+  if (T == 0) {
+    // no rows: every weight gradient is zero
+    for (auto pr : {std::make_pair(dw1, E * f * d), std::make_pair(dw3, E * f * d), std::make_pair(dw2, E * d * f),
+                    std::make_pair(dwg, E * d), std::make_pair(dbias, int64_t(E))})
+      if (int st = hip_status(launch_fill_zero(pr.first, pr.second, s))) return st;
+    return MOE_OK;
+  }
+  {
+    StageScope sc(MOE_STAGE_PLAN, s);
+    if (int st = hip_status(launch_plan(counts, offsets, E, P, b.max_mb, 256, b.mblocks, b.n_mblocks, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_WT, s);
+    // W2 [E][d][f] -> [E][f][d]; W1, W3 [E][f][d] -> the two column halves of [E][d][2f]
+    if (int st = hip_status(launch_transpose(w2, b.w2t, d, f, E, d * f, f * d, d, 0, s))) return st;
+    if (int st = hip_status(launch_transpose(w1, b.w13t, f, d, E, f * d, d * 2 * f, 2 * f, 0, s))) return st;
+    if (int st = hip_status(launch_transpose(w3, b.w13t, f, d, E, f * d, d * 2 * f, 2 * f, f, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_FC1, s);
+    if (int st = hip_status(launch_fc1_gu(x, perm, k, T, w1, w3, b.gu, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_DH, s);
+    if (int st = hip_status(launch_bwd_q(dout, perm, k, T, b.w2t, b.q, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_SWIGLU, s);
+    if (int st = hip_status(launch_swiglu_bwd(b.q, b.gu, perm, topk_w, P, f, b.dgu, b.dwp, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_ROUTE, s);
+    if (int st = hip_status(launch_route_bwd(topk_idx, topk_w, inv_perm, b.dwp, T, k, E, b.dl, dtopk_w, dlogits, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_DX, s);
+    if (int st = hip_status(launch_bwd_dx(b.dgu, b.w13t, b.dxs, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_DXSUM, s);
+    if (int st = hip_status(launch_dx_combine(b.dxs, inv_perm, topk_idx, b.dl, wg, T, k, E, d, dx, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_ACT_T, s);
+    if (int st = hip_status(launch_colmap(counts, offsets, E, P, b.pp, b.kofs, b.colmap, s))) return st;
+    if (int st = hip_status(launch_gather_transpose(0, x, b.colmap, perm, topk_w, k, P, d, d, b.xgt, b.pp, s)))
+      return st;
+    if (int st = hip_status(launch_gather_transpose(0, dout, b.colmap, perm, topk_w, k, P, d, d, b.dyt, b.pp, s)))
+      return st;
+    if (int st = hip_status(launch_gather_transpose(2, b.gu, b.colmap, perm, topk_w, k, P, f, 2 * f, b.ht, b.pp, s)))
+      return st;
+    if (int st = hip_status(
+            launch_gather_transpose(3, b.dgu, b.colmap, perm, topk_w, k, P, 2 * f, 2 * f, b.dgut, b.pp, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_WG2, s);
+    // dW2_e [d][f] = dout^T (w h) over expert e's rows
+    if (int st = hip_status(launch_wgrad(b.dyt, b.ht, dw2, nullptr, b.kofs, b.pp, E, d, f, d, s))) return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_BWD_WG13, s);
+    // [dW1_e ; dW3_e] [2f][d] = [dg | du]^T x over expert e's rows
+    if (int st = hip_status(launch_wgrad(b.dgut, b.xgt, dw1, dw3, b.kofs, b.pp, E, 2 * f, d, f, s))) return st;
+  }
+  StageScope sc(MOE_STAGE_BWD_GATE, s);
+  return hip_status(launch_gate_grad(x, perm, offsets, b.dl, T, k, d, E, b.gpart, b.bpart, dwg, dbias, s));
 }
 
 int moe_timing_enable(int capacity, unsigned stage_mask) {

@@ -17,8 +17,8 @@ Recipe (one generator per tensor, in a fixed order, so every tensor is
 reproducible on its own):
 
 * ``torch.Generator(device)`` seeded with ``seed * 1000 + tensor_id``;
-  tensor ids: x=1, wg=2, w1=3, w3=4, w2=5, and for shared experts sw1=6,
-  sw3=7, sw2=8.
+  tensor ids: x=1, wg=2, w1=3, w3=4, w2=5, for shared experts sw1=6,
+  sw3=7, sw2=8, and the backward's output gradient dout=9 (N(0, 1), [T][d]).
 * expert weight tensors are drawn one expert at a time, expert 0 first;
 * each draw is fp32 ``torch.randn``, multiplied by fp32 ``1/sqrt(fan_in)``,
   then converted to the activation dtype (bf16 conversion rounds to nearest
@@ -46,9 +46,9 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["LayerConfig", "CONFIGS", "TENSOR_IDS", "make_layer_inputs", "gate_bias", "config"]
+__all__ = ["LayerConfig", "CONFIGS", "TENSOR_IDS", "make_layer_inputs", "gate_bias", "config", "output_grad"]
 
-TENSOR_IDS = {"x": 1, "wg": 2, "w1": 3, "w3": 4, "w2": 5, "sw1": 6, "sw3": 7, "sw2": 8}
+TENSOR_IDS = {"x": 1, "wg": 2, "w1": 3, "w3": 4, "w2": 5, "sw1": 6, "sw3": 7, "sw2": 8, "dout": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -150,6 +150,15 @@ def make_layer_inputs(cfg: LayerConfig, seed: int = 0, device="cpu",
         out["sw3"] = _expert_tensor(S, cfg.f, cfg.d, 1.0 / math.sqrt(cfg.d), seed, TENSOR_IDS["sw3"], dev, dt)
         out["sw2"] = _expert_tensor(S, cfg.d, cfg.f, 1.0 / math.sqrt(cfg.f), seed, TENSOR_IDS["sw2"], dev, dt)
     return out
+
+
+def output_grad(T: int, d: int, dtype: str = "bf16", seed: int = 0, device="cpu") -> torch.Tensor:
+    """The backward's seeded output gradient dout [T][d], N(0, 1) in the activation dtype."""
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 1000 + TENSOR_IDS["dout"])
+    return _draw((T, d), 1.0, gen, dev, dt)
 
 
 def random_inputs(T: int, d: int, f: int, E: int, k: int, dtype: str = "bf16", bias_scale: float = 0.0,

@@ -8,4 +8,5 @@ nothing from the product path.
 from .moe_oracle import *  # noqa: F401,F403
 from .moe_oracle import __all__  # noqa: F401
 from . import moe_backward  # noqa: F401
-from .moe_backward import layer_backward, routing_backward, expert_backward_sorted, dsilu  # noqa: F401
+from .moe_backward import (layer_backward, routing_backward, expert_backward_sorted, dsilu,  # noqa: F401
+                           token_backward, expert_grad_slices)

@@ -50,7 +50,8 @@ import numpy as np
 
 from .moe_oracle import decode, route, dispatch
 
-__all__ = ["layer_backward", "routing_backward", "expert_backward_sorted", "dsilu"]
+__all__ = ["layer_backward", "routing_backward", "expert_backward_sorted", "dsilu", "token_backward",
+           "expert_grad_slices"]
 
 
 def _sigmoid(z: np.ndarray) -> np.ndarray:
@@ -149,3 +150,62 @@ def layer_backward(x, wg, bias, w1, w3, w2, k: int, dtype: str, dout, routing: d
     return {"dx": ex["dx_ffn"] + rt["dx_gate"], "dwg": rt["dwg"], "dbias": rt["dbias"],
             "dw1": ex["dw1"], "dw3": ex["dw3"], "dw2": ex["dw2"], "dlogits": rt["dlogits"],
             "dtopk_w": ex["dw"], "topk_idx": idx, "topk_w": w}
+
+
+def token_backward(x_rows, idx_rows, w_rows, w1, w3, w2, wg, dout_rows, dtype: str) -> dict:
+    """dx, dtopk_w and dlogits of a few tokens, straight from the definition
+    (sampled checks at sizes where the full backward is too slow).
+
+    x_rows [n, d], idx_rows / w_rows [n, k], dout_rows [n, d] belong to the
+    sampled tokens; w1, w3, w2 index by expert (whole tensors or lazy per-expert
+    lookups) and wg is [E, d]. Returns fp64 dx [n, d], dtopk_w [n, k], dl [n, k]."""
+    xf = decode(x_rows, dtype).astype(np.float64)
+    df = np.asarray(dout_rows, np.float64) if dout_rows.dtype != np.uint16 else decode(dout_rows, dtype).astype(np.float64)
+    wgf = decode(wg, dtype).astype(np.float64)
+    n, k = idx_rows.shape
+    wf = np.asarray(w_rows, np.float64)
+    dx = np.zeros_like(xf)
+    dw = np.zeros((n, k))
+    for r in range(n):
+        for j in range(k):
+            e = int(idx_rows[r, j])
+            W1 = decode(w1[e], dtype).astype(np.float64)
+            W3 = decode(w3[e], dtype).astype(np.float64)
+            W2 = decode(w2[e], dtype).astype(np.float64)
+            g = W1 @ xf[r]
+            u = W3 @ xf[r]
+            s = _sigmoid(g)
+            h = g * s * u
+            dw[r, j] = df[r] @ (W2 @ h)
+            dh = W2.T @ (wf[r, j] * df[r])
+            dx[r] += W1.T @ (dh * u * dsilu(g)) + W3.T @ (dh * g * s)
+    dl = wf * (dw - np.sum(wf * dw, axis=1, keepdims=True))
+    for r in range(n):
+        for j in range(k):
+            dx[r] += dl[r, j] * wgf[int(idx_rows[r, j])]
+    return {"dx": dx, "dtopk_w": dw, "dl": dl}
+
+
+def expert_grad_slices(x, dout, w, perm, offsets, w1e, w3e, w2e, k: int, e: int, cols, dtype: str) -> dict:
+    """Slices of expert e's weight gradients along FFN columns `cols` (sampled
+    checks): dW1_e[cols, :], dW3_e[cols, :] (rows of [f, d]) and dW2_e[:, cols]
+    (columns of [d, f]); each needs only the FFN columns `cols` of every row of
+    expert e. w1e, w3e [f, d] and w2e [d, f] are expert e's matrices. fp64."""
+    xf = decode(x, dtype).astype(np.float64)
+    df = np.asarray(dout, np.float64) if dout.dtype != np.uint16 else decode(dout, dtype).astype(np.float64)
+    cols = np.asarray(cols, np.int64)
+    p0, p1 = int(offsets[e]), int(offsets[e + 1])
+    a = np.asarray(perm, np.int64)[p0:p1]
+    X = xf[a // k]
+    D = np.asarray(w, np.float64).reshape(-1)[a][:, None] * df[a // k]
+    W1c = decode(w1e[cols], dtype).astype(np.float64)            # [c, d]
+    W3c = decode(w3e[cols], dtype).astype(np.float64)
+    W2c = decode(w2e[:, cols], dtype).astype(np.float64)         # [d, c]
+    G = X @ W1c.T
+    U = X @ W3c.T
+    S = _sigmoid(G)
+    H = G * S * U
+    dH = D @ W2c
+    dG = dH * U * dsilu(G)
+    dU = dH * G * S
+    return {"dw1": dG.T @ X, "dw3": dU.T @ X, "dw2": D.T @ H}

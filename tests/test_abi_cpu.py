@@ -142,3 +142,24 @@ def test_layer_shared_validation():
         ctypes.byref(_dims()), 1)
     assert lib.moe_workspace_bytes_shared(ctypes.byref(_dims()), 0) == 0
     assert base > 0
+
+
+def test_layer_backward_validation():
+    """moe_layer_backward rejects fp32 data, shapes off the 256 grid, null gradient
+    outputs and a short workspace before anything is launched."""
+    lib = moe.load_library()
+    good = dict(d=256, f=512)
+
+    def call(dims=None, dw1=A, ws_bytes=1 << 40, dlogits=None):
+        dm = _dims(**{**good, **(dims or {})})
+        return lib.moe_layer_backward(ctypes.byref(dm), A, A, A, A, A, A, A, A, A, A, A, A, A, A, A, dw1, A, A,
+                                      dlogits, None, A, ws_bytes, None)
+    assert call(dims=dict(dtype=0)) == 2             # fp32: the backward runs on bf16 only
+    assert call(dims=dict(d=192)) == 2               # d % 256 != 0
+    assert call(dims=dict(f=320)) == 2               # f % 256 != 0
+    assert call(dw1=None) == 1
+    assert call(dlogits=A + 2) == 1                  # misaligned optional output
+    assert call(ws_bytes=16) == 3
+    need = lib.moe_backward_workspace_bytes(ctypes.byref(_dims(**good)))
+    assert need > lib.moe_backward_workspace_bytes(ctypes.byref(_dims(**{**good, "T": 1})))
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(_dims(k=0))) == 0

@@ -171,3 +171,26 @@ def test_bf16_inputs_decode_like_forward():
     ref = _autograd(dec, k, dout, g["topk_idx"])
     for name in ("dx", "dw1", "dw3", "dw2"):
         assert _rel(g[name], ref[name]) < 1e-6, name
+
+
+def test_sampled_helpers_agree_with_full_backward():
+    """The sampled forms used at full size give the same numbers as the full backward."""
+    T, d, f, E, k = 9, 16, 24, 4, 2
+    inp = _inputs(T, d, f, E, k, dtype="bf16", s=0.7)
+    dout = _dout(T, d)
+    g = oracle.layer_backward(inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], k, "bf16", dout)
+    toks = np.array([0, 4, 8])
+    tb = oracle.token_backward(inp["x"][toks], g["topk_idx"][toks], g["topk_w"][toks], inp["w1"], inp["w3"],
+                               inp["w2"], inp["wg"], dout[toks], "bf16")
+    assert _rel(tb["dx"], g["dx"][toks]) < 1e-12
+    assert _rel(tb["dtopk_w"], g["dtopk_w"][toks]) < 1e-12
+    rows = np.repeat(np.arange(toks.size), k)
+    assert _rel(tb["dl"].reshape(-1), g["dlogits"][toks[rows], g["topk_idx"][toks].reshape(-1)]) < 1e-12
+    _, offsets, perm, _ = oracle.dispatch(g["topk_idx"], E)
+    cols = np.array([1, 7, 23])
+    for e in range(E):
+        sl = oracle.expert_grad_slices(inp["x"], dout, g["topk_w"], perm, offsets, inp["w1"][e], inp["w3"][e],
+                                       inp["w2"][e], k, e, cols, "bf16")
+        np.testing.assert_allclose(sl["dw1"], g["dw1"][e][cols], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sl["dw3"], g["dw3"][e][cols], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sl["dw2"], g["dw2"][e][:, cols], rtol=1e-12, atol=1e-14)
