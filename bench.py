@@ -5,6 +5,7 @@ grouped FC1 + SiLU*mul, grouped FC2, combine) on one batch of synthetic
 inputs already resident in HBM. Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceilings]
+  python bench.py --backward [--workload NAME] ...   (the layer's backward instead)
 
 The default workload is the Mixtral-8x22B-shaped decode layer (T=256, d=6144,
 f=16384, E=8, top-2, bf16, balanced routing). The roofline object covers the
@@ -42,6 +43,8 @@ def parse():
                    help="instead of the layer: time one expert's FC1 + FC2 against rows per expert")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured HBM-read and MFMA ceilings (diagnostic, about a second)")
+    p.add_argument("--backward", action="store_true",
+                   help="time the layer's backward (moe_layer_backward) instead of the forward")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run 5 device copies of 1 GiB (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -237,7 +240,131 @@ def main():
         return
     seeds = [int(v) for v in args.seeds.split(",") if v] or [args.seed]
     for seed in seeds:
-        print(json.dumps(run_one(args, seed)), flush=True)
+        print(json.dumps(run_backward(args, seed) if args.backward else run_one(args, seed)), flush=True)
+
+
+def cpu_baseline_backward(cfg, inp, dout, ntok: int, seed: int = 0):
+    """Time the CPU backward oracle (as it stands) on the first ntok tokens."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    cores = len(os.sched_getaffinity(0))
+    h = {n: host(v) for n, v in inp.items()}
+    t0 = time.perf_counter()
+    oracle.layer_backward(h["x"][:ntok], h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], cfg.k, cfg.dtype,
+                          host(dout[:ntok]))
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle layer backward (numpy, fp64, routing recomputed) on the first {ntok} of {cfg.T} "
+                      f"tokens of workload {cfg.name}, seed {seed} inputs; {dt:.1f} s"}
+
+
+def run_backward(args, seed: int) -> dict:
+    """One measurement of moe_layer_backward on the workload's inputs for `seed`:
+    the forward runs once for the routing, then every step computes all
+    gradients (dx, dwg, dbias, dw1, dw3, dw2, dlogits, dtopk_w) from dout."""
+    import torch
+    import moe_inputs
+    import mixture_experts_layer_gate_amd as moe
+    from mixture_experts_layer_gate_amd import roofline as rf
+
+    cfg = moe_inputs.config(args.workload)
+    if cfg.n_shared or cfg.dtype != "bf16":
+        raise SystemExit(f"the backward runs on bf16 layers without shared experts; {cfg.name} is not one")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = moe_inputs.make_layer_inputs(cfg, seed, dev)
+    dout = moe_inputs.output_grad(cfg.T, cfg.d, cfg.dtype, seed, dev)
+    dims = moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype)
+    stream = torch.cuda.current_stream()
+    _, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                             return_routing=True)
+    counts = r["counts"].cpu().tolist()
+    ws = torch.empty(moe.backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    grads = moe.layer_backward(dims, inp["x"], inp["wg"], inp["w1"], inp["w3"], inp["w2"], r, dout, ws=ws,
+                               want_dlogits=True, want_dtopk_w=True)
+
+    def step():
+        moe.layer_backward(dims, inp["x"], inp["wg"], inp["w1"], inp["w3"], inp["w2"], r, dout, ws=ws,
+                           stream=stream, want_dlogits=True, want_dtopk_w=True, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    bwd = [s_ for s_ in moe.STAGES if s_.startswith("bwd_")] + ["plan"]
+    # untimed pass with every stage recorded: per-stage times, and the dominant GEMM
+    nbreak = min(args.steps, 5)
+    moe.timing_enable(nbreak, stages=bwd)
+    for _ in range(nbreak):
+        step()
+    torch.cuda.synchronize()
+    moe.timing_disable()
+    stages = {s_: moe.timing_read(s_) for s_ in bwd}
+    stage_ms = {s_: v[0] / max(v[1], 1) for s_, v in stages.items() if v[1] > 0}
+    dom = max(rf.BACKWARD_GEMM_FLOPS_PER_ROW, key=lambda s_: stage_ms.get(s_, 0.0))
+    # timed region: events only around the dominant GEMM, on its launch stream
+    moe.timing_enable(args.steps, stages=[dom])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    moe.timing_disable()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    rec = moe.timing_read(dom)
+    dom_ms = rec[0] / max(rec[1], 1)
+    P = cfg.T * cfg.k
+    dom_flops = rf.BACKWARD_GEMM_FLOPS_PER_ROW[dom] * cfg.d * cfg.f * P
+    roof = {"bound": "mfma", "achieved": round(dom_flops / (dom_ms * 1e-3) / 1e12, 1), "peak": 2500.0,
+            "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = {"bwd_fc1": "gemm_dl_kernel<FC1 recompute g|u, 256x256>",
+                      "bwd_dh": "gemm_dl_kernel<dout W2, 256x256>",
+                      "bwd_dx": "gemm_dl_kernel<[dg|du] [W1;W3], 256x256>",
+                      "bwd_wg2": "gemm_dl_kernel<weight gradient dW2, 256x256>",
+                      "bwd_wg13": "gemm_dl_kernel<weight gradients dW1|dW3, 256x256>"}[dom]
+    roof["kernel_ms"] = round(dom_ms, 4)
+    gemm_rates = {s_: round(rf.BACKWARD_GEMM_FLOPS_PER_ROW[s_] * cfg.d * cfg.f * P / (stage_ms[s_] * 1e-3) / 1e12, 1)
+                  for s_ in rf.BACKWARD_GEMM_FLOPS_PER_ROW if s_ in stage_ms}
+    flops = rf.backward_flops(P, cfg.d, cfg.f, cfg.T, cfg.k)
+    res = {
+        "metric": "MoE layer backward tokens/s at 1 GPU; % bf16 MFMA peak of the dominant GEMM (roofline)",
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "pass": "backward", "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+                   "k": cfg.k, "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 1),
+                  "recompute_tflop": round(rf.fc1_flops(P, cfg.d, cfg.f) / 1e12, 3),
+                  "kappa": round(rf.kappa(counts), 3), "active_experts": rf.active_experts(counts)},
+        "gemm_tflops": gemm_rates,
+        "stages_ms": {s_: round(v, 4) for s_, v in stage_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        ntok = min(cfg.T, args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else 32)
+        res["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dout, ntok, seed)
+    else:
+        res["cpu_baseline"] = None
+    del inp, ws, grads
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_one(args, seed: int) -> dict:

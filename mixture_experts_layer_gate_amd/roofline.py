@@ -53,6 +53,18 @@ def fc2_flops(rows: int, d: int, f: int) -> int:
     return 2 * d * f * rows
 
 
+def backward_flops(rows: int, d: int, f: int, T: int = 0, k: int = 0) -> int:
+    """Algorithmic FLOP of the layer's backward: DGrad (W2^T dout 2*d*f and
+    [W1;W3]^T [dg;du] 4*d*f per row), WGrad (dW2 2*d*f, dW1 and dW3 4*d*f per
+    row) and the gate part (dWg and the gate's dx, 2*d each per selected logit).
+    The FC1 recompute is implementation work, not counted."""
+    return 12 * d * f * rows + 4 * d * T * k
+
+
+# FLOP of each matrix-product stage of the backward, per sorted row
+BACKWARD_GEMM_FLOPS_PER_ROW = {"bwd_fc1": 4, "bwd_dh": 2, "bwd_dx": 4, "bwd_wg2": 2, "bwd_wg13": 4}
+
+
 def active_experts(counts: Iterable[int]) -> int:
     return sum(1 for c in counts if int(c) > 0)
 
