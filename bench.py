@@ -43,6 +43,8 @@ def parse():
                    help="instead of the layer: time one expert's FC1 + FC2 against rows per expert")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured HBM-read and MFMA ceilings (diagnostic, about a second)")
+    p.add_argument("--fused", action="store_true",
+                   help="time moe_layer_forward_fused (FC1, FC2 and combine in one persistent launch)")
     p.add_argument("--backward", action="store_true",
                    help="time the layer's backward (moe_layer_backward) instead of the forward")
     p.add_argument("--copy-probe", action="store_true",
@@ -386,6 +388,8 @@ def run_one(args, seed: int) -> dict:
 
     S = cfg.n_shared
     if S:
+        if args.fused:
+            raise SystemExit("the fused FFN launch covers layers without shared experts")
         ws = torch.empty(moe.workspace_bytes_shared(dims, S), dtype=torch.uint8, device=dev)
 
     def step():
@@ -394,7 +398,7 @@ def run_one(args, seed: int) -> dict:
                                      inp["sw1"], inp["sw3"], inp["sw2"], out=out, ws=ws, stream=stream)
         else:
             moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], out=out,
-                              ws=ws, stream=stream)
+                              ws=ws, stream=stream, fused=args.fused)
 
     for _ in range(args.warmup):
         step()
@@ -411,9 +415,10 @@ def run_one(args, seed: int) -> dict:
     kk = cfg.k + S
     torch.cuda.synchronize()
 
-    # Timed region: events only around the dominant kernel (FC1), on the
-    # stream it is launched on.
-    moe.timing_enable(args.steps, stages=["fc1"])
+    # Timed region: events only around the dominant kernel (FC1, or the fused
+    # FC1 + FC2 + combine launch), on the stream it is launched on.
+    dom = "ffn_fused" if args.fused else "fc1"
+    moe.timing_enable(args.steps, stages=[dom])
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -424,7 +429,7 @@ def run_one(args, seed: int) -> dict:
     moe.timing_disable()
     total_ms = ev0.elapsed_time(ev1)
     ms = total_ms / args.steps
-    fc1_rec = moe.timing_read("fc1")
+    fc1_rec = moe.timing_read(dom)
     # Per-stage breakdown from a separate, untimed pass with every stage recorded.
     nbreak = min(args.steps, 5)
     moe.timing_enable(nbreak)
@@ -433,13 +438,19 @@ def run_one(args, seed: int) -> dict:
     torch.cuda.synchronize()
     moe.timing_disable()
     stages = {s: moe.timing_read(s) for s in moe.STAGES}
-    stages["fc1"] = fc1_rec
+    stages[dom] = fc1_rec
 
     elt = 2 if cfg.dtype == "bf16" else 4
     n = cfg.T * kk
-    fc1_ms = stages["fc1"][0] / max(stages["fc1"][1], 1)
-    fc1_flops = rf.fc1_flops(n, cfg.d, cfg.f)
-    fc1_bytes = rf.fc1_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt)
+    fc1_ms = stages[dom][0] / max(stages[dom][1], 1)
+    if args.fused:
+        # one launch does FC1, FC2 and the combine: FFN FLOP, and all expert weights + x + h + y + out bytes
+        fc1_flops = rf.ffn_flops(n, cfg.d, cfg.f)
+        fc1_bytes = (rf.fc1_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt) +
+                     rf.fc2_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt) + cfg.T * cfg.d * elt)
+    else:
+        fc1_flops = rf.fc1_flops(n, cfg.d, cfg.f)
+        fc1_bytes = rf.fc1_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt)
     cls = rf.classify(fc1_flops, fc1_bytes)
     if cls.bound == "hbm":
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
@@ -449,10 +460,13 @@ def run_one(args, seed: int) -> dict:
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(cfg.name, "fc1")
+    roof["traffic"] = None if args.fused else measured_traffic(cfg.name, "fc1")
     big_tile = cfg.dtype == "bf16" and os.environ.get("MOE_GEMM_REGIME", "1") != "0"
-    roof["kernel"] = ("gemm_dl_kernel<gated, 256x256> (FC1 + SiLU*mul)" if big_tile
-                      else "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)")
+    if args.fused:
+        roof["kernel"] = "ffn_fused_kernel (FC1 + SiLU*mul, FC2, combine; one launch)"
+    else:
+        roof["kernel"] = ("gemm_dl_kernel<gated, 256x256> (FC1 + SiLU*mul)" if big_tile
+                          else "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)")
     roof["kernel_ms"] = round(fc1_ms, 4)
 
     ceilings = None
@@ -482,7 +496,7 @@ def run_one(args, seed: int) -> dict:
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
-                   "n_shared": S, "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
+                   "n_shared": S, "ffn": "fused" if args.fused else "separate launches", "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "gbps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),

@@ -159,6 +159,22 @@ int moe_layer_forward_shared(const moe_dims_t* dims, int n_shared, const void* x
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* The same layer with FC1, FC2 and the combine in one persistent launch
+ * (route and dispatch run before it as usual). Workgroups take tiles from one
+ * device-side sequence (FC1 tiles, then FC2 tiles, then blocks of 8 tokens
+ * for the combine); an FC2 tile starts once every FC1 tile of its block of
+ * rows is stored, the combine once every FC2 tile is, tracked by readiness
+ * counters in the workspace instead of kernel boundaries (the next step of
+ * the pages' megakernel design: MegaFlux, section 2.1, MegaMoE's tiled
+ * FC1/FC2). The arithmetic is that of moe_layer_forward tile for tile, so
+ * the outputs are bitwise equal. bf16 only (MOE_ERR_UNSUPPORTED otherwise);
+ * other arguments, limits and the workspace size (moe_workspace_bytes) as
+ * moe_layer_forward. */
+int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+                            const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                            int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- backward pass ----
  * Gradients of the layer for a scalar loss whose gradient with respect to
  * `out` is `dout`. The pages name the parts (MegaFlux, section 2.1: token
@@ -221,7 +237,8 @@ enum {
   MOE_STAGE_BWD_WG2 = 18,     /* backward: WGrad of W2 */
   MOE_STAGE_BWD_WG13 = 19,    /* backward: WGrad of W1 and W3 */
   MOE_STAGE_BWD_GATE = 20,    /* backward: gate weight and bias gradients */
-  MOE_NUM_STAGES = 21
+  MOE_STAGE_FFN_FUSED = 21,   /* FC1 + FC2 + combine in one launch (moe_layer_forward_fused) */
+  MOE_NUM_STAGES = 22
 };
 /* Start recording; `capacity` = launches per stage to keep (host memory only);
  * `stage_mask` = bit s set records stage s (0 = every stage). Discards

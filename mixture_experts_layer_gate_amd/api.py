@@ -19,7 +19,7 @@ _LIB_NAME = "libmoe_amd.so"
 
 STAGES = ["gate", "topk", "hist", "scan", "scatter", "plan", "fc1", "fc2", "combine", "dispatch",
           "bwd_wt", "bwd_fc1", "bwd_dh", "bwd_swiglu", "bwd_route", "bwd_dx", "bwd_dxsum", "bwd_act_t",
-          "bwd_wg2", "bwd_wg13", "bwd_gate"]
+          "bwd_wg2", "bwd_wg13", "bwd_gate", "ffn_fused"]
 MOE_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 # Every symbol include/moe.h declares.
@@ -27,7 +27,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
-           "moe_layer_backward"]
+           "moe_layer_backward", "moe_layer_forward_fused"]
 
 
 class MoeError(RuntimeError):
@@ -83,6 +83,7 @@ def load_library():
     lib.moe_grouped_ffn.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P]
     lib.moe_layer_forward.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
+    lib.moe_layer_forward_fused.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_workspace_bytes_shared.restype = _S
     lib.moe_workspace_bytes_shared.argtypes = [_DP, ctypes.c_int]
     lib.moe_layer_forward_shared.argtypes = [_DP, ctypes.c_int] + [_P] * 18 + [_S, _P]
@@ -95,7 +96,7 @@ def load_library():
     lib.moe_probe_hbm_read.argtypes = [_P, _S, _P, _P]
     lib.moe_probe_mfma.argtypes = [ctypes.c_int, _P, _P]
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-               "moe_layer_forward_shared", "moe_layer_backward",
+               "moe_layer_forward_shared", "moe_layer_backward", "moe_layer_forward_fused",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -207,8 +208,11 @@ def combine(dims: Dims, y_sorted, inv_perm, topk_w, out=None, stream=None):
     return out
 
 
-def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False):
-    """The whole layer. With return_routing, also returns the routing arrays as a dict."""
+def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False,
+                  fused=False):
+    """The whole layer. With return_routing, also returns the routing arrays as a dict.
+    fused=True runs FC1, FC2 and the combine as one persistent launch
+    (moe_layer_forward_fused; bitwise the same result)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", dims.dtype, (dims.T, dims.d))
@@ -232,7 +236,8 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
              "inv_perm": torch.empty(n, dtype=torch.int32, device=dev)}
     ws, nws = _ws(dims, ws)
     g = r.get
-    _check("moe_layer_forward", lib.moe_layer_forward(
+    fn = "moe_layer_forward_fused" if fused else "moe_layer_forward"
+    _check(fn, getattr(lib, fn)(
         ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
         _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")), _ptr(g("counts")), _ptr(g("offsets")),
         _ptr(g("perm")), _ptr(g("inv_perm")), _ptr(ws), nws, _stream(stream)))

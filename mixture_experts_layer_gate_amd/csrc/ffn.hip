@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <utility>
 
+#include "combine_vec.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -345,70 +346,75 @@ __host__ __device__ constexpr bool mode_gated(int m) { return m == kModeFc1 || m
 __host__ __device__ constexpr bool mode_gather(int m) { return m == kModeFc1 || m == kModeFc1GU || m == kModeBwdQ; }
 __host__ __device__ constexpr bool mode_f32_out(int m) { return m >= kModeBwdQ; }
 
+// One tile of a large-tile GEMM form (the kernel's loop body): tile index ->
+// (m-block, n-block), operand descriptors, the pipelined K loop and the
+// epilogue. pre(mb) runs once the tile's m-block is known and before any of
+// its loads are issued; post(mb) after its results are stored and the tile
+// buffer is free again (both no-ops for the standalone kernel).
 template <int kMode, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
-  // device-only body: the buffer-resource builtins have no host form, and the
-  // host pass only needs the kernel's launch stub
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr bool kGated = mode_gated(kMode);
-  constexpr bool kWgrad = kMode == kModeWgrad;
-  constexpr int BK = 64;                   // K per step
-  constexpr int RB = BK * 2;               // bytes per LDS row
-  constexpr int CPR = RB / 16;             // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;            // rows per load instruction
-  constexpr int R256 = 16 / CPR;           // rows per 256 bytes
-  constexpr int NW = WM * WN;              // waves per workgroup
-  constexpr int NT = 64 * NW;              // threads per workgroup
-  constexpr int AI = BM / (NW * RPI);      // A load instructions per wave per stage
-  constexpr int BI = BN / (NW * RPI);      // B load instructions per wave per stage
-  constexpr int LPS = AI + BI;             // loads per thread per stage
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MI = TM / 32;              // 32-row units of the wave's rows (padding granularity)
-  constexpr int MI16 = TM / 16, NJ16 = TN / 16;  // 16 x 16 MFMA blocks of the wave tile
-  constexpr int KS = BK / 32;              // MFMA sub-steps (K = 32) per stage
+struct DlGemm {
+  static constexpr bool kGated = mode_gated(kMode);
+  static constexpr bool kWgrad = kMode == kModeWgrad;
+  static constexpr int BK = 64;                   // K per step
+  static constexpr int RB = BK * 2;               // bytes per LDS row
+  static constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;            // rows per load instruction
+  static constexpr int R256 = 16 / CPR;           // rows per 256 bytes
+  static constexpr int NW = WM * WN;              // waves per workgroup
+  static constexpr int NT = 64 * NW;              // threads per workgroup
+  static constexpr int AI = BM / (NW * RPI);      // A load instructions per wave per stage
+  static constexpr int BI = BN / (NW * RPI);      // B load instructions per wave per stage
+  static constexpr int LPS = AI + BI;             // loads per thread per stage
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int MI = TM / 32;              // 32-row units of the wave's rows (padding granularity)
+  static constexpr int MI16 = TM / 16, NJ16 = TN / 16;  // 16 x 16 MFMA blocks of the wave tile
+  static constexpr int KS = BK / 32;              // MFMA sub-steps (K = 32) per stage
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(!kGated || (NJ16 % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(KS == 2, "two 32-wide sub-steps per 64-wide stage");
   static_assert(AI * NW * RPI == BM && BI * NW * RPI == BN, "load tiling");
   // LDS: two A buffers, then as many B buffers (up to 8) as fit in the CU's
   // 160 KB, so weight loads run NBB-1 steps ahead
-  constexpr int A_ST = BM * RB, B_ST = BN * RB;
-  constexpr int NBA = 2;
-  constexpr int NBB_FIT = (160 * 1024 - NBA * A_ST) / B_ST;
-  constexpr int NBB = NBB_FIT > 8 ? 8 : NBB_FIT;
+  static constexpr int A_ST = BM * RB, B_ST = BN * RB;
+  static constexpr int NBA = 2;
+  static constexpr int NBB_FIT = (160 * 1024 - NBA * A_ST) / B_ST;
+  static constexpr int NBB = NBB_FIT > 8 ? 8 : NBB_FIT;
   static_assert(NBB >= 2, "two A and two B buffers fit in LDS");
-  constexpr int LDS_BYTES = NBA * A_ST + NBB * B_ST;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  static constexpr int LDS_BYTES = NBA * A_ST + NBB * B_ST;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
-  const int wm = wv / WN, wn = wv % WN;
-  const int64_t K = g.K, N = g.N;
-  const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
-  // weight gradients: every expert has M / BM m-blocks of output rows
-  const int mbe = kWgrad ? static_cast<int>(g.M / BM) : 0;
-  const int nmb = kWgrad ? g.n_experts * mbe : g.n_mblocks[0];
-  const int64_t ntiles = static_cast<int64_t>(nmb) * nbc;
-  int nk = static_cast<int>(K / BK);
-  const int lrow = lane / CPR;                                          // row within a load instruction
-  // Chunk this lane fetches for a load instruction whose first row is R0.
-  // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
-  // and R0 / R256 mod CPR is 0 for 64-byte rows and 0 or 4 for 128-byte rows
-  // (alternating with the instruction index, which the code passes in).
-  auto chunk_off = [&](int r0_phase) -> uint32_t {
-    return static_cast<uint32_t>(((lane % CPR) ^ ((r0_phase + lrow / R256) % CPR)) * 16);
-  };
-  constexpr int PH = (RPI / R256) % CPR;  // phase step per load instruction (0 or 4)
-  const int fsw = ((lane & 15) / R256) % CPR;                           // read-side swizzle of row (lane & 15)
-  // x spans T*K*2 bytes (< 2^32, checked on the host)
-  const uint32_t a_bytes = mode_gather(kMode) ? static_cast<uint32_t>(g.T * K * 2) : 0u;
+  // tiles of one launch: m-blocks (or experts x output-row blocks) x column blocks
+  __device__ static int64_t tiles(const GemmArgs& g) {
+    const int64_t N = g.N;
+    const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
+    const int nmb = kWgrad ? g.n_experts * static_cast<int>(g.M / BM) : g.n_mblocks[0];
+    return static_cast<int64_t>(nmb) * nbc;
+  }
 
-  // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
-  // b % 8). Renumber so that the gridDim/8 workgroups of one XCD take
-  // consecutive tiles of each round, which share A and B blocks in that XCD's L2.
-  const int G = gridDim.x;
-  const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int64_t tile = slot; tile < ntiles; tile += G) {
+  template <class Pre, class Post>
+  __device__ static __forceinline__ void tile(const GemmArgs& g, char* lds, int64_t tile, Pre pre, Post post) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
+    const int wm = wv / WN, wn = wv % WN;
+    const int64_t K = g.K, N = g.N;
+    const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
+    // weight gradients: every expert has M / BM m-blocks of output rows
+    const int mbe = kWgrad ? static_cast<int>(g.M / BM) : 0;
+    const int nmb = kWgrad ? g.n_experts * mbe : g.n_mblocks[0];
+    int nk = static_cast<int>(K / BK);
+    const int lrow = lane / CPR;                                          // row within a load instruction
+    // Chunk this lane fetches for a load instruction whose first row is R0.
+    // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
+    // and R0 / R256 mod CPR is 0 for 64-byte rows and 0 or 4 for 128-byte rows
+    // (alternating with the instruction index, which the code passes in).
+    auto chunk_off = [&](int r0_phase) -> uint32_t {
+      return static_cast<uint32_t>(((lane % CPR) ^ ((r0_phase + lrow / R256) % CPR)) * 16);
+    };
+    constexpr int PH = (RPI / R256) % CPR;  // phase step per load instruction (0 or 4)
+    const int fsw = ((lane & 15) / R256) % CPR;                           // read-side swizzle of row (lane & 15)
+    // x spans T*K*2 bytes (< 2^32, checked on the host)
+    const uint32_t a_bytes = mode_gather(kMode) ? static_cast<uint32_t>(g.T * K * 2) : 0u;
+
     int mb, nb, e, row0, rows;
     __amdgpu_buffer_rsrc_t ars;
     uint32_t aoff[AI];
@@ -472,6 +478,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
         }
       }
     }
+    pre(mb);  // the tile's operands are ready (fused kernels wait here)
+
     // B: weight rows of expert e (gated: first half W1, second half W3, same
     // columns); weight gradients: rows of the transposed operand, K window of expert e.
     __amdgpu_buffer_rsrc_t brs0, brs1;
@@ -691,66 +699,184 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
         }
       }
     } else {
-    // Epilogue through LDS: every wave writes its fragment values (bf16) into a
-    // row-major [BM][CW] tile, then all threads store whole 16-byte row chunks.
-    // The recompute form keeps g and u apart: columns 0..BN/2-1 of the tile
-    // are g, the rest u, stored to the two halves of a [rows][2N] row.
-    constexpr int CW = (kGated && kMode != kModeFc1GU) ? BN / 2 : BN;  // output columns of the tile
-    static_assert(BM * CW * 2 <= LDS_BYTES, "epilogue tile fits in the stage buffers");
-    lds_barrier();
-    bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
+      // Epilogue through LDS: every wave writes its fragment values (bf16) into a
+      // row-major [BM][CW] tile, then all threads store whole 16-byte row chunks.
+      // The recompute form keeps g and u apart: columns 0..BN/2-1 of the tile
+      // are g, the rest u, stored to the two halves of a [rows][2N] row.
+      constexpr int CW = (kGated && kMode != kModeFc1GU) ? BN / 2 : BN;  // output columns of the tile
+      static_assert(BM * CW * 2 <= LDS_BYTES, "epilogue tile fits in the stage buffers");
+      lds_barrier();
+      bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
 #pragma unroll
-    for (int i = 0; i < MI16; ++i) {
+      for (int i = 0; i < MI16; ++i) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = wm * TM + 16 * i + 4 * (lane >> 4) + v;
-        if constexpr (kMode == kModeFc1GU) {
+        for (int v = 0; v < 4; ++v) {
+          const int r = wm * TM + 16 * i + 4 * (lane >> 4) + v;
+          if constexpr (kMode == kModeFc1GU) {
 #pragma unroll
-          for (int j = 0; j < NJ16 / 2; ++j) {
-            const int c = wn * (TN / 2) + 16 * j + (lane & 15);
-            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
-            ct[r * CW + BN / 2 + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j + NJ16 / 2][v]));
+            for (int j = 0; j < NJ16 / 2; ++j) {
+              const int c = wn * (TN / 2) + 16 * j + (lane & 15);
+              ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
+              ct[r * CW + BN / 2 + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j + NJ16 / 2][v]));
+            }
+          } else if constexpr (kGated) {
+#pragma unroll
+            for (int j = 0; j < NJ16 / 2; ++j) {
+              const int c = wn * (TN / 2) + 16 * j + (lane & 15);
+              ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + NJ16 / 2][v])));
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJ16; ++j) {
+              const int c = wn * TN + 16 * j + (lane & 15);
+              ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
+            }
           }
-        } else if constexpr (kGated) {
-#pragma unroll
-          for (int j = 0; j < NJ16 / 2; ++j) {
-            const int c = wn * (TN / 2) + 16 * j + (lane & 15);
-            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + NJ16 / 2][v])));
+        }
+      }
+      __syncthreads();
+      {
+        bf16_t* C = static_cast<bf16_t*>(g.C);
+        constexpr int VPR = CW / 8;  // 16-byte vectors per tile row
+        if constexpr (kMode == kModeFc1GU) {
+          const int64_t col0 = static_cast<int64_t>(nb) * (BN / 2);
+          for (int q = tid; q < rows * VPR; q += NT) {
+            const int r = q / VPR, c8 = (q % VPR) * 8;
+            const int cc = c8 % (BN / 2);
+            if (col0 + cc < N)
+              *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * 2 * N + (c8 >= BN / 2 ? N : 0) + col0 + cc) =
+                  *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
           }
         } else {
-#pragma unroll
-          for (int j = 0; j < NJ16; ++j) {
-            const int c = wn * TN + 16 * j + (lane & 15);
-            ct[r * CW + c] = static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
+          const int64_t col0 = static_cast<int64_t>(nb) * CW;
+          for (int q = tid; q < rows * VPR; q += NT) {
+            const int r = q / VPR, c8 = (q % VPR) * 8;
+            if (col0 + c8 < N)
+              *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
+                  *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
           }
         }
       }
     }
-    __syncthreads();
-    {
-      bf16_t* C = static_cast<bf16_t*>(g.C);
-      constexpr int VPR = CW / 8;  // 16-byte vectors per tile row
-      if constexpr (kMode == kModeFc1GU) {
-        const int64_t col0 = static_cast<int64_t>(nb) * (BN / 2);
-        for (int q = tid; q < rows * VPR; q += NT) {
-          const int r = q / VPR, c8 = (q % VPR) * 8;
-          const int cc = c8 % (BN / 2);
-          if (col0 + cc < N)
-            *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * 2 * N + (c8 >= BN / 2 ? N : 0) + col0 + cc) =
-                *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
-        }
-      } else {
-        const int64_t col0 = static_cast<int64_t>(nb) * CW;
-        for (int q = tid; q < rows * VPR; q += NT) {
-          const int r = q / VPR, c8 = (q % VPR) * 8;
-          if (col0 + c8 < N)
-            *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
-                *reinterpret_cast<const u32x4_t*>(ct + r * CW + c8);
-        }
+    __syncthreads();  // the tile buffer is read out before the next tile's loads refill the stages
+    post(mb);
+#endif
+  }
+};
+
+template <int kMode, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
+  // device-only body: the buffer-resource builtins have no host form, and the
+  // host pass only needs the kernel's launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
+  using D = DlGemm<kMode, BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) char lds[D::LDS_BYTES];
+  const int64_t ntiles = D::tiles(g);
+  // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+  // b % 8). Renumber so that the gridDim/8 workgroups of one XCD take
+  // consecutive tiles of each round, which share A and B blocks in that XCD's L2.
+  const int G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int64_t tile = slot; tile < ntiles; tile += G) D::tile(g, lds, tile, [](int) {}, [](int) {});
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Fused expert FFN: FC1 tiles, FC2 tiles and the combine in one persistent
+// launch, with device-side readiness counters in place of kernel boundaries
+// (the next step the pages' megakernel design points to: FC2 of a block of
+// rows may start as soon as that block's FC1 tiles are stored; MegaFlux,
+// section 2.1, MegaMoE's tiled FC1/FC2).
+//
+// Tiles are handed out in one increasing sequence by an atomic counter: all
+// FC1 tiles, then all FC2 tiles, then the combine's token blocks. An FC2 tile
+// waits until every FC1 tile of its m-block has been stored; a combine block
+// waits until every FC2 tile has. A tile only ever waits on tiles with lower
+// numbers, which running workgroups took earlier and finish without waiting
+// on anything later, so the launch cannot deadlock whatever the number of
+// resident workgroups. Each wait is bounded: past the limit the workgroup
+// sets an error word and goes on (the results are then wrong, never a hang).
+// Producers publish with a device-scope release (their stores reach the
+// point of coherence of every XCD's L2); consumers take a device-scope
+// acquire before reading.
+// sync words: [0] next tile, [1] FC2 tiles stored, [2] error flags,
+// [4 + mb] FC1 tiles of m-block mb stored.
+constexpr int kFusedSyncHead = 4;
+[[maybe_unused]] constexpr int kCombineTokens = 8;  // tokens per combine block
+[[maybe_unused]] constexpr int kSpinLimit = 1 << 22;  // polls of a readiness counter before giving up
+
+struct FusedFfnArgs {
+  GemmArgs fc1, fc2;
+  const int32_t* inv_perm;
+  const float* topk_w;
+  void* out;
+  int64_t T, d;
+  int k, n_shared;
+  int32_t* sync;
+};
+
+__device__ __forceinline__ void wait_count(int32_t* counter, int target, int32_t* err) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// Every wave waits until its stores are complete in its XCD's L2, then one
+// device-scope release (an L2 write-back) makes all of them visible to the
+// other XCDs before the counter moves. A write-back per wave costs about as
+// much again as the whole FC1 phase at decode sizes.
+__device__ __forceinline__ void publish(int32_t* counter) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BN2, int WM2, int WN2>
+__global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using F1 = DlGemm<kModeFc1, 256, 256, 2, 4>;
+  using F2 = DlGemm<kModeFc2, 256, BN2, WM2, WN2>;
+  static_assert(F1::NT == 512 && F2::NT == 512, "both tile forms use 8 waves");
+  constexpr int LDS = F1::LDS_BYTES > F2::LDS_BYTES ? F1::LDS_BYTES : F2::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS];
+  int64_t* s_tile = reinterpret_cast<int64_t*>(lds);  // the tile buffers are free between tiles
+  const int64_t n1 = F1::tiles(a.fc1), n2 = F2::tiles(a.fc2);
+  const int64_t nc = (a.T + kCombineTokens - 1) / kCombineTokens;
+  const int nbc1 = static_cast<int>((a.fc1.N + 127) / 128);  // FC1 tiles per m-block
+  int32_t* err = a.sync + 2;
+  int32_t* done1 = a.sync + kFusedSyncHead;
+  for (;;) {
+    __syncthreads();  // the previous tile is done with the buffers
+    if (threadIdx.x == 0)
+      *s_tile = __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t t = *s_tile;
+    __syncthreads();  // every thread has read it before the tile's loads refill the buffers
+    if (t < n1) {
+      F1::tile(a.fc1, lds, t, [](int) {}, [&](int mb) { publish(done1 + mb); });
+    } else if (t < n1 + n2) {
+      F2::tile(a.fc2, lds, t - n1, [&](int mb) { wait_count(done1 + mb, nbc1, err); },
+               [&](int) { publish(a.sync + 1); });
+    } else if (t < n1 + n2 + nc) {
+      wait_count(a.sync + 1, static_cast<int>(n2), err);
+      const int64_t t0 = (t - n1 - n2) * kCombineTokens;
+      const int64_t nt = a.T - t0 < kCombineTokens ? a.T - t0 : kCombineTokens;
+      const int64_t nvec = a.d / 8;
+      for (int64_t q = threadIdx.x; q < nt * nvec; q += 512)
+        combine_vec<1>(a.fc2.C, a.inv_perm, a.topk_w, a.out, a.d, a.k, a.T * a.k, a.n_shared, a.T, t0 + q / nvec,
+                       q % nvec);
+    } else {
+      break;
     }
-    __syncthreads();  // the tile buffer is read out before the next tile's loads refill the stages
   }
 #endif
 }
@@ -857,6 +983,42 @@ hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, con
   const int64_t tiles = static_cast<int64_t>(E) * (M / 256) * (N / 256);
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(tiles, device_cu_count())));
   hipLaunchKernelGGL((gemm_dl_kernel<kModeWgrad, 256, 256, 2, 4>), dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+size_t fused_sync_words(int64_t max_mb) { return static_cast<size_t>(kFusedSyncHead + max_mb); }
+
+// FC1, FC2 and combine in one launch (bf16). The sync words must be zero on
+// entry. FC2 tiles are 256 or, under the same rule as launch_fc2, 192 columns wide.
+hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
+                            const void* w2, void* h, void* y, const int4* mblocks, const int32_t* n_mblocks,
+                            int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
+                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, hipStream_t s) {
+  FusedFfnArgs a{};
+  a.fc1 = GemmArgs{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f, T * k, sh.w1, sh.w3,
+                   sh.n > 0 ? sh.E_routed : INT32_MAX};
+  a.fc2 = GemmArgs{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d, 0, sh.w2, nullptr,
+                   sh.n > 0 ? sh.E_routed : INT32_MAX};
+  a.inv_perm = inv_perm;
+  a.topk_w = topk_w;
+  a.out = out;
+  a.T = T;
+  a.d = d;
+  a.k = k;
+  a.n_shared = sh.n;
+  a.sync = sync;
+  const int64_t cus = device_cu_count();
+  bool narrow = false;
+  if (est_mb * ((d + 255) / 256) < 2 * cus) {
+    const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
+    const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
+    narrow = t192 < t256;
+  }
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * ((f + 127) / 128), cus)));
+  if (narrow)
+    hipLaunchKernelGGL((ffn_fused_kernel<192, 4, 2>), dim3(grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_fused_kernel<256, 2, 4>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -68,6 +68,14 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
                       const SharedExperts& sh, hipStream_t s);
 
+// FC1, FC2 and the combine in one persistent launch with device-side
+// readiness counters (bf16). sync: fused_sync_words(max_mb) int32, zero on entry.
+size_t fused_sync_words(int64_t max_mb);
+hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
+                            const void* w2, void* h, void* y, const int4* mblocks, const int32_t* n_mblocks,
+                            int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
+                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, hipStream_t s);
+
 // Weighted combine.
 // With n_shared > 0, out[t] also adds y[T*k + s*T + t] for s ascending.
 hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, const float* w,

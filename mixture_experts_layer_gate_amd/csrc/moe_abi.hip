@@ -108,7 +108,7 @@ size_t permute_ws(const moe_dims_t* dm, void* ws, PermuteWs* out) {
 // Sorted rows of the grouped FFN: T*k routed rows, then T rows per shared expert.
 int64_t ffn_rows(const moe_dims_t* dm, int n_shared) { return dm->T * dm->k + static_cast<int64_t>(n_shared) * dm->T; }
 
-struct FfnWs { int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; };
+struct FfnWs { int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; int32_t* sync; };
 size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   Carver c(ws);
   FfnWs r{};
@@ -116,6 +116,7 @@ size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
   r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
   r.h = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->f);
+  r.sync = c.take<int32_t>(sizeof(int32_t) * fused_sync_words(r.max_mb));  // fused FFN's readiness counters
   if (out) *out = r;
   return c.off;
 }
@@ -235,6 +236,15 @@ int gemm_regime(const moe_dims_t* dm) {
   return dm->dtype == MOE_DTYPE_BF16 ? choose_gemm_regime(dm->T, dm->k, dm->E) : 0;
 }
 
+// m-blocks expected under even routing (the list holds at most max_mb): picks
+// the FC2 tile width before the counts are known on the host
+int64_t expected_mblocks(const moe_dims_t* dm, int64_t br, int64_t max_mb, int n_shared) {
+  const int64_t n = dm->T * dm->k, active = n < dm->E ? n : dm->E;
+  int64_t est_mb = active > 0 ? active * (((n + active - 1) / active + br - 1) / br) : 1;
+  est_mb += static_cast<int64_t>(n_shared) * ((dm->T + br - 1) / br);
+  return est_mb < max_mb ? est_mb : max_mb;
+}
+
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
            const FfnWs& fw, hipStream_t s, bool planned = false, const SharedExperts& sh = SharedExperts{}) {
@@ -250,12 +260,9 @@ int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32
                                        fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, s))) return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
-  // expected m-blocks under even routing (the list holds at most max_mb)
-  const int64_t n = dm->T * dm->k, active = n < dm->E ? n : dm->E, br = regime_block_rows(regime);
-  int64_t est_mb = active > 0 ? active * (((n + active - 1) / active + br - 1) / br) : 1;
-  est_mb += static_cast<int64_t>(sh.n) * ((dm->T + br - 1) / br);
   return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
-                               est_mb < fw.max_mb ? est_mb : fw.max_mb, dm->d, dm->f, sh, s));
+                               expected_mblocks(dm, regime_block_rows(regime), fw.max_mb, sh.n), dm->d, dm->f, sh,
+                               s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
@@ -291,10 +298,23 @@ int bwd_shape_ok(const moe_dims_t* dm) {
 }
 
 // The layer: route, dispatch, grouped FFN over the routed (and shared) rows, combine.
+// FC1, FC2 and combine as one persistent launch (the plan already in fw).
+int do_ffn_fused(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* inv_perm,
+                 const float* topk_w, const void* w1, const void* w3, const void* w2, void* y, void* out,
+                 const FfnWs& fw, const SharedExperts& sh, hipStream_t s) {
+  if (int st = hip_status(launch_fill_zero(reinterpret_cast<float*>(fw.sync),
+                                           static_cast<int64_t>(fused_sync_words(fw.max_mb)), s)))
+    return st;
+  StageScope sc(MOE_STAGE_FFN_FUSED, s);
+  return hip_status(launch_ffn_fused(x, perm, dm->k, dm->T, w1, w3, w2, fw.h, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
+                                     expected_mblocks(dm, 256, fw.max_mb, sh.n), dm->d, dm->f, inv_perm, topk_w, out,
+                                     fw.sync, sh, s));
+}
+
 int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, const void* wg, const float* bias,
               const void* w1, const void* w3, const void* w2, void* out, float* logits, int32_t* topk_idx,
               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
-              size_t ws_bytes, void* stream) {
+              size_t ws_bytes, void* stream, bool fused = false) {
   if (int st = check_dims(dm)) return st;
   if (dm->T == 0) return MOE_OK;
   if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(out) ||
@@ -302,6 +322,7 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
       !ok4_or_null(offsets) || !ok4_or_null(perm) || !ok4_or_null(inv_perm))
     return MOE_ERR_INVALID;
   if (int st = ffn_shape_ok(dm, sh.n)) return st;
+  if (fused && dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
   if (ws_bytes < layer_ws(dm, nullptr, nullptr, sh.n)) return MOE_ERR_WORKSPACE;
   LayerWs lw{};
@@ -329,11 +350,29 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
                                                     plan_inline ? fw.n_mblocks : nullptr, s)))
         return st;
     }
+    if (fused) {
+      if (!plan_inline) {
+        StageScope sc(MOE_STAGE_PLAN, s);
+        if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, 256, fw.mblocks, fw.n_mblocks, s,
+                                            sh.n, dm->T)))
+          return st;
+      }
+      return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s);
+    }
     if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, plan_inline, sh)) return st;
   } else {
     PermuteWs pw{};
     permute_ws(dm, lw.sub, &pw);
     if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
+    if (fused) {
+      {
+        StageScope sc(MOE_STAGE_PLAN, s);
+        if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, 256, fw.mblocks, fw.n_mblocks, s,
+                                            sh.n, dm->T)))
+          return st;
+      }
+      return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s);
+    }
     if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, false, sh)) return st;
   }
   return do_combine(dm, lw.y, inv_perm, topk_w, out, s, sh.n);
@@ -431,6 +470,14 @@ int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const
                       int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
                    perm, inv_perm, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_fused(const moe_dims_t* dm, const void* x, const void* wg, const float* bias,
+                            const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                            int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
+                   perm, inv_perm, ws, ws_bytes, stream, true);
 }
 
 size_t moe_workspace_bytes_shared(const moe_dims_t* dm, int n_shared) {

@@ -1,0 +1,92 @@
+"""The fused FFN launch (moe_layer_forward_fused): FC1, FC2 and the combine in one
+persistent kernel with device-side readiness counters.
+
+Its tiles do exactly the arithmetic of moe_layer_forward's separate launches,
+so the bar is bitwise equality with that path (itself held to the oracle in
+test_gpu_parity.py), checked twice in a row on the same buffers (a missed
+wait or a stale read would show up as a difference), plus the oracle bar on
+small shapes directly.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+import mixture_experts_layer_gate_amd as moe
+from conftest import to_numpy
+from parity import OUT_TOL, gpu_float, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _both(cfg_or_shape, seed=0):
+    if isinstance(cfg_or_shape, str):
+        cfg = moe_inputs.config(cfg_or_shape)
+        inp = moe_inputs.make_layer_inputs(cfg, seed, "cuda")
+        T, d, f, E, k = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
+    else:
+        T, d, f, E, k, s = cfg_or_shape
+        inp = moe_inputs.random_inputs(T, d, f, E, k, "bf16", s, seed, device="cuda")
+    dims = moe.Dims(T, d, f, E, k, torch.bfloat16)
+    ref = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    ws = moe.make_workspace(dims)
+    outs = []
+    for _ in range(2):
+        out, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], ws=ws,
+                                   return_routing=True, fused=True)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    return inp, ref, outs, r
+
+
+FUSED_SHAPES = [
+    # T, d, f, E, k, bias scale
+    (200, 256, 512, 8, 2, 0.0),
+    (300, 512, 768, 4, 2, 1.5),
+    (64, 256, 256, 16, 4, 2.0),      # experts without rows
+    (40, 128, 256, 8, 8, 0.0),       # k = E
+    (1, 256, 256, 4, 2, 0.0),
+    (1000, 512, 1024, 8, 2, 0.0),    # several m-blocks per expert
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
+def test_fused_small_bitwise_and_oracle(shape):
+    _say(f"case fused {shape}")
+    inp, ref, outs, r = _both(shape)
+    for o in outs:
+        assert torch.equal(o, ref)
+    T, d, f, E, k, _ = shape
+    h = {n: to_numpy(v, "bf16") for n, v in inp.items()}
+    want = oracle.layer_forward(h["x"], h["wg"], h["bias"], h["w1"], h["w3"], h["w2"], k, "bf16")["out"]
+    err = rel_err(gpu_float(outs[0]), want)
+    _say(f"  bitwise equal to the separate launches; out rel_err={err:.2e}")
+    assert err <= OUT_TOL
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill_skew", "dbrx_zipf", "deepseek_skew",
+                                  "deepseek_bal"])
+def test_fused_full_size_bitwise(name):
+    _say(f"case fused full {name}")
+    _, ref, outs, _ = _both(name)
+    for o in outs:
+        assert torch.equal(o, ref)
+    _say("  bitwise equal to the separate launches, twice")
+
+
+def test_fused_rejects_fp32():
+    cfg = moe_inputs.config("tiny_fp32")
+    inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    dims = moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, torch.float32)
+    with pytest.raises(moe.MoeError) as ex:
+        moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], fused=True)
+    assert ex.value.status == 2
