@@ -788,20 +788,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // rows may start as soon as that block's FC1 tiles are stored; MegaFlux,
 // section 2.1, MegaMoE's tiled FC1/FC2).
 //
-// Tiles are handed out in one increasing sequence by an atomic counter: all
-// FC1 tiles, then all FC2 tiles, then the combine's token blocks. An FC2 tile
-// waits until every FC1 tile of its m-block has been stored; a combine block
-// waits until every FC2 tile has. A tile only ever waits on tiles with lower
-// numbers, which running workgroups took earlier and finish without waiting
-// on anything later, so the launch cannot deadlock whatever the number of
-// resident workgroups. Each wait is bounded: past the limit the workgroup
-// sets an error word and goes on (the results are then wrong, never a hang).
-// Producers publish with a device-scope release (their stores reach the
-// point of coherence of every XCD's L2); consumers take a device-scope
-// acquire before reading.
-// sync words: [0] next tile, [1] FC2 tiles stored, [2] error flags,
-// [4 + mb] FC1 tiles of m-block mb stored.
-constexpr int kFusedSyncHead = 4;
+// Tiles are handed out by atomic counters, one per group of workgroups
+// b = x (mod 8) (the workgroups of one XCD): group x takes, in order, its share
+// of the FC1 tiles, then its share of the FC2 tiles, then its share of the
+// combine's token blocks, each share being the tiles the separate launches'
+// XCD-aware numbering gives that XCD (so neighbouring tiles meet in one L2).
+// An FC2 tile waits until every FC1 tile of its m-block has been stored; a
+// combine block waits until every FC2 tile has. No launch can deadlock: a
+// group takes an FC2 tile only after all of its FC1 tiles are taken, every
+// taken FC1 tile belongs to a running workgroup that finishes it without
+// waiting, and likewise for FC2 tiles under the combine; the grid is a
+// multiple of 8, so every group has workgroups. Each wait is bounded: past
+// the limit the workgroup sets an error word and goes on (the results are
+// then wrong, never a hang). Producers publish with a device-scope release
+// (their stores reach the point of coherence of every XCD's L2); consumers
+// take a device-scope acquire before reading.
+// sync words: [0..7] next tile of each group, [8] FC2 tiles stored,
+// [9] error flags, [16 + mb] FC1 tiles of m-block mb stored.
+constexpr int kFusedSyncHead = 16;
 [[maybe_unused]] constexpr int kCombineTokens = 8;  // tokens per combine block
 [[maybe_unused]] constexpr int kSpinLimit = 1 << 22;  // polls of a readiness counter before giving up
 
@@ -852,23 +856,30 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
   const int64_t n1 = F1::tiles(a.fc1), n2 = F2::tiles(a.fc2);
   const int64_t nc = (a.T + kCombineTokens - 1) / kCombineTokens;
   const int nbc1 = static_cast<int>((a.fc1.N + 127) / 128);  // FC1 tiles per m-block
-  int32_t* err = a.sync + 2;
+  int32_t* fc2_done = a.sync + 8;
+  int32_t* err = a.sync + 9;
   int32_t* done1 = a.sync + kFusedSyncHead;
+  // group x = blockIdx.x % 8 owns, in every round of G tiles, tiles
+  // x*W .. x*W + W-1 (W = G / 8): its share of n tiles, and its j-th tile
+  const int64_t G = gridDim.x, W = G / 8, x = blockIdx.x % 8;
+  auto share = [&](int64_t n) { return (n / G) * W + min(max(n % G - x * W, int64_t(0)), W); };
+  auto nth = [&](int64_t j) { return (j / W) * G + x * W + j % W; };
+  const int64_t s1 = share(n1), s2 = share(n2), sc = share(nc);
   for (;;) {
     __syncthreads();  // the previous tile is done with the buffers
     if (threadIdx.x == 0)
-      *s_tile = __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_tile = __hip_atomic_fetch_add(a.sync + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int64_t t = *s_tile;
+    const int64_t j = *s_tile;
     __syncthreads();  // every thread has read it before the tile's loads refill the buffers
-    if (t < n1) {
-      F1::tile(a.fc1, lds, t, [](int) {}, [&](int mb) { publish(done1 + mb); });
-    } else if (t < n1 + n2) {
-      F2::tile(a.fc2, lds, t - n1, [&](int mb) { wait_count(done1 + mb, nbc1, err); },
-               [&](int) { publish(a.sync + 1); });
-    } else if (t < n1 + n2 + nc) {
-      wait_count(a.sync + 1, static_cast<int>(n2), err);
-      const int64_t t0 = (t - n1 - n2) * kCombineTokens;
+    if (j < s1) {
+      F1::tile(a.fc1, lds, nth(j), [](int) {}, [&](int mb) { publish(done1 + mb); });
+    } else if (j < s1 + s2) {
+      F2::tile(a.fc2, lds, nth(j - s1), [&](int mb) { wait_count(done1 + mb, nbc1, err); },
+               [&](int) { publish(fc2_done); });
+    } else if (j < s1 + s2 + sc) {
+      wait_count(fc2_done, static_cast<int>(n2), err);
+      const int64_t t0 = nth(j - s1 - s2) * kCombineTokens;
       const int64_t nt = a.T - t0 < kCombineTokens ? a.T - t0 : kCombineTokens;
       const int64_t nvec = a.d / 8;
       for (int64_t q = threadIdx.x; q < nt * nvec; q += 512)
@@ -1014,7 +1025,9 @@ hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T
     const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
     narrow = t192 < t256;
   }
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * ((f + 127) / 128), cus)));
+  // a multiple of 8 workgroups (every tile group must have workgroups), at most one per CU
+  int64_t grid = std::min<int64_t>(max_mb * ((f + 127) / 128), cus) / 8 * 8;
+  if (grid < 8) grid = 8;
   if (narrow)
     hipLaunchKernelGGL((ffn_fused_kernel<192, 4, 2>), dim3(grid), dim3(512), 0, s, a);
   else
