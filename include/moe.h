@@ -197,8 +197,9 @@ int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* w
  * dwg [E][d], dbias [E], dw1 [E][f][d], dw3 [E][f][d], dw2 [E][d][f] fp32
  * (every entry written, zero for experts that received no rows); optional
  * (NULL to skip) dlogits [T][E] and dtopk_w [T][k] fp32.
- * FC1 is recomputed (g and u are not kept by the forward); the weights are
- * transposed into the workspace each call. Accumulation is fp32 throughout;
+ * FC1 is recomputed (g and u are not kept by the forward); W1, W3 and W2
+ * are read as stored (the DGrad products take them through transposing LDS
+ * loads, no copies). Accumulation is fp32 throughout;
  * dg, du, h and w*dout enter the matrix products as bf16. Every reduction
  * has a fixed order: results are deterministic.
  * Limits: d and f multiples of 256, else MOE_ERR_UNSUPPORTED; pointers
@@ -226,7 +227,7 @@ enum {
   MOE_STAGE_FC2 = 7,      /* grouped FC2 */
   MOE_STAGE_COMBINE = 8,  /* weighted combine */
   MOE_STAGE_DISPATCH = 9, /* single-workgroup histogram + scan + scatter (+ tile plan) */
-  MOE_STAGE_BWD_WT = 10,      /* backward: weight transposes */
+  MOE_STAGE_BWD_WT = 10,      /* reserved (the backward reads the weights as stored) */
   MOE_STAGE_BWD_FC1 = 11,     /* backward: FC1 recompute (g | u) */
   MOE_STAGE_BWD_DH = 12,      /* backward: DGrad of FC2 (q = dout W2) */
   MOE_STAGE_BWD_SWIGLU = 13,  /* backward: dg | du and dtopk_w */

@@ -1,5 +1,6 @@
 // Backward pass of the MoE expert layer: everything except the grouped GEMMs
-// (which are forms of the large-tile GEMM in ffn.hip).
+// (which are forms of the large-tile GEMM in ffn.hip; the DGrad forms read
+// W1, W3 and W2 as stored, through transposing LDS loads).
 //
 // The pages name the backward's parts: token blocks stream through DGrad and
 // WGrad, and the final top-k sum stays a step of its own (MegaFlux, section
@@ -15,8 +16,6 @@
 //   dx_t += sum_j dl_j Wg_{e_j}.
 //
 // Kernels here:
-// * transpose_kernel: [R][C] -> [C][R] bf16 tiles through LDS (the weights, so
-//   that every GEMM reads both operands K-contiguous);
 // * colmap_kernel: each expert's rows padded to a multiple of 64 columns in
 //   the transposed activations (the WGrad K dimension), and the column -> row map;
 // * gather_transpose_kernel: transposed activations for WGrad (x and dout rows
@@ -61,38 +60,6 @@ __device__ __forceinline__ int32_t clamp_assign(int32_t a, int64_t n) {
 
 constexpr int kTT = 64;        // transpose tile (elements per side)
 constexpr int kTP = kTT + 2;   // LDS row pitch (elements)
-
-// dst[b][c][dst_col0 + r] = src[b][r][c]; R and C are multiples of 64.
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
-                                                        int64_t R, int64_t C, int64_t src_bstride,
-                                                        int64_t dst_bstride, int64_t dst_pitch, int64_t dst_col0) {
-  __shared__ bf16_t tile[kTT * kTP];
-  const int tid = threadIdx.x;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTT, r0 = static_cast<int64_t>(blockIdx.y) * kTT;
-  const bf16_t* s = src + blockIdx.z * src_bstride;
-  bf16_t* d = dst + blockIdx.z * dst_bstride;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rr = tid / 8 + 32 * i, cc = (tid % 8) * 8;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(s + (r0 + rr) * C + c0 + cc);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      tile[rr * kTP + cc + 2 * m] = static_cast<bf16_t>(v[m] & 0xffffu);
-      tile[rr * kTP + cc + 2 * m + 1] = static_cast<bf16_t>(v[m] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int cc = tid / 8 + 32 * i, rr = (tid % 8) * 8;
-    u32x4_t v;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      v[m] = static_cast<uint32_t>(tile[(rr + 2 * m) * kTP + cc]) |
-             (static_cast<uint32_t>(tile[(rr + 2 * m + 1) * kTP + cc]) << 16);
-    *reinterpret_cast<u32x4_t*>(d + (c0 + cc) * dst_pitch + dst_col0 + r0 + rr) = v;
-  }
-}
 
 // One workgroup: kofs[e] = sum over e' < e of counts rounded up to 64, and
 // colmap[c] = the sorted row at padded column c, or -1 for padding.
@@ -375,15 +342,6 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 int gate_parts() { return kGateParts; }
-
-hipError_t launch_transpose(const void* src, void* dst, int64_t R, int64_t C, int batch, int64_t src_bstride,
-                            int64_t dst_bstride, int64_t dst_pitch, int64_t dst_col0, hipStream_t s) {
-  if (batch <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>(C / kTT), static_cast<unsigned>(R / kTT), batch),
-                     dim3(256), 0, s, static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), R, C, src_bstride,
-                     dst_bstride, dst_pitch, dst_col0);
-  return hipGetLastError();
-}
 
 hipError_t launch_colmap(const int32_t* counts, const int32_t* offsets, int E, int64_t rows, int64_t cols,
                          int32_t* kofs, int32_t* colmap, hipStream_t s) {

@@ -53,6 +53,10 @@ struct GemmArgs {
   int64_t M;              // output rows per expert (rows of A)
   int64_t split;          // output rows per output tensor (M, or M / 2 with C2)
   int n_experts;
+  // rows of the m-block's A (non-gathered forms): row pitch in elements (0 = K)
+  // and first column; fp32 forms: add to C instead of storing
+  int64_t a_pitch, a_col0;
+  int accumulate;
 };
 
 // Token of sorted row p (FC1): routed rows through perm, shared rows directly.
@@ -338,13 +342,23 @@ enum GemmMode : int {
   kModeFc1 = 0,    // h = SiLU(x W1^T) * (x W3^T), A rows gathered by token, bf16 out
   kModeFc2 = 1,    // y = h W2^T, A = the m-block's rows, bf16 out
   kModeFc1GU = 2,  // g | u = x W1^T | x W3^T stored side by side ([rows][2N] bf16): the backward's recompute
-  kModeBwdQ = 3,   // q = dout W2 (B = W2 transposed), A rows gathered by token, fp32 out
-  kModeBwdDx = 4,  // dx rows = [dg | du] [W1 ; W3] (B = both transposed, K = 2f), fp32 out
+  kModeBwdQ = 3,   // q = dout W2 (B = W2 as stored, [K][N]), A rows gathered by token, fp32 out
+  kModeBwdDx = 4,  // dx rows += dg W1 or du W3 (A = one half of the dg|du rows, B as stored, K = f), fp32 out
   kModeWgrad = 5,  // dW_e = A_e B_e^T, K = expert e's padded rows, fp32 out
 };
 __host__ __device__ constexpr bool mode_gated(int m) { return m == kModeFc1 || m == kModeFc1GU; }
 __host__ __device__ constexpr bool mode_gather(int m) { return m == kModeFc1 || m == kModeFc1GU || m == kModeBwdQ; }
 __host__ __device__ constexpr bool mode_f32_out(int m) { return m >= kModeBwdQ; }
+// B stored [K][N] (rows N-contiguous): the weights read by the backward's DGrad
+__host__ __device__ constexpr bool mode_b_kn(int m) { return m == kModeBwdQ || m == kModeBwdDx; }
+
+// Swizzle of the 16-byte chunks of row k of a [K][256] bf16 LDS stage: chunk c
+// of row k sits in slot c ^ f(k). The transposing reads of a B fragment touch
+// 16 rows k = 8g + 4h + i (g, i in 0..3) at the same columns; f spreads every
+// half-wave over all 64 banks.
+__device__ __forceinline__ int kn_swz(int k) { return (k % 4) * 4 + (k / 4) % 4; }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // One tile of a large-tile GEMM form (the kernel's loop body): tile index ->
 // (m-block, n-block), operand descriptors, the pipelined K loop and the
@@ -355,6 +369,7 @@ template <int kMode, int BM, int BN, int WM, int WN>
 struct DlGemm {
   static constexpr bool kGated = mode_gated(kMode);
   static constexpr bool kWgrad = kMode == kModeWgrad;
+  static constexpr bool kBKN = mode_b_kn(kMode);
   static constexpr int BK = 64;                   // K per step
   static constexpr int RB = BK * 2;               // bytes per LDS row
   static constexpr int CPR = RB / 16;             // 16-byte chunks per row
@@ -373,6 +388,7 @@ struct DlGemm {
   static_assert(!kGated || (NJ16 % 2 == 0), "gated tiles pair gate and up blocks");
   static_assert(KS == 2, "two 32-wide sub-steps per 64-wide stage");
   static_assert(AI * NW * RPI == BM && BI * NW * RPI == BN, "load tiling");
+  static_assert(!kBKN || (BN == 256 && !kGated), "[K][N] weights: 512-byte LDS rows, two per load instruction");
   // LDS: two A buffers, then as many B buffers (up to 8) as fit in the CU's
   // 160 KB, so weight loads run NBB-1 steps ahead
   static constexpr int A_ST = BM * RB, B_ST = BN * RB;
@@ -469,12 +485,13 @@ struct DlGemm {
           }
         }
       } else {
-        const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * K * 2);
-        ars = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(row0) * K * 2, hb);
+        const int64_t ap = g.a_pitch > 0 ? g.a_pitch : K;  // row pitch of A (elements)
+        const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * ap * 2);
+        ars = make_rsrc(static_cast<const char*>(g.A) + (static_cast<int64_t>(row0) * ap + g.a_col0) * 2, hb);
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
           const int r = (wv * AI + i) * RPI + lrow;
-          aoff[i] = r < rows ? static_cast<uint32_t>(r * K * 2) + chunk_off(((wv * AI + i) * PH) % CPR) : hb;
+          aoff[i] = r < rows ? static_cast<uint32_t>(r * ap * 2) + chunk_off(((wv * AI + i) * PH) % CPR) : hb;
         }
       }
     }
@@ -484,7 +501,20 @@ struct DlGemm {
     // columns); weight gradients: rows of the transposed operand, K window of expert e.
     __amdgpu_buffer_rsrc_t brs0, brs1;
     uint32_t boff[BI];
-    if constexpr (kWgrad) {
+    if constexpr (kBKN) {
+      // [K][N] weights (DGrad reads them as stored): a stage is BK rows of BN
+      // columns, 512 bytes per row, two rows per load instruction; the lane that
+      // fills slot c' of row r fetches chunk c' ^ f(r).
+      const int64_t ebytes = K * N * 2;
+      brs0 = make_rsrc(expert_base(g, g.B0, g.S0, e, ebytes), static_cast<uint32_t>(ebytes));
+      brs1 = brs0;
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int r = 2 * (wv * BI + i) + lane / 32;  // stage row of this lane's 16 bytes
+        boff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * N * 2 + static_cast<int64_t>(nb) * BN * 2 +
+                                        ((lane % 32) ^ kn_swz(r)) * 16);
+      }
+    } else if constexpr (kWgrad) {
       const int k0 = g.kofs[e];
       brs0 = make_rsrc(static_cast<const char*>(g.B0) + static_cast<int64_t>(k0) * 2,
                        static_cast<uint32_t>((N * g.pitch - k0) * 2));
@@ -538,6 +568,16 @@ struct DlGemm {
     auto issue_b = [&](int slot, int kt) {
       const bool real = kt < nk;
       char* sb = lds + NBA * A_ST + slot * B_ST;
+      if constexpr (kBKN) {
+        // step kt is weight rows kt*BK..
+        const uint32_t koff = real ? static_cast<uint32_t>(kt) * static_cast<uint32_t>(BK * N * 2) : 0u;
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? brs0 : nul,
+                                                   (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024),
+                                                   16, boff[i], koff, 0, 0);
+        return;
+      }
       const uint32_t koff = real ? static_cast<uint32_t>(kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
@@ -564,6 +604,27 @@ struct DlGemm {
     };
     auto read_b = [&](int set, int s, int b_slot) {
       const char* sb = lds + NBA * A_ST + b_slot * B_ST;
+      if constexpr (kBKN) {
+        // Transposing reads (ds_read_b64_tr_b16): in each group of 16 lanes,
+        // lane 16g + 4i + q reads 4 columns 4q.. of row k = 8g + 4h + i, and the
+        // instruction hands lane l the column l % 16 of rows 8(l / 16) + 4h + 0..3:
+        // two reads (h = 0, 1) give the fragment's 8 K values of one column.
+        // Per lane: row k0 = 8g + 4h + i of the 32-row sub-step, the byte within
+        // the 16-byte chunk, and the row's swizzle (f(32s + k0) = f(k0)).
+#pragma unroll
+        for (int j = 0; j < NJ16; ++j) {
+          const int c = (wn * TN + 16 * j) / 8 + (lane % 4) / 2;  // 16-byte chunk of the lane's 4 columns
+          i16x4_t half[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int k0 = 8 * (lane / 16) + 4 * h + (lane % 16) / 4;
+            const char* p = sb + s * (32 * 512) + k0 * 512 + (lane % 2) * 8 + ((c ^ kn_swz(k0)) & 31) * 16;
+            half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+          }
+          fb[set][j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < NJ16; ++j) {
         int brow;
@@ -693,9 +754,11 @@ struct DlGemm {
         for (int q = tid; q < SR * VPR; q += NT) {
           const int rl = q / VPR, c4 = (q % VPR) * 4;
           const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
-          if (r < rows && col0 + c4 < N)
-            *reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * N + col0 + c4) =
-                *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
+          if (r < rows && col0 + c4 < N) {
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * N + col0 + c4);
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
+            *dst = g.accumulate ? *dst + v : v;
+          }
         }
       }
     } else {
@@ -974,16 +1037,22 @@ hipError_t launch_fc1_gu(const void* x, const int32_t* perm, int k, int64_t T, c
   return launch_big<kModeFc1GU, 256, 256, 2, 4>(a, max_mb, f, s);
 }
 
-hipError_t launch_bwd_q(const void* dout, const int32_t* perm, int k, int64_t T, const void* w2t, float* q,
+hipError_t launch_bwd_q(const void* dout, const int32_t* perm, int k, int64_t T, const void* w2, float* q,
                         const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
                         hipStream_t s) {
-  GemmArgs a{dout, perm, k, T, w2t, nullptr, q, mblocks, n_mblocks, d, f, T * k, nullptr, nullptr, INT32_MAX};
+  GemmArgs a{dout, perm, k, T, w2, nullptr, q, mblocks, n_mblocks, d, f, T * k, nullptr, nullptr, INT32_MAX};
   return launch_big<kModeBwdQ, 256, 256, 2, 4>(a, max_mb, f, s);
 }
 
-hipError_t launch_bwd_dx(const void* dgu, const void* w13t, float* dxs, const int4* mblocks,
+hipError_t launch_bwd_dx(const void* dgu, const void* w1, const void* w3, float* dxs, const int4* mblocks,
                          const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s) {
-  GemmArgs a{dgu, nullptr, 1, 0, w13t, nullptr, dxs, mblocks, n_mblocks, 2 * f, d, 0, nullptr, nullptr, INT32_MAX};
+  // two passes over the dg|du rows: dxs = dg W1, then dxs += du W3
+  GemmArgs a{dgu, nullptr, 1, 0, w1, nullptr, dxs, mblocks, n_mblocks, f, d, 0, nullptr, nullptr, INT32_MAX};
+  a.a_pitch = 2 * f;
+  if (hipError_t err = launch_big<kModeBwdDx, 256, 256, 2, 4>(a, max_mb, d, s)) return err;
+  a.B0 = w3;
+  a.a_col0 = f;
+  a.accumulate = 1;
   return launch_big<kModeBwdDx, 256, 256, 2, 4>(a, max_mb, d, s);
 }
 

@@ -86,19 +86,17 @@ hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, con
 hipError_t launch_fc1_gu(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
                          void* gu, const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d,
                          int64_t f, hipStream_t s);
-// q[p] = dout[token(p)] W2_e (w2t = W2 transposed, [E][f][d]), fp32 [rows][f].
-hipError_t launch_bwd_q(const void* dout, const int32_t* perm, int k, int64_t T, const void* w2t, float* q,
+// q[p] = dout[token(p)] W2_e (w2 as stored, [E][d][f], read through transposing LDS loads), fp32 [rows][f].
+hipError_t launch_bwd_q(const void* dout, const int32_t* perm, int k, int64_t T, const void* w2, float* q,
                         const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
                         hipStream_t s);
-// dxs[p] = dgu[p] [W1_e ; W3_e] (w13t = [E][d][2f]), fp32 [rows][d].
-hipError_t launch_bwd_dx(const void* dgu, const void* w13t, float* dxs, const int4* mblocks,
+// dxs[p] = dg[p] W1_e + du[p] W3_e (w1, w3 as stored, [E][f][d]; two launches), fp32 [rows][d].
+hipError_t launch_bwd_dx(const void* dgu, const void* w1, const void* w3, float* dxs, const int4* mblocks,
                          const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
 // Weight gradients C_e = A_e B_e^T over expert e's padded K window [kofs[e], kofs[e+1]);
 // A [M][pitch], B [N][pitch] bf16; output rows >= split go to c2. M, N multiples of 256.
 hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, const int32_t* kofs, int64_t pitch,
                         int E, int64_t M, int64_t N, int64_t split, hipStream_t s);
-hipError_t launch_transpose(const void* src, void* dst, int64_t R, int64_t C, int batch, int64_t src_bstride,
-                            int64_t dst_bstride, int64_t dst_pitch, int64_t dst_col0, hipStream_t s);
 hipError_t launch_colmap(const int32_t* counts, const int32_t* offsets, int E, int64_t rows, int64_t cols,
                          int32_t* kofs, int32_t* colmap, hipStream_t s);
 // mode 0: rows of src (x or dout) by token, 2: w * SiLU(g) u from gu, 3: dgu rows.

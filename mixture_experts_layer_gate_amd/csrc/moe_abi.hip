@@ -150,7 +150,6 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 // activations (every expert's rows rounded up to a multiple of 64).
 struct BwdWs {
   int4* mblocks; int32_t* n_mblocks; int64_t max_mb;
-  void* w2t; void* w13t;         // [E][f][d], [E][d][2f] bf16
   void* gu; void* dgu;           // [P][2f] bf16
   float* q;                      // [P][f]
   float* dxs;                    // [P][d]
@@ -169,8 +168,6 @@ size_t bwd_ws(const moe_dims_t* dm, void* ws, BwdWs* out) {
   r.pp = (P + 63) / 64 * 64 + 64 * E;
   r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
   r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
-  r.w2t = c.take<char>(size_t(2) * E * f * d);
-  r.w13t = c.take<char>(size_t(2) * E * d * 2 * f);
   r.gu = c.take<char>(size_t(2) * P * 2 * f);
   r.dgu = c.take<char>(size_t(2) * P * 2 * f);
   r.q = c.take<float>(sizeof(float) * P * f);
@@ -541,20 +538,13 @@ int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, cons
     if (int st = hip_status(launch_plan(counts, offsets, E, P, b.max_mb, 256, b.mblocks, b.n_mblocks, s))) return st;
   }
   {
-    StageScope sc(MOE_STAGE_BWD_WT, s);
-    // W2 [E][d][f] -> [E][f][d]; W1, W3 [E][f][d] -> the two column halves of [E][d][2f]
-    if (int st = hip_status(launch_transpose(w2, b.w2t, d, f, E, d * f, f * d, d, 0, s))) return st;
-    if (int st = hip_status(launch_transpose(w1, b.w13t, f, d, E, f * d, d * 2 * f, 2 * f, 0, s))) return st;
-    if (int st = hip_status(launch_transpose(w3, b.w13t, f, d, E, f * d, d * 2 * f, 2 * f, f, s))) return st;
-  }
-  {
     StageScope sc(MOE_STAGE_BWD_FC1, s);
     if (int st = hip_status(launch_fc1_gu(x, perm, k, T, w1, w3, b.gu, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
       return st;
   }
   {
     StageScope sc(MOE_STAGE_BWD_DH, s);
-    if (int st = hip_status(launch_bwd_q(dout, perm, k, T, b.w2t, b.q, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
+    if (int st = hip_status(launch_bwd_q(dout, perm, k, T, w2, b.q, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
       return st;
   }
   {
@@ -568,7 +558,7 @@ int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, cons
   }
   {
     StageScope sc(MOE_STAGE_BWD_DX, s);
-    if (int st = hip_status(launch_bwd_dx(b.dgu, b.w13t, b.dxs, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
+    if (int st = hip_status(launch_bwd_dx(b.dgu, w1, w3, b.dxs, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
       return st;
   }
   {
