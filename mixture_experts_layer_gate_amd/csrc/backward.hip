@@ -295,7 +295,27 @@ __global__ __launch_bounds__(256) void dwg_partial_kernel(const bf16_t* __restri
     float acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
-    for (int64_t p = lo; p < hi; ++p) {
+    // rows ascending; eight rows' loads are issued before their products are added
+    constexpr int U = 8;
+    int64_t p = lo;
+    for (; p + U <= hi; p += U) {
+      u32x4_t xr[U];
+      float l[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t a = clamp_assign(perm[p + u], n_assign);
+        l[u] = dl[a];
+        xr[u] = *reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(a / k) * d + c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float xv[8];
+        unpack8(xr[u], xv);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] += l[u] * xv[m];
+      }
+    }
+    for (; p < hi; ++p) {
       const int32_t a = clamp_assign(perm[p], n_assign);
       const float l = dl[a];
       float xv[8];
@@ -307,10 +327,14 @@ __global__ __launch_bounds__(256) void dwg_partial_kernel(const bf16_t* __restri
     *reinterpret_cast<f32x4_t*>(o) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4_t*>(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    float s = 0.0f;
-    for (int64_t p = lo; p < hi; ++p) s += dl[clamp_assign(perm[p], n_assign)];
-    bpart[r * E + e] = s;
+  if (blockIdx.x == 0) {
+    // bias part: thread t sums rows lo + t, lo + t + 256, ... in order, then a
+    // fixed-order reduction over the workgroup
+    __shared__ float red[4];
+    float sb = 0.0f;
+    for (int64_t q = lo + threadIdx.x; q < hi; q += 256) sb += dl[clamp_assign(perm[q], n_assign)];
+    sb = block_sum_256(sb, red);
+    if (threadIdx.x == 0) bpart[r * E + e] = sb;
   }
 }
 
