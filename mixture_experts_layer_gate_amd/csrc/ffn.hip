@@ -57,7 +57,40 @@ struct GemmArgs {
   // and first column; fp32 forms: add to C instead of storing
   int64_t a_pitch, a_col0;
   int accumulate;
+  // split K, for launches with fewer tiles than CUs: each tile's K steps are
+  // cut into parts, each part's fp32 accumulators go to `partial`
+  // ([virtual tile][BM][BN]), and splitk_reduce_kernel sums them in part order.
+  // At most `splits` parts, at most split_target virtual tiles in all, at
+  // most partial_cap of them stored.
+  float* partial;
+  int splits, split_target, partial_cap;
 };
+
+// Parts per tile of a launch of `ntiles` tiles (1: no split): as many as keep
+// the virtual tiles within one round of split_target workgroups. The GEMM and
+// the reduce kernel derive the same number from the same plan.
+__device__ __forceinline__ int eff_splits(const GemmArgs& g, int64_t ntiles) {
+  if (g.splits <= 1 || ntiles <= 0 || ntiles >= g.split_target) return 1;
+  int64_t s = g.split_target / ntiles;
+  if (s > g.splits) s = g.splits;
+  if (s * ntiles > g.partial_cap) s = g.partial_cap / ntiles;
+  return s < 2 ? 1 : static_cast<int>(s);
+}
+
+// m-block and column block of tile `tile` of a plan-driven launch: tiles run
+// group by group (the plan's runs of up to kTileGroup m-blocks of one expert),
+// m-block-fastest inside a group; a malformed group entry falls back to a
+// group of one.
+__device__ __forceinline__ void decode_group_tile(const GemmArgs& g, int64_t tile, int nbc, int nmb, int& mb,
+                                                  int& nb) {
+  const int row = static_cast<int>(tile / nbc);
+  const int info = g.mblocks[row].w;
+  int m0 = info >> 4, gs = info & 15;
+  if (gs < 1 || gs > kTileGroup || m0 > row || row >= m0 + gs || m0 + gs > nmb) m0 = row, gs = 1;
+  const int64_t o = tile - static_cast<int64_t>(m0) * nbc;
+  mb = m0 + static_cast<int>(o % gs);
+  nb = static_cast<int>(o / gs);
+}
 
 // Token of sorted row p (FC1): routed rows through perm, shared rows directly.
 __device__ __forceinline__ int64_t row_token(const GemmArgs& g, int64_t p) {
@@ -398,16 +431,18 @@ struct DlGemm {
   static_assert(NBB >= 2, "two A and two B buffers fit in LDS");
   static constexpr int LDS_BYTES = NBA * A_ST + NBB * B_ST;
 
-  // tiles of one launch: m-blocks (or experts x output-row blocks) x column blocks
+  // tiles of one launch: m-blocks (or experts x output-row blocks) x column
+  // blocks, times the parts of a split launch
   __device__ static int64_t tiles(const GemmArgs& g) {
     const int64_t N = g.N;
     const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
     const int nmb = kWgrad ? g.n_experts * static_cast<int>(g.M / BM) : g.n_mblocks[0];
-    return static_cast<int64_t>(nmb) * nbc;
+    const int64_t nt = static_cast<int64_t>(nmb) * nbc;
+    return nt * eff_splits(g, nt);
   }
 
   template <class Pre, class Post>
-  __device__ static __forceinline__ void tile(const GemmArgs& g, char* lds, int64_t tile, Pre pre, Post post) {
+  __device__ static __forceinline__ void tile(const GemmArgs& g, char* lds, int64_t vtile, Pre pre, Post post) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
@@ -418,6 +453,11 @@ struct DlGemm {
     const int mbe = kWgrad ? static_cast<int>(g.M / BM) : 0;
     const int nmb = kWgrad ? g.n_experts * mbe : g.n_mblocks[0];
     int nk = static_cast<int>(K / BK);
+    // split launch: virtual tile = tile * sp + part, part covering K steps kt0 ..
+    const int sp = kWgrad ? 1 : eff_splits(g, static_cast<int64_t>(nmb) * nbc);
+    const int64_t tile = vtile / sp;
+    const int part = static_cast<int>(vtile % sp);
+    int kt0 = 0;
     const int lrow = lane / CPR;                                          // row within a load instruction
     // Chunk this lane fetches for a load instruction whose first row is R0.
     // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
@@ -454,16 +494,11 @@ struct DlGemm {
         aoff[i] = static_cast<uint32_t>((row0 + r2) * g.pitch * 2) + chunk_off(((wv * AI + i) * PH) % CPR);
       }
     } else {
-      // Tiles run group by group (the plan's runs of up to kTileGroup m-blocks
-      // of one expert), m-block-fastest inside a group; a malformed group entry
-      // falls back to a group of one.
-      const int row = static_cast<int>(tile / nbc);
-      const int info = g.mblocks[row].w;
-      int m0 = info >> 4, gs = info & 15;
-      if (gs < 1 || gs > kTileGroup || m0 > row || row >= m0 + gs || m0 + gs > nmb) m0 = row, gs = 1;
-      const int64_t o = tile - static_cast<int64_t>(m0) * nbc;
-      mb = m0 + static_cast<int>(o % gs);
-      nb = static_cast<int>(o / gs);
+      decode_group_tile(g, tile, nbc, nmb, mb, nb);
+      if (sp > 1) {
+        kt0 = static_cast<int>(static_cast<int64_t>(part) * nk / sp);
+        nk = static_cast<int>(static_cast<int64_t>(part + 1) * nk / sp) - kt0;
+      }
       const int4 blk = g.mblocks[mb];
       e = __builtin_amdgcn_readfirstlane(blk.x);
       row0 = __builtin_amdgcn_readfirstlane(blk.y);
@@ -558,7 +593,7 @@ struct DlGemm {
     auto issue_a = [&](int slot, int kt) {
       const bool real = kt < nk;
       char* sa = lds + slot * A_ST;
-      const uint32_t koff = real ? static_cast<uint32_t>(kt) * RB : 0u;
+      const uint32_t koff = real ? static_cast<uint32_t>(kt0 + kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < AI; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -570,7 +605,7 @@ struct DlGemm {
       char* sb = lds + NBA * A_ST + slot * B_ST;
       if constexpr (kBKN) {
         // step kt is weight rows kt*BK..
-        const uint32_t koff = real ? static_cast<uint32_t>(kt) * static_cast<uint32_t>(BK * N * 2) : 0u;
+        const uint32_t koff = real ? static_cast<uint32_t>(kt0 + kt) * static_cast<uint32_t>(BK * N * 2) : 0u;
 #pragma unroll
         for (int i = 0; i < BI; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? brs0 : nul,
@@ -578,7 +613,7 @@ struct DlGemm {
                                                    16, boff[i], koff, 0, 0);
         return;
       }
-      const uint32_t koff = real ? static_cast<uint32_t>(kt) * RB : 0u;
+      const uint32_t koff = real ? static_cast<uint32_t>(kt0 + kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
         const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
@@ -721,7 +756,7 @@ struct DlGemm {
       }
     }
 
-    if constexpr (mode_f32_out(kMode)) {
+    if (mode_f32_out(kMode) || sp > 1) {
       // fp32 epilogue through LDS, one 16-row block i of every wave's rows at a
       // time (so the accumulators of block i die as it is stored): the waves
       // write acc[i] into a [WM * 16][BN + 4] tile (the 4-float pad spreads a
@@ -731,8 +766,14 @@ struct DlGemm {
       constexpr int SR = WM * 16;  // rows per slice
       static_assert(SR * CP * 4 <= LDS_BYTES, "slice fits in the stage buffers");
       float* ct = reinterpret_cast<float*>(lds);
+      // destination: rows of pitch cp from column col0, ncols columns in all
       float* cbase;
-      if constexpr (kWgrad) {
+      int64_t cp = N, col0 = static_cast<int64_t>(nb) * BN, ncols = N;
+      if (sp > 1) {
+        // one part of a split tile: the raw accumulators, [BM][BN]
+        cbase = g.partial + vtile * (BM * BN);
+        cp = BN, col0 = 0, ncols = BN;
+      } else if constexpr (kWgrad) {
         const int64_t m0 = static_cast<int64_t>(row0);
         const bool second = m0 >= g.split;
         cbase = static_cast<float*>(second ? g.C2 : g.C) + static_cast<int64_t>(e) * g.split * N +
@@ -740,7 +781,6 @@ struct DlGemm {
       } else {
         cbase = static_cast<float*>(g.C) + static_cast<int64_t>(row0) * N;
       }
-      const int64_t col0 = static_cast<int64_t>(nb) * BN;
       constexpr int VPR = BN / 4;  // 16-byte vectors per tile row
 #pragma unroll
       for (int i = 0; i < MI16; ++i) {
@@ -754,10 +794,10 @@ struct DlGemm {
         for (int q = tid; q < SR * VPR; q += NT) {
           const int rl = q / VPR, c4 = (q % VPR) * 4;
           const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
-          if (r < rows && col0 + c4 < N) {
-            f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * N + col0 + c4);
+          if (r < rows && col0 + c4 < ncols) {
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * cp + col0 + c4);
             const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
-            *dst = g.accumulate ? *dst + v : v;
+            *dst = (g.accumulate && sp == 1) ? *dst + v : v;
           }
         }
       }
@@ -955,6 +995,65 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
 #endif
 }
 
+// Second half of a split launch: per output element of every split tile, the
+// sum of its parts in part order, then what the GEMM's bf16 epilogue applies:
+// SiLU(g) * u for FC1 (a wave's TN accumulator columns hold TN/2 gate columns
+// then the TN/2 up columns of the same outputs), bf16 rounding.
+template <bool kGated, int BM, int BN, int WN>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+  constexpr int OC = kGated ? BN / 2 : BN;  // output columns of a tile
+  constexpr int TN = BN / WN;
+  const int64_t N = g.N;
+  const int nbc = static_cast<int>((N + OC - 1) / OC);
+  const int nmb = g.n_mblocks[0];
+  const int64_t nt = static_cast<int64_t>(nmb) * nbc;
+  const int sp = eff_splits(g, nt);
+  if (sp <= 1) return;  // the GEMM wrote its outputs itself
+  bf16_t* C = static_cast<bf16_t*>(g.C);
+  for (int64_t t = blockIdx.x; t < nt; t += gridDim.x) {
+    int mb, nb;
+    decode_group_tile(g, t, nbc, nmb, mb, nb);
+    const int4 blk = g.mblocks[mb];
+    const int row0 = blk.y, rows = blk.z;
+    const float* part = g.partial + t * sp * (BM * BN);
+    for (int q = threadIdx.x; q < rows * OC; q += blockDim.x) {
+      const int r = q / OC, oc = q % OC;
+      const int64_t col = static_cast<int64_t>(nb) * OC + oc;
+      if (col >= N) continue;
+      const int pc = kGated ? (oc / (TN / 2)) * TN + oc % (TN / 2) : oc;
+      const float* src = part + r * BN + pc;
+      float a = src[0];
+      float b = kGated ? src[TN / 2] : 0.f;
+      for (int p = 1; p < sp; ++p) {
+        a += src[p * (BM * BN)];
+        if constexpr (kGated) b += src[p * (BM * BN) + TN / 2];
+      }
+      const float v = kGated ? silu_mul(a, b) : a;
+      C[static_cast<int64_t>(row0 + r) * N + col] = static_cast<bf16_t>(f32_to_bf16_bits(v));
+    }
+  }
+}
+
+// Largest number of K parts per tile: each part keeps at least 8 K steps of
+// 64; MOE_SPLIT_K=0 in the environment turns splitting off (=n caps it at n).
+static int split_k_parts(int64_t K) {
+  int s = static_cast<int>(std::min<int64_t>(8, K / (64 * 8)));
+  if (const char* env = getenv("MOE_SPLIT_K")) {
+    const int v = atoi(env);
+    if (v >= 0 && v < s) s = v;
+  }
+  return s;
+}
+
+size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, int64_t f) {
+  if (dtype != 1 || regime < 1) return 0;
+  const int64_t cus = device_cu_count();
+  // FC1 tiles: 128 output columns; FC2: 192 or 256
+  const bool fc1 = max_mb * ((f + 127) / 128) < cus && split_k_parts(d) > 1;
+  const bool fc2 = max_mb * ((d + 255) / 256) < cus && split_k_parts(f) > 1;
+  return fc1 || fc2 ? static_cast<size_t>(cus) * 256 * 256 * sizeof(float) : 0;
+}
+
 static int persistent_grid(int64_t max_tiles) {
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
   int64_t g = max_tiles < cap ? max_tiles : cap;
@@ -985,13 +1084,40 @@ static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, h
   return hipGetLastError();
 }
 
+// Forward FC1/FC2 launch, split along K when even the largest plan has fewer
+// tiles than CUs (few rows and few experts: a decode step of a handful of
+// tokens) and the partial buffer is there; the tiles' parts then run on all
+// CUs and a second kernel sums them.
+template <int kMode, int BM, int BN, int WM, int WN>
+static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* partial, size_t partial_bytes,
+                             hipStream_t s) {
+  const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
+  const int64_t nb = (ncols + cols - 1) / cols;
+  const int64_t cus = device_cu_count();
+  const int parts = split_k_parts(a.K);
+  const int64_t cap = static_cast<int64_t>(partial_bytes / (sizeof(float) * BM * BN));
+  if (partial == nullptr || parts < 2 || max_mb * nb >= cus || max_mb * nb * 2 > cap)
+    return launch_big<kMode, BM, BN, WM, WN>(a, max_mb, ncols, s);
+  a.partial = partial;
+  a.splits = parts;
+  a.split_target = static_cast<int>(cus);
+  a.partial_cap = static_cast<int>(cap);
+  hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
+                     a);
+  if (hipError_t err = hipGetLastError()) return err;
+  hipLaunchKernelGGL((splitk_reduce_kernel<mode_gated(kMode), BM, BN, WN>), dim3(static_cast<int>(max_mb * nb)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, hipStream_t s) {
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f,
              T * k, sh.w1, sh.w3, sh.n > 0 ? sh.E_routed : INT32_MAX};
-  if (dtype == 1 && regime >= 1) return launch_big<kModeFc1, 256, 256, 2, 4>(a, max_mb, f, s);
+  if (dtype == 1 && regime >= 1)
+    return launch_fwd<kModeFc1, 256, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -1002,7 +1128,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, hipStream_t s) {
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d,
              0, sh.w2, nullptr, sh.n > 0 ? sh.E_routed : INT32_MAX};
   if (dtype == 1 && regime >= 1) {
@@ -1017,8 +1143,8 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
       const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
       narrow = t192 < t256;
     }
-    return narrow ? launch_big<kModeFc2, 256, 192, 4, 2>(a, max_mb, d, s)
-                  : launch_big<kModeFc2, 256, 256, 2, 4>(a, max_mb, d, s);
+    return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2>(a, max_mb, d, partial, partial_bytes, s)
+                  : launch_fwd<kModeFc2, 256, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, s);
   }
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)

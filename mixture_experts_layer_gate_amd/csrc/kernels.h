@@ -63,10 +63,13 @@ int regime_block_rows(int regime);
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, hipStream_t s);
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s);
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, hipStream_t s);
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s);
+// bytes of the split-K partial buffer a forward FFN of this shape can use (0:
+// its launches never split)
+size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, int64_t f);
 
 // FC1, FC2 and the combine in one persistent launch with device-side
 // readiness counters (bf16). sync: fused_sync_words(max_mb) int32, zero on entry.

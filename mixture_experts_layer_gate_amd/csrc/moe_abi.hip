@@ -108,7 +108,11 @@ size_t permute_ws(const moe_dims_t* dm, void* ws, PermuteWs* out) {
 // Sorted rows of the grouped FFN: T*k routed rows, then T rows per shared expert.
 int64_t ffn_rows(const moe_dims_t* dm, int n_shared) { return dm->T * dm->k + static_cast<int64_t>(n_shared) * dm->T; }
 
-struct FfnWs { int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; int32_t* sync; };
+struct FfnWs {
+  int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; int32_t* sync;
+  float* partial; size_t partial_bytes;  // split-K parts of FC1/FC2 tiles (none when no launch can split)
+};
+int gemm_regime(const moe_dims_t* dm);
 size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   Carver c(ws);
   FfnWs r{};
@@ -117,6 +121,8 @@ size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
   r.h = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->f);
   r.sync = c.take<int32_t>(sizeof(int32_t) * fused_sync_words(r.max_mb));  // fused FFN's readiness counters
+  r.partial_bytes = splitk_partial_bytes(dm->dtype, gemm_regime(dm), r.max_mb, dm->d, dm->f);
+  r.partial = r.partial_bytes ? c.take<float>(r.partial_bytes) : nullptr;
   if (out) *out = r;
   return c.off;
 }
@@ -254,12 +260,13 @@ int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32
   {
     StageScope sc(MOE_STAGE_FC1, s);
     if (int st = hip_status(launch_fc1(dm->dtype, regime, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
-                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, s))) return st;
+                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, fw.partial, fw.partial_bytes, s)))
+      return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
   return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
                                expected_mblocks(dm, regime_block_rows(regime), fw.max_mb, sh.n), dm->d, dm->f, sh,
-                               s));
+                               fw.partial, fw.partial_bytes, s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,

@@ -77,6 +77,10 @@ CONFIGS: Dict[str, LayerConfig] = {c.name: c for c in [
                 "tiny layer, fp32, balanced routing"),
     LayerConfig("mixtral_decode", 256, 6144, 16384, 8, 2, "bf16", 0.0,
                 "Mixtral-8x22B-shaped layer, decode batch, balanced routing"),
+    LayerConfig("mixtral_decode_t1", 1, 6144, 16384, 8, 2, "bf16", 0.0,
+                "Mixtral-8x22B-shaped layer, one token (latency of a single decode step)"),
+    LayerConfig("mixtral_decode_t16", 16, 6144, 16384, 8, 2, "bf16", 0.0,
+                "Mixtral-8x22B-shaped layer, 16-token decode batch"),
     LayerConfig("mixtral_prefill_skew", 8192, 6144, 16384, 8, 2, "bf16", 1.5,
                 "Mixtral-8x22B-shaped layer, prefill batch, Zipf-like skew 1.5"),
     LayerConfig("mixtral_prefill_bal", 8192, 6144, 16384, 8, 2, "bf16", 0.0,

@@ -1,8 +1,8 @@
 """The fused FFN launch (moe_layer_forward_fused): FC1, FC2 and the combine in one
 persistent kernel with device-side readiness counters.
 
-Its tiles do exactly the arithmetic of moe_layer_forward's separate launches,
-so the bar is bitwise equality with that path (itself held to the oracle in
+Its tiles do exactly the arithmetic of moe_layer_forward's separate launches
+when those do not split K (MOE_SPLIT_K=0), so the bar is bitwise equality with that path (itself held to the oracle in
 test_gpu_parity.py), checked twice in a row on the same buffers (a missed
 wait or a stale read would show up as a difference), plus the oracle bar on
 small shapes directly.
@@ -20,6 +20,13 @@ from conftest import to_numpy
 from parity import OUT_TOL, gpu_float, rel_err
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _whole_k(monkeypatch):
+    # the fused kernel never splits K; the separate launches it is compared with
+    # bit for bit must not either
+    monkeypatch.setenv("MOE_SPLIT_K", "0")
 
 
 def _say(msg):

@@ -194,6 +194,35 @@ def test_each_gemm_tile_regime(monkeypatch, regime, shape):
     _full_oracle_check(cfg, inp)
 
 
+SPLIT_SHAPES = [
+    # T, d, f, E, k, bias scale: launches with fewer tiles than CUs, K cut into parts
+    (1, 2048, 1024, 8, 2, 0.0),     # one token: FC1 in 4 parts, FC2 in 2
+    (2, 1088, 2112, 8, 2, 0.0),     # column tails in both GEMMs; 17 and 33 K steps in uneven parts
+    (3, 512, 2240, 4, 2, 0.0),      # FC2 alone split: 35 K steps in 4 parts
+    (600, 2048, 1024, 2, 1, 1.0),   # few experts with many rows: parts of up to 256 rows
+    (100, 1024, 1536, 1, 1, 0.0),   # one expert: FC2 in 3 parts
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
+def test_split_k_launches(monkeypatch, shape):
+    """Few-tile launches split along K: oracle bar, bitwise repeatable, and within the
+    oracle bar of the same layer run unsplit (MOE_SPLIT_K=0)."""
+    T, d, f, E, k, s = shape
+    _say(f"case split-K {shape}")
+    cfg = moe_inputs.LayerConfig("splitk", T, d, f, E, k, "bf16", s)
+    inp = moe_inputs.make_layer_inputs(cfg, 13, "cuda")
+    out, _, ref = _full_oracle_check(cfg, inp)
+    again, _ = _run_layer(cfg, inp)
+    assert torch.equal(out, again)
+    monkeypatch.setenv("MOE_SPLIT_K", "0")
+    whole, _ = _run_layer(cfg, inp)
+    err = rel_err(gpu_float(whole), ref["out"])
+    diff = rel_err(gpu_float(out), gpu_float(whole))
+    _say(f"  unsplit rel_err={err:.3e}; split vs unsplit {diff:.3e}")
+    assert err <= OUT_TOL and diff <= OUT_TOL
+
+
 # Rows per expert chosen so that, in 256-row blocks, the upper and lower 128-row
 # halves of a block hold every number (0..4) of non-empty 32-row sub-blocks.
 PARTIAL_COUNTS = [1, 40, 70, 100, 128, 129, 170, 200, 255, 256, 300]
@@ -270,7 +299,7 @@ def test_shared_experts_layer(monkeypatch, shape, path):
     assert err <= OUT_TOL
 
 
-FULL = ["mixtral_decode", "dbrx_bal", "dbrx_zipf", "mixtral_prefill_skew", "mixtral_prefill_bal",
+FULL = ["mixtral_decode", "mixtral_decode_t1", "mixtral_decode_t16", "dbrx_bal", "dbrx_zipf", "mixtral_prefill_skew", "mixtral_prefill_bal",
         "deepseek_skew", "deepseek_bal"]
 
 
