@@ -464,9 +464,11 @@ def run_one(args, seed: int) -> dict:
     big_tile = cfg.dtype == "bf16" and os.environ.get("MOE_GEMM_REGIME", "1") != "0"
     if args.fused:
         roof["kernel"] = "ffn_fused_kernel (FC1 + SiLU*mul, FC2, combine; one launch)"
+    elif big_tile:
+        rows = moe.ffn_block_rows(moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype))
+        roof["kernel"] = f"gemm_dl_kernel<gated, {rows}x256> (FC1 + SiLU*mul)"
     else:
-        roof["kernel"] = ("gemm_dl_kernel<gated, 256x256> (FC1 + SiLU*mul)" if big_tile
-                          else "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)")
+        roof["kernel"] = "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)"
     roof["kernel_ms"] = round(fc1_ms, 4)
 
     ceilings = None

@@ -86,6 +86,14 @@ const char* moe_status_string(int status);
  * most). 0 if dims is invalid. The workspace must be 256-byte aligned. */
 size_t moe_workspace_bytes(const moe_dims_t* dims);
 
+/* Rows per m-block (the tile-aligned token blocks of at most beta rows that
+ * the grouped FFN's tiles cover; MegaFlux section 3.1) that moe_grouped_ffn and
+ * moe_layer_forward use for `dims`: 128 when the batch has few rows per active
+ * expert (96 or fewer on average, decode batches) or the data is fp32, else 256.
+ * The MOE_GEMM_REGIME environment switch overrides the choice. 0 if dims is
+ * invalid. Host-only query: no device work. */
+int moe_ffn_block_rows(const moe_dims_t* dims);
+
 /* Gate GEMM + bias, top-k selection and renormalised weights
  * (MegaScale-Infer, Fused Kernels, steps 1 and 3).
  *   x      [T][d]   tokens

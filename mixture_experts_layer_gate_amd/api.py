@@ -27,7 +27,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
-           "moe_layer_backward", "moe_layer_forward_fused"]
+           "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows"]
 
 
 class MoeError(RuntimeError):
@@ -78,6 +78,8 @@ def load_library():
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_workspace_bytes.restype = _S
     lib.moe_workspace_bytes.argtypes = [_DP]
+    lib.moe_ffn_block_rows.restype = ctypes.c_int
+    lib.moe_ffn_block_rows.argtypes = [_DP]
     lib.moe_route.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_permute.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_grouped_ffn.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
@@ -131,6 +133,11 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape):
 
 def workspace_bytes(dims: Dims) -> int:
     return int(load_library().moe_workspace_bytes(ctypes.byref(dims.c())))
+
+
+def ffn_block_rows(dims: Dims) -> int:
+    """Rows per m-block of the grouped FFN for these dims (128 or 256; 0 if invalid)."""
+    return int(load_library().moe_ffn_block_rows(ctypes.byref(dims.c())))
 
 
 def make_workspace(dims: Dims, device="cuda") -> torch.Tensor:

@@ -600,7 +600,9 @@ struct DlGemm {
             real ? ars : nul, (__attribute__((address_space(3))) void*)(sa + (wv * AI + i) * 1024), 16, aoff[i],
             koff, 0, 0);
     };
-    auto issue_b = [&](int slot, int kt) {
+    // aux_c: cache policy of the weight loads (0, or 2 = non-temporal)
+    auto issue_b = [&](int slot, int kt, auto aux_c) {
+      constexpr int AUX = decltype(aux_c)::value;
       const bool real = kt < nk;
       char* sb = lds + NBA * A_ST + slot * B_ST;
       if constexpr (kBKN) {
@@ -610,7 +612,7 @@ struct DlGemm {
         for (int i = 0; i < BI; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? brs0 : nul,
                                                    (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024),
-                                                   16, boff[i], koff, 0, 0);
+                                                   16, boff[i], koff, 0, AUX);
         return;
       }
       const uint32_t koff = real ? static_cast<uint32_t>(kt0 + kt) * RB : 0u;
@@ -619,7 +621,7 @@ struct DlGemm {
         const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             real ? (second ? brs1 : brs0) : nul, (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024),
-            16, boff[i], koff, 0, 0);
+            16, boff[i], koff, 0, AUX);
       }
     };
     // bf16 MFMA 16x16x32 (under a sustained power limit it keeps a higher
@@ -683,7 +685,7 @@ struct DlGemm {
       }
     };
 
-    auto kloop = [&](auto ma_c) {
+    auto kloop = [&](auto ma_c, auto aux_c) {
       constexpr int MA16 = 2 * decltype(ma_c)::value < MI16 ? 2 * decltype(ma_c)::value : MI16;
       // Step j uses A buffer j & 1 and B buffer j % NBB; both are free once
       // every wave passed step j's barrier (its reads are done by then), so
@@ -693,18 +695,18 @@ struct DlGemm {
       // B(NBB-2), A1, B(NBB-1) (two buffers: B0 A0 A1 B1). At step kt's
       // barrier only the newest B batch, B(kt+NBB-1), may then be in flight.
       if constexpr (NBB == 2) {
-        issue_b(0, 0);
+        issue_b(0, 0, aux_c);
         issue_a(0, 0);
         issue_a(1, 1);
-        issue_b(1, 1);
+        issue_b(1, 1, aux_c);
       } else {
-        issue_b(0, 0);
+        issue_b(0, 0, aux_c);
 #pragma unroll
-        for (int j = 1; j <= NBB - 3; ++j) issue_b(j, j);
+        for (int j = 1; j <= NBB - 3; ++j) issue_b(j, j, aux_c);
         issue_a(0, 0);
-        issue_b(NBB - 2, NBB - 2);
+        issue_b(NBB - 2, NBB - 2, aux_c);
         issue_a(1, 1);
-        issue_b(NBB - 1, NBB - 1);
+        issue_b(NBB - 1, NBB - 1, aux_c);
       }
       wait_vmcnt<(NBB == 2 ? AI + BI : AI + 2 * BI)>();  // A0 and B0 landed
       lds_barrier();
@@ -729,7 +731,7 @@ struct DlGemm {
         wait_lds_reads();  // and its reads of step kt's buffers are done: they may be refilled after the barrier
         lds_barrier();
         issue_a(cur, kt + 2);
-        issue_b(bsl, kt + NBB);
+        issue_b(bsl, kt + NBB, aux_c);
         if constexpr (MA16 > 0) {
           // sub-step 1: its MFMAs with the reads of step kt+1's sub-step 0
           // (on the last step: zeros, unused)
@@ -744,16 +746,32 @@ struct DlGemm {
     };
 
     const int ma = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * TM + 31) / 32)));
-    if (ma >= MI) {
-      kloop(std::integral_constant<int, MI>{});
-    } else {
-      static_assert(MI <= 4, "active-block dispatch covers up to four 32-row blocks per wave");
-      switch (ma) {
-        case 0: kloop(std::integral_constant<int, 0>{}); break;
-        case 1: kloop(std::integral_constant<int, (MI > 1 ? 1 : MI)>{}); break;
-        case 2: kloop(std::integral_constant<int, (MI > 2 ? 2 : MI)>{}); break;
-        default: kloop(std::integral_constant<int, (MI > 3 ? 3 : MI)>{}); break;
+    auto run = [&](auto aux_c) {
+      if (ma >= MI) {
+        kloop(std::integral_constant<int, MI>{}, aux_c);
+      } else {
+        static_assert(MI <= 4, "active-block dispatch covers up to four 32-row blocks per wave");
+        switch (ma) {
+          case 0: kloop(std::integral_constant<int, 0>{}, aux_c); break;
+          case 1: kloop(std::integral_constant<int, (MI > 1 ? 1 : MI)>{}, aux_c); break;
+          case 2: kloop(std::integral_constant<int, (MI > 2 ? 2 : MI)>{}, aux_c); break;
+          default: kloop(std::integral_constant<int, (MI > 3 ? 3 : MI)>{}, aux_c); break;
+        }
       }
+    };
+    // Forward weight tiles of an m-block that is alone in its plan group (an
+    // expert with at most one block of rows, as in decode batches) are read by
+    // this tile only: they are streamed with the non-temporal cache policy,
+    // which sustains a higher HBM read rate. Weights that the neighbouring
+    // m-blocks of a group read again keep the default policy, under which the
+    // other reads hit in L2.
+    if constexpr (kMode == kModeFc1 || kMode == kModeFc2) {
+      if ((g.mblocks[mb].w & 15) == 1)
+        run(std::integral_constant<int, 2>{});
+      else
+        run(std::integral_constant<int, 0>{});
+    } else {
+      run(std::integral_constant<int, 0>{});
     }
 
     if (mode_f32_out(kMode) || sp > 1) {
@@ -1061,17 +1079,20 @@ static int persistent_grid(int64_t max_tiles) {
 }
 
 int choose_gemm_regime(int64_t T, int k, int E) {
-  (void)T, (void)k, (void)E;
   if (const char* env = getenv("MOE_GEMM_REGIME")) {
     const int r = atoi(env);
-    if (r >= 0 && r <= 2) return r;
+    if (r >= 0 && r <= 3) return r;
   }
-  // 256-row m-blocks for every batch size: weights are streamed once per
-  // m-block, so few large blocks suit weight-bound (decode) batches too
+  // Few rows per expert (decode batches: the expert's weights are read once,
+  // by one m-block): 128-row tiles, whose smaller A stages leave LDS for one
+  // more weight step in flight. 96 rows on average keeps the busiest experts
+  // of balanced routing within one 128-row block. Otherwise 256-row tiles.
+  const int64_t n = T * k, active = n < E ? n : E;
+  if (active > 0 && (n + active - 1) / active <= 96) return 3;
   return 1;
 }
 
-int regime_block_rows(int regime) { return regime >= 1 ? 256 : 128; }
+int regime_block_rows(int regime) { return regime == 1 || regime == 2 ? 256 : 128; }
 
 // Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take up
 // to the CU's 160 KB), persistent over the tile list.
@@ -1116,6 +1137,8 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
                       const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f,
              T * k, sh.w1, sh.w3, sh.n > 0 ? sh.E_routed : INT32_MAX};
+  if (dtype == 1 && regime == 3)
+    return launch_fwd<kModeFc1, 128, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, s);
   if (dtype == 1 && regime >= 1)
     return launch_fwd<kModeFc1, 256, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
@@ -1143,6 +1166,9 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
       const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
       narrow = t192 < t256;
     }
+    if (regime == 3)
+      return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4>(a, max_mb, d, partial, partial_bytes, s)
+                    : launch_fwd<kModeFc2, 128, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, s);
     return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2>(a, max_mb, d, partial, partial_bytes, s)
                   : launch_fwd<kModeFc2, 256, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, s);
   }

@@ -6,7 +6,7 @@
 namespace moe {
 
 // Smallest rows per m-block of the grouped GEMM (tile-aligned token blocks);
-// the large-tile regime uses 256.
+// the large-tile regimes use 256.
 constexpr int kBlockRows = 128;
 // Largest tile group (m-blocks of one expert walked together by the GEMM).
 constexpr int kTileGroup = 8;
@@ -46,8 +46,9 @@ hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int
 // staged, two workgroups per CU (the fp32 path); 1: 256-row tiles fed by
 // buffer loads into LDS, 8 waves, one workgroup per CU (bf16), FC1 256 weight
 // rows wide, FC2 256 or, when few m-blocks would leave CUs idle, 192
-// columns; 2: as 1 with FC2 always 256 columns. MOE_GEMM_REGIME overrides
-// the choice.
+// columns; 2: as 1 with FC2 always 256 columns; 3: as 1 with 128-row tiles
+// and m-blocks (few rows per expert: one more weight step in flight).
+// MOE_GEMM_REGIME overrides the choice.
 // Shared (always-active) experts appended to the routed ones: expert ids
 // E_routed .. E_routed + n - 1, each with T rows after the T*k routed rows.
 struct SharedExperts {

@@ -349,7 +349,7 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
     {
       StageScope sc(MOE_STAGE_DISPATCH, s);
       if (int st = hip_status(launch_dispatch_fused(topk_idx, n, dm->E, counts, offsets, perm, inv_perm,
-                                                    regime_block_rows(gemm_regime(dm)), fw.max_mb,
+                                                    fused ? 256 : regime_block_rows(gemm_regime(dm)), fw.max_mb,
                                                     plan_inline ? fw.mblocks : nullptr,
                                                     plan_inline ? fw.n_mblocks : nullptr, s)))
         return st;
@@ -400,6 +400,11 @@ const char* moe_status_string(int status) {
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     default: return "unknown status";
   }
+}
+
+int moe_ffn_block_rows(const moe_dims_t* dm) {
+  if (check_dims(dm) != MOE_OK) return 0;
+  return regime_block_rows(gemm_regime(dm));
 }
 
 size_t moe_workspace_bytes(const moe_dims_t* dm) {

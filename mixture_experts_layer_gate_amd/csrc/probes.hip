@@ -2,8 +2,9 @@
 // against measured ceilings next to the datasheet peaks.
 //
 // * hbm_read_probe: one workgroup of 8 waves per CU streams a contiguous slice
-//   of a device buffer into LDS with 16-byte buffer loads (the same load form
-//   the grouped GEMM uses), 32 KiB per step, three steps in flight.
+//   of a device buffer into LDS with 16-byte non-temporal buffer loads (the
+//   load form of the grouped GEMM's weight stream), 32 KiB per step, three
+//   steps in flight.
 // * mfma_probe: 8 waves per CU each run eight independent chains of bf16
 //   16x16x32 MFMAs (the GEMM's form) on register operands; no memory traffic.
 //   Each wave does 4 x 8 x 16384 = 524288 FLOP per iteration.
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(kProbeThreads, 1) void hbm_read_probe(const char* s
     for (int i = 0; i < 4; ++i) {  // 4 x 1 KiB per wave, 32 KiB per workgroup; past the slice: zeros, no request
       const int inst = wv * 4 + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16,
-                                               s * kProbeStep + inst * 1024 + lane * 16, 0, 0, 0);
+                                               s * kProbeStep + inst * 1024 + lane * 16, 0, 0, 2);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70 | 12);  // vmcnt(12): three steps of 4 loads in flight
   }

@@ -51,6 +51,28 @@ def test_workspace_bytes_rejects_bad_dims(bad):
     assert moe.load_library().moe_workspace_bytes(ctypes.byref(_dims(**bad))) == 0
 
 
+def test_ffn_block_rows_choice(monkeypatch):
+    """128-row m-blocks for batches with at most 96 rows per active expert (and fp32),
+    256 otherwise; the environment switch overrides; invalid dims give 0."""
+    monkeypatch.delenv("MOE_GEMM_REGIME", raising=False)
+    lib = moe.load_library()
+
+    def rows(**kw):
+        return lib.moe_ffn_block_rows(ctypes.byref(_dims(**kw)))
+    assert rows(T=256, d=6144, f=16384, E=8, k=2) == 128      # decode: 64 rows per expert
+    assert rows(T=1, d=6144, f=16384, E=8, k=2) == 128        # one token: 1 row per active expert
+    assert rows(T=384, E=8, k=2) == 128                       # exactly 96 per expert
+    assert rows(T=385, E=8, k=2) == 256                       # just above
+    assert rows(T=8192, d=6144, f=16384, E=8, k=2) == 256     # prefill
+    assert rows(T=4096, d=7168, f=2048, E=256, k=8) == 256    # 128 per expert
+    assert rows(T=8192, dtype=0) == 128                       # fp32: the small-tile kernel
+    assert rows(k=0) == 0
+    monkeypatch.setenv("MOE_GEMM_REGIME", "1")
+    assert rows(T=1, d=6144, f=16384, E=8, k=2) == 256
+    monkeypatch.setenv("MOE_GEMM_REGIME", "3")
+    assert rows(T=8192) == 128
+
+
 def test_workspace_bytes_grows_with_shape():
     lib = moe.load_library()
     a = lib.moe_workspace_bytes(ctypes.byref(_dims()))

@@ -179,7 +179,7 @@ REGIME_SHAPES = [
 ]
 
 
-GEMM_REGIMES = [0, 1, 2]
+GEMM_REGIMES = [0, 1, 2, 3]
 
 
 @pytest.mark.parametrize("regime", GEMM_REGIMES)
@@ -204,12 +204,18 @@ SPLIT_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("regime", ["default", "1"])
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
-def test_split_k_launches(monkeypatch, shape):
+def test_split_k_launches(monkeypatch, shape, regime):
     """Few-tile launches split along K: oracle bar, bitwise repeatable, and within the
-    oracle bar of the same layer run unsplit (MOE_SPLIT_K=0)."""
+    oracle bar of the same layer run unsplit (MOE_SPLIT_K=0); with the tiles the batch
+    size picks and with 256-row tiles forced."""
     T, d, f, E, k, s = shape
-    _say(f"case split-K {shape}")
+    _say(f"case split-K {shape} regime {regime}")
+    if regime == "default":
+        monkeypatch.delenv("MOE_GEMM_REGIME", raising=False)
+    else:
+        monkeypatch.setenv("MOE_GEMM_REGIME", regime)
     cfg = moe_inputs.LayerConfig("splitk", T, d, f, E, k, "bf16", s)
     inp = moe_inputs.make_layer_inputs(cfg, 13, "cuda")
     out, _, ref = _full_oracle_check(cfg, inp)
