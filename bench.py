@@ -1,8 +1,12 @@
 """Throughput of the MoE-layer forward pass on one MI355X.
 
-One step = one moe_layer_forward call (gate GEMM + top-k, dispatch, tile plan,
-grouped FC1 + SiLU*mul, grouped FC2, combine) on one batch of synthetic
-inputs already resident in HBM. Prints one JSON line.
+One step = one layer call (gate GEMM + top-k, dispatch, tile plan, grouped
+FC1 + SiLU*mul, grouped FC2, combine) on one batch of synthetic inputs already
+resident in HBM. Prints one JSON line. By default the bf16 layers read expert
+weights that moe_pack_weights re-laid once, before the steps, in the order the
+grouped FFN streams them (moe_layer_forward_packed: the same arithmetic and
+bitwise the same output as moe_layer_forward); --weights stored times
+moe_layer_forward on the weights as stored.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceilings]
   python bench.py --backward [--workload NAME] ...   (the layer's backward instead)
@@ -45,6 +49,10 @@ def parse():
                    help="skip the measured HBM-read and MFMA ceilings (diagnostic, about a second)")
     p.add_argument("--fused", action="store_true",
                    help="time moe_layer_forward_fused (FC1, FC2 and combine in one persistent launch)")
+    p.add_argument("--weights", choices=["auto", "packed", "stored"], default="auto",
+                   help="packed: moe_layer_forward_packed on the expert weights re-laid once in stage order "
+                        "(moe_pack_weights, timed apart, not part of a step); stored: moe_layer_forward on the "
+                        "weights as stored; auto: packed for bf16 layers without shared experts, unless --fused")
     p.add_argument("--backward", action="store_true",
                    help="time the layer's backward (moe_layer_backward) instead of the forward")
     p.add_argument("--copy-probe", action="store_true",
@@ -138,7 +146,8 @@ def protocol(args):
         runs = []
         for _ in range(2):
             cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--seeds", "0,1,2",
-                   "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-ceilings"]
+                   "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-ceilings",
+                   "--weights", args.weights]
             out = subprocess.run(cmd, check=True, capture_output=True, text=True).stdout
             runs += [json.loads(l) for l in out.splitlines() if l.startswith("{")]
         ms = [r["ms_per_step"] for r in runs]
@@ -387,10 +396,22 @@ def run_one(args, seed: int) -> dict:
     stream = torch.cuda.current_stream()
 
     S = cfg.n_shared
+    use_packed = args.weights == "packed" or (
+        args.weights == "auto" and cfg.dtype == "bf16" and not S and not args.fused)
     if S:
-        if args.fused:
-            raise SystemExit("the fused FFN launch covers layers without shared experts")
+        if args.fused or use_packed:
+            raise SystemExit("the fused FFN launch and the packed weights cover layers without shared experts")
         ws = torch.empty(moe.workspace_bytes_shared(dims, S), dtype=torch.uint8, device=dev)
+    packed, pack_ms = None, None
+    if use_packed:
+        if args.fused:
+            raise SystemExit("the fused FFN launch reads the weights as stored")
+        pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pe0.record(stream)
+        packed = moe.pack_weights(dims, inp["w1"], inp["w3"], inp["w2"], stream=stream)
+        pe1.record(stream)
+        torch.cuda.synchronize()
+        pack_ms = pe0.elapsed_time(pe1)
 
     def step():
         if S:
@@ -398,7 +419,7 @@ def run_one(args, seed: int) -> dict:
                                      inp["sw1"], inp["sw3"], inp["sw2"], out=out, ws=ws, stream=stream)
         else:
             moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], out=out,
-                              ws=ws, stream=stream, fused=args.fused)
+                              ws=ws, stream=stream, fused=args.fused, packed=packed)
 
     for _ in range(args.warmup):
         step()
@@ -460,13 +481,14 @@ def run_one(args, seed: int) -> dict:
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None if args.fused else measured_traffic(cfg.name, "fc1")
+    roof["traffic"] = None if args.fused else measured_traffic(cfg.name, "fc1_packed" if use_packed else "fc1")
     big_tile = cfg.dtype == "bf16" and os.environ.get("MOE_GEMM_REGIME", "1") != "0"
     if args.fused:
         roof["kernel"] = "ffn_fused_kernel (FC1 + SiLU*mul, FC2, combine; one launch)"
     elif big_tile:
         rows = moe.ffn_block_rows(moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype))
-        roof["kernel"] = f"gemm_dl_kernel<gated, {rows}x256> (FC1 + SiLU*mul)"
+        roof["kernel"] = (f"gemm_dl_kernel<gated, {rows}x256{', stage-order weights' if use_packed else ''}> "
+                          "(FC1 + SiLU*mul)")
     else:
         roof["kernel"] = "grouped_gemm_kernel<gated, 128x128> (FC1 + SiLU*mul)"
     roof["kernel_ms"] = round(fc1_ms, 4)
@@ -498,7 +520,10 @@ def run_one(args, seed: int) -> dict:
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E, "k": cfg.k,
-                   "n_shared": S, "ffn": "fused" if args.fused else "separate launches", "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
+                   "n_shared": S, "ffn": "fused" if args.fused else "separate launches",
+                   "weights": (f"stage order (packed once in {pack_ms:.2f} ms, outside the steps)" if use_packed
+                               else "as stored [E][f][d], [E][d][f]"),
+                   "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "gbps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),

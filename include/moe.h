@@ -183,6 +183,32 @@ int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* w
                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                             int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* Expert weights re-laid in the order the grouped FFN streams them (no
+ * arithmetic: a permutation of each expert matrix's bf16 values). The expert
+ * FFN's FC1/FC2 tiles (MegaFlux, section 2.1) read a column block of weight
+ * rows one 64-wide K step at a time, 128 bytes from each of hundreds of rows;
+ * in this order every 64-row group of a matrix is K/64 contiguous 8 KiB
+ * blocks, one per K step, each already in the order the loads place it in
+ * LDS, which HBM streams faster. Meant for weights that are packed once and
+ * read by many calls (decode); the packing is not part of a layer call.
+ *   moe_pack_weights: w1p, w3p [E][f][d] and w2p [E][d][f] (device buffers the
+ *     caller owns, the sizes of w1, w3, w2, 16-byte aligned, not overlapping
+ *     the inputs) receive the stage-order copies of w1, w3, w2; asynchronous
+ *     on `stream`. bf16 only (MOE_ERR_UNSUPPORTED otherwise); d and f
+ *     multiples of 64 as for the layer.
+ *   moe_layer_forward_packed: moe_layer_forward reading the packed weights
+ *     in place of w1, w3, w2; same arguments, limits, workspace and outputs,
+ *     and bitwise the same result (the tiles load the same values into LDS).
+ * Element (e, n, k) of a packed tensor of row length K (d for w1p, w3p; f for
+ * w2p) sits at 16-byte unit (((e*N/64 + n/64) * K/64 + k/64) * 64 + n%64) * 8
+ * + ((k%64)/8 ^ ((n%64)/2)%8), element k%8 of the unit. */
+int moe_pack_weights(const moe_dims_t* dims, const void* w1, const void* w3, const void* w2, void* w1p,
+                     void* w3p, void* w2p, void* stream);
+int moe_layer_forward_packed(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+                             const void* w1p, const void* w3p, const void* w2p, void* out, float* logits,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- backward pass ----
  * Gradients of the layer for a scalar loss whose gradient with respect to
  * `out` is `dout`. The pages name the parts (MegaFlux, section 2.1: token

@@ -27,7 +27,8 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
-           "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows"]
+           "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_pack_weights",
+           "moe_layer_forward_packed"]
 
 
 class MoeError(RuntimeError):
@@ -86,6 +87,8 @@ def load_library():
     lib.moe_combine.argtypes = [_DP, _P, _P, _P, _P, _P]
     lib.moe_layer_forward.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_layer_forward_fused.argtypes = lib.moe_layer_forward.argtypes
+    lib.moe_pack_weights.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P]
+    lib.moe_layer_forward_packed.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_workspace_bytes_shared.restype = _S
     lib.moe_workspace_bytes_shared.argtypes = [_DP, ctypes.c_int]
     lib.moe_layer_forward_shared.argtypes = [_DP, ctypes.c_int] + [_P] * 18 + [_S, _P]
@@ -215,17 +218,36 @@ def combine(dims: Dims, y_sorted, inv_perm, topk_w, out=None, stream=None):
     return out
 
 
+def pack_weights(dims: Dims, w1, w3, w2, stream=None):
+    """Stage-order copies (w1p, w3p, w2p) of the expert weights for layer_forward(packed=...):
+    tensors of the same shapes and dtype whose values are permuted within each expert."""
+    lib = load_library()
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    w1p, w3p, w2p = torch.empty_like(w1), torch.empty_like(w3), torch.empty_like(w2)
+    _check("moe_pack_weights", lib.moe_pack_weights(ctypes.byref(dims.c()), _ptr(w1), _ptr(w3), _ptr(w2),
+                                                    _ptr(w1p), _ptr(w3p), _ptr(w2p), _stream(stream)))
+    return w1p, w3p, w2p
+
+
 def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False,
-                  fused=False):
+                  fused=False, packed=None):
     """The whole layer. With return_routing, also returns the routing arrays as a dict.
     fused=True runs FC1, FC2 and the combine as one persistent launch
-    (moe_layer_forward_fused; bitwise the same result)."""
+    (moe_layer_forward_fused; bitwise the same result). packed=(w13p, w2p) from
+    pack_weights reads the stage-order weights instead of w1, w3, w2 (which may
+    then be None; moe_layer_forward_packed, bitwise the same result)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", dims.dtype, (dims.T, dims.d))
     _need(wg, "wg", dims.dtype, (dims.E, dims.d))
     if bias is not None:
         _need(bias, "bias", torch.float32, (dims.E,))
+    if packed is not None:
+        if fused:
+            raise ValueError("the fused launch reads the weights as stored")
+        w1, w3, w2 = packed
     for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
                          ("w2", w2, (dims.E, dims.d, dims.f))):
         _need(w, name, dims.dtype, shp)
@@ -243,7 +265,8 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
              "inv_perm": torch.empty(n, dtype=torch.int32, device=dev)}
     ws, nws = _ws(dims, ws)
     g = r.get
-    fn = "moe_layer_forward_fused" if fused else "moe_layer_forward"
+    fn = "moe_layer_forward_packed" if packed is not None else (
+        "moe_layer_forward_fused" if fused else "moe_layer_forward")
     _check(fn, getattr(lib, fn)(
         ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
         _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")), _ptr(g("counts")), _ptr(g("offsets")),

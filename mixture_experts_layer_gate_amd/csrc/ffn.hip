@@ -398,7 +398,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 // epilogue. pre(mb) runs once the tile's m-block is known and before any of
 // its loads are issued; post(mb) after its results are stored and the tile
 // buffer is free again (both no-ops for the standalone kernel).
-template <int kMode, int BM, int BN, int WM, int WN>
+template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 struct DlGemm {
   static constexpr bool kGated = mode_gated(kMode);
   static constexpr bool kWgrad = kMode == kModeWgrad;
@@ -561,6 +561,13 @@ struct DlGemm {
                   chunk_off(((wv * BI + i) * PH) % CPR);
       }
     } else {
+      // Weights as stored, or (kPacked) in the stage order of pack_weights_kernel:
+      // the 64-row group g of an expert's matrix is K / 64 blocks of 8 KiB, block
+      // kt holding rows 64g.. x K elements 64kt.. already swizzled as the LDS
+      // stage expects, so the lane of stage row r and slot c reads 16 bytes at
+      // (g * K/64 + kt) * 8192 + (r % 64) * 128 + c * 16. The stage's column
+      // block starts on a multiple of 64 rows, so r % 64 is the row's place in
+      // its group and the swizzle matches.
       const int64_t ebytes = N * K * 2;
       brs0 = make_rsrc(expert_base(g, g.B0, g.S0, e, ebytes), static_cast<uint32_t>(ebytes));
       brs1 = kGated ? make_rsrc(expert_base(g, g.B1, g.S1, e, ebytes), static_cast<uint32_t>(ebytes)) : brs0;
@@ -572,8 +579,14 @@ struct DlGemm {
           n = static_cast<int64_t>(nb) * (BN / 2) + (r % (BN / 2));
         else
           n = static_cast<int64_t>(nb) * BN + r;
-        if (n >= N) n = N - 1;  // column tail: computed on a valid row, never stored
-        boff[i] = static_cast<uint32_t>(n * K * 2) + chunk_off(((wv * BI + i) * PH) % CPR);
+        if constexpr (kPacked) {
+          int64_t grp = n / 64;
+          if (grp >= N / 64) grp = N / 64 - 1;  // column tail: a valid group, never stored
+          boff[i] = static_cast<uint32_t>(grp * (K / 64) * 8192 + (r % 64) * 128 + (lane % CPR) * 16);
+        } else {
+          if (n >= N) n = N - 1;  // column tail: computed on a valid row, never stored
+          boff[i] = static_cast<uint32_t>(n * K * 2) + chunk_off(((wv * BI + i) * PH) % CPR);
+        }
       }
     }
 
@@ -590,6 +603,7 @@ struct DlGemm {
     // again, so every step issues the same number of loads and the issue can
     // sit in the same basic block as the MFMAs.
     const __amdgpu_buffer_rsrc_t nul = make_rsrc(g.B0, 0u);
+    constexpr uint32_t kstride = kPacked ? 8192u : static_cast<uint32_t>(RB);  // B bytes per K step
     auto issue_a = [&](int slot, int kt) {
       const bool real = kt < nk;
       char* sa = lds + slot * A_ST;
@@ -615,7 +629,8 @@ struct DlGemm {
                                                    16, boff[i], koff, 0, AUX);
         return;
       }
-      const uint32_t koff = real ? static_cast<uint32_t>(kt0 + kt) * RB : 0u;
+      // (steps past the end read through the empty descriptor: the offset is moot)
+      const uint32_t koff = static_cast<uint32_t>(kt0 + kt) * kstride;
 #pragma unroll
       for (int i = 0; i < BI; ++i) {
         const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
@@ -885,12 +900,12 @@ struct DlGemm {
   }
 };
 
-template <int kMode, int BM, int BN, int WM, int WN>
+template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   // device-only body: the buffer-resource builtins have no host form, and the
   // host pass only needs the kernel's launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  using D = DlGemm<kMode, BM, BN, WM, WN>;
+  using D = DlGemm<kMode, BM, BN, WM, WN, kPacked>;
   __shared__ __attribute__((aligned(1024))) char lds[D::LDS_BYTES];
   const int64_t ntiles = D::tiles(g);
   // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
@@ -1052,6 +1067,40 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   }
 }
 
+// Stage order of one expert-weight tensor W [E][N][K] (bf16, N and K multiples
+// of 64): the same E x N x K values, as 64-row groups of K/64 blocks of 8 KiB.
+// 16-byte unit u = (((e * N/64 + g) * K/64 + kt) * 64 + rr) * 8 + s holds
+// elements kt*64 + 8 * (s ^ ((rr / 2) % 8)) .. +7 of row 64g + rr of expert e:
+// exactly what the GEMM's loads place in slot s of a stage row whose index is
+// rr modulo 64 (the 8-slot XOR swizzle of 128-byte rows), so each K step of a
+// column block reads whole 8 KiB blocks.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* w, u32x4_t* out, int64_t units, int64_t K) {
+  const int64_t nk = K / 64;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < units;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int s = static_cast<int>(u % 8);
+    const int rr = static_cast<int>((u / 8) % 64);
+    const int64_t kt = (u / 512) % nk;
+    const int64_t row = (u / (512 * nk)) * 64 + rr;  // row of the [E*N][K] matrix
+    out[u] = *reinterpret_cast<const u32x4_t*>(w + row * K + kt * 64 + 8 * (s ^ ((rr / 2) % 8)));
+  }
+}
+
+hipError_t launch_pack_weights(const void* w1, const void* w3, const void* w2, void* w1p, void* w3p, void* w2p,
+                               int64_t E, int64_t d, int64_t f, hipStream_t s) {
+  const int64_t units = E * d * f / 8;  // 16-byte units of one tensor
+  const int grid = static_cast<int>(std::min<int64_t>((units + 255) / 256, 65536));
+  const void* src[3] = {w1, w3, w2};
+  void* dst[3] = {w1p, w3p, w2p};
+  const int64_t kdim[3] = {d, d, f};
+  for (int t = 0; t < 3; ++t) {
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(src[t]),
+                       static_cast<u32x4_t*>(dst[t]), units, kdim[t]);
+    if (hipError_t err = hipGetLastError()) return err;
+  }
+  return hipSuccess;
+}
+
 // Largest number of K parts per tile: each part keeps at least 8 K steps of
 // 64; MOE_SPLIT_K=0 in the environment turns splitting off (=n caps it at n).
 static int split_k_parts(int64_t K) {
@@ -1096,12 +1145,12 @@ int regime_block_rows(int regime) { return regime == 1 || regime == 2 ? 256 : 12
 
 // Large-tile launch: one workgroup of 8 waves per CU (the LDS buffers take up
 // to the CU's 160 KB), persistent over the tile list.
-template <int kMode, int BM, int BN, int WM, int WN>
+template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, hipStream_t s) {
   const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
   const int64_t nb = (ncols + cols - 1) / cols;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, device_cu_count())));
-  hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
+  hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN, kPacked>), dim3(grid), dim3(64 * WM * WN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1109,7 +1158,7 @@ static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, h
 // tiles than CUs (few rows and few experts: a decode step of a handful of
 // tokens) and the partial buffer is there; the tiles' parts then run on all
 // CUs and a second kernel sums them.
-template <int kMode, int BM, int BN, int WM, int WN>
+template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* partial, size_t partial_bytes,
                              hipStream_t s) {
   const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
@@ -1118,12 +1167,12 @@ static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* p
   const int parts = split_k_parts(a.K);
   const int64_t cap = static_cast<int64_t>(partial_bytes / (sizeof(float) * BM * BN));
   if (partial == nullptr || parts < 2 || max_mb * nb >= cus || max_mb * nb * 2 > cap)
-    return launch_big<kMode, BM, BN, WM, WN>(a, max_mb, ncols, s);
+    return launch_big<kMode, BM, BN, WM, WN, kPacked>(a, max_mb, ncols, s);
   a.partial = partial;
   a.splits = parts;
   a.split_target = static_cast<int>(cus);
   a.partial_cap = static_cast<int>(cap);
-  hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
+  hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN, kPacked>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
                      a);
   if (hipError_t err = hipGetLastError()) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<mode_gated(kMode), BM, BN, WN>), dim3(static_cast<int>(max_mb * nb)),
@@ -1134,9 +1183,14 @@ static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* p
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s) {
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f,
              T * k, sh.w1, sh.w3, sh.n > 0 ? sh.E_routed : INT32_MAX};
+  // packed: w1, w3 in stage order (pack_weights_kernel), read by the large-tile
+  // kernels only
+  if (dtype == 1 && packed)
+    return regime == 3 ? launch_fwd<kModeFc1, 128, 256, 2, 4, true>(a, max_mb, f, partial, partial_bytes, s)
+                       : launch_fwd<kModeFc1, 256, 256, 2, 4, true>(a, max_mb, f, partial, partial_bytes, s);
   if (dtype == 1 && regime == 3)
     return launch_fwd<kModeFc1, 128, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, s);
   if (dtype == 1 && regime >= 1)
@@ -1151,7 +1205,7 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
 
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s) {
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d,
              0, sh.w2, nullptr, sh.n > 0 ? sh.E_routed : INT32_MAX};
   if (dtype == 1 && regime >= 1) {
@@ -1165,6 +1219,13 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
       const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
       const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
       narrow = t192 < t256;
+    }
+    if (packed) {  // W2 in stage order (pack_weights_kernel)
+      if (regime == 3)
+        return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s)
+                      : launch_fwd<kModeFc2, 128, 256, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s);
+      return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2, true>(a, max_mb, d, partial, partial_bytes, s)
+                    : launch_fwd<kModeFc2, 256, 256, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s);
     }
     if (regime == 3)
       return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4>(a, max_mb, d, partial, partial_bytes, s)

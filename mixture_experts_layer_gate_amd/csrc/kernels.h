@@ -64,10 +64,14 @@ int regime_block_rows(int regime);
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s);
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s);
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, hipStream_t s);
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s);
+// Forward weights in stage order (packed = true above): each of w1, w3, w2
+// re-laid within its own E x N x K footprint (bf16, N, K multiples of 64).
+hipError_t launch_pack_weights(const void* w1, const void* w3, const void* w2, void* w1p, void* w3p, void* w2p,
+                               int64_t E, int64_t d, int64_t f, hipStream_t s);
 // bytes of the split-K partial buffer a forward FFN of this shape can use (0:
 // its launches never split)
 size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, int64_t f);

@@ -248,10 +248,17 @@ int64_t expected_mblocks(const moe_dims_t* dm, int64_t br, int64_t max_mb, int n
   return est_mb < max_mb ? est_mb : max_mb;
 }
 
+// Weights in stage order are read by the large-tile kernels only
+int layer_regime(const moe_dims_t* dm, bool packed) {
+  const int r = gemm_regime(dm);
+  return packed && r == 0 ? 1 : r;
+}
+
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
-           const FfnWs& fw, hipStream_t s, bool planned = false, const SharedExperts& sh = SharedExperts{}) {
-  const int regime = gemm_regime(dm);
+           const FfnWs& fw, hipStream_t s, bool planned = false, const SharedExperts& sh = SharedExperts{},
+           bool packed = false) {
+  const int regime = layer_regime(dm, packed);
   if (!planned) {
     StageScope sc(MOE_STAGE_PLAN, s);
     if (int st = hip_status(launch_plan(counts, offsets, dm->E, dm->T * dm->k, fw.max_mb, regime_block_rows(regime),
@@ -260,13 +267,14 @@ int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32
   {
     StageScope sc(MOE_STAGE_FC1, s);
     if (int st = hip_status(launch_fc1(dm->dtype, regime, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
-                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, fw.partial, fw.partial_bytes, s)))
+                                       fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, fw.partial, fw.partial_bytes, packed,
+                                       s)))
       return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
   return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
                                expected_mblocks(dm, regime_block_rows(regime), fw.max_mb, sh.n), dm->d, dm->f, sh,
-                               fw.partial, fw.partial_bytes, s));
+                               fw.partial, fw.partial_bytes, packed, s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
@@ -318,7 +326,7 @@ int do_ffn_fused(const moe_dims_t* dm, const void* x, const int32_t* perm, const
 int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, const void* wg, const float* bias,
               const void* w1, const void* w3, const void* w2, void* out, float* logits, int32_t* topk_idx,
               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
-              size_t ws_bytes, void* stream, bool fused = false) {
+              size_t ws_bytes, void* stream, bool fused = false, bool packed = false) {
   if (int st = check_dims(dm)) return st;
   if (dm->T == 0) return MOE_OK;
   if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(out) ||
@@ -349,7 +357,7 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
     {
       StageScope sc(MOE_STAGE_DISPATCH, s);
       if (int st = hip_status(launch_dispatch_fused(topk_idx, n, dm->E, counts, offsets, perm, inv_perm,
-                                                    fused ? 256 : regime_block_rows(gemm_regime(dm)), fw.max_mb,
+                                                    fused ? 256 : regime_block_rows(layer_regime(dm, packed)), fw.max_mb,
                                                     plan_inline ? fw.mblocks : nullptr,
                                                     plan_inline ? fw.n_mblocks : nullptr, s)))
         return st;
@@ -363,7 +371,7 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
       }
       return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s);
     }
-    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, plan_inline, sh)) return st;
+    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, plan_inline, sh, packed)) return st;
   } else {
     PermuteWs pw{};
     permute_ws(dm, lw.sub, &pw);
@@ -377,7 +385,7 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
       }
       return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s);
     }
-    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, false, sh)) return st;
+    if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, false, sh, packed)) return st;
   }
   return do_combine(dm, lw.y, inv_perm, topk_w, out, s, sh.n);
 }
@@ -479,6 +487,26 @@ int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const
                       int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
                    perm, inv_perm, ws, ws_bytes, stream);
+}
+
+int moe_pack_weights(const moe_dims_t* dm, const void* w1, const void* w3, const void* w2, void* w1p, void* w3p,
+                     void* w2p, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (int st = ffn_shape_ok(dm)) return st;
+  if (!ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(w1p) || !ok16(w3p) || !ok16(w2p)) return MOE_ERR_INVALID;
+  return hip_status(
+      launch_pack_weights(w1, w3, w2, w1p, w3p, w2p, dm->E, dm->d, dm->f, static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_forward_packed(const moe_dims_t* dm, const void* x, const void* wg, const float* bias, const void* w1p,
+                             const void* w3p, const void* w2p, void* out, float* logits, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  return run_layer(dm, SharedExperts{}, x, wg, bias, w1p, w3p, w2p, out, logits, topk_idx, topk_w, counts, offsets,
+                   perm, inv_perm, ws, ws_bytes, stream, false, true);
 }
 
 int moe_layer_forward_fused(const moe_dims_t* dm, const void* x, const void* wg, const float* bias,

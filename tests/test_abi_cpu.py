@@ -121,6 +121,22 @@ def test_layer_validation():
 
 
 @needs_no_gpu
+def test_packed_validation():
+    lib = moe.load_library()
+    dm = _dims()
+    assert lib.moe_pack_weights(ctypes.byref(_dims(dtype=0)), A, A, A, A, A, A, None) == 2
+    assert lib.moe_pack_weights(ctypes.byref(_dims(f=100)), A, A, A, A, A, A, None) == 2
+    assert lib.moe_pack_weights(ctypes.byref(dm), A, A, A, None, A, A, None) == 1
+    assert lib.moe_pack_weights(ctypes.byref(dm), A, A + 8, A, A, A, A, None) == 1
+    fwd = lambda dims=dm, w1p=A, wsb=1 << 40: lib.moe_layer_forward_packed(  # noqa: E731
+        ctypes.byref(dims), A, A, None, w1p, A, A, A, None, None, None, None, None, None, None, A, wsb, None)
+    assert fwd(dims=_dims(dtype=0)) == 2
+    assert fwd(w1p=None) == 1
+    assert fwd(wsb=1024) == 3
+    assert fwd(dims=_dims(T=0)) == 0
+
+
+@needs_no_gpu
 def test_permute_ffn_combine_validation():
     lib = moe.load_library()
     dm = _dims()
