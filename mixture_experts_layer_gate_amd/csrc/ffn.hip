@@ -57,24 +57,32 @@ struct GemmArgs {
   // and first column; fp32 forms: add to C instead of storing
   int64_t a_pitch, a_col0;
   int accumulate;
-  // split K, for launches with fewer tiles than CUs: each tile's K steps are
-  // cut into parts, each part's fp32 accumulators go to `partial`
-  // ([virtual tile][BM][BN]), and splitk_reduce_kernel sums them in part order.
-  // At most `splits` parts, at most split_target virtual tiles in all, at
-  // most partial_cap of them stored.
+  // split K, for launches with fewer tiles than CUs: the tiles past the last
+  // full round of split_target workgroups (all of them here) have their K
+  // steps cut into parts, each part's fp32 accumulators go to `partial`
+  // ([part slot][BM][BN]), and splitk_reduce_kernel sums them in part order.
+  // At most `splits` parts, at most split_target part slots (one round of the
+  // persistent grid), at most partial_cap of them stored.
   float* partial;
   int splits, split_target, partial_cap;
 };
 
-// Parts per tile of a launch of `ntiles` tiles (1: no split): as many as keep
-// the virtual tiles within one round of split_target workgroups. The GEMM and
-// the reduce kernel derive the same number from the same plan.
-__device__ __forceinline__ int eff_splits(const GemmArgs& g, int64_t ntiles) {
-  if (g.splits <= 1 || ntiles <= 0 || ntiles >= g.split_target) return 1;
-  int64_t s = g.split_target / ntiles;
+// How a launch of ntiles tiles is cut: tiles [0, full) whole (the full rounds of
+// split_target workgroups), the rest in sp parts each, part slots in order.
+// The GEMM and the reduce kernel derive the same cut from the same plan.
+struct SplitCut {
+  int64_t full;
+  int sp;
+};
+__device__ __forceinline__ SplitCut split_cut(const GemmArgs& g, int64_t ntiles) {
+  if (g.splits <= 1 || ntiles <= 0 || g.split_target <= 0) return {ntiles, 1};
+  const int64_t rest = ntiles % g.split_target;
+  if (rest == 0) return {ntiles, 1};
+  int64_t s = g.split_target / rest;
   if (s > g.splits) s = g.splits;
-  if (s * ntiles > g.partial_cap) s = g.partial_cap / ntiles;
-  return s < 2 ? 1 : static_cast<int>(s);
+  if (s * rest > g.partial_cap) s = g.partial_cap / rest;
+  if (s < 2) return {ntiles, 1};
+  return {ntiles - rest, static_cast<int>(s)};
 }
 
 // m-block and column block of tile `tile` of a plan-driven launch: tiles run
@@ -438,7 +446,9 @@ struct DlGemm {
     const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
     const int nmb = kWgrad ? g.n_experts * static_cast<int>(g.M / BM) : g.n_mblocks[0];
     const int64_t nt = static_cast<int64_t>(nmb) * nbc;
-    return nt * eff_splits(g, nt);
+    if constexpr (kWgrad) return nt;
+    const SplitCut c = split_cut(g, nt);
+    return c.full + (nt - c.full) * c.sp;
   }
 
   template <class Pre, class Post>
@@ -453,10 +463,19 @@ struct DlGemm {
     const int mbe = kWgrad ? static_cast<int>(g.M / BM) : 0;
     const int nmb = kWgrad ? g.n_experts * mbe : g.n_mblocks[0];
     int nk = static_cast<int>(K / BK);
-    // split launch: virtual tile = tile * sp + part, part covering K steps kt0 ..
-    const int sp = kWgrad ? 1 : eff_splits(g, static_cast<int64_t>(nmb) * nbc);
-    const int64_t tile = vtile / sp;
-    const int part = static_cast<int>(vtile % sp);
+    // Virtual tiles: the whole tiles of the full rounds, then the parts of the
+    // split tiles, tile-major (part p covers K steps kt0 ..).
+    int sp = 1, part = 0;
+    int64_t tile = vtile, pslot = 0;
+    if constexpr (!kWgrad) {
+      const SplitCut c = split_cut(g, static_cast<int64_t>(nmb) * nbc);
+      if (vtile >= c.full) {
+        sp = c.sp;
+        pslot = vtile - c.full;
+        tile = c.full + pslot / sp;
+        part = static_cast<int>(pslot % sp);
+      }
+    }
     int kt0 = 0;
     const int lrow = lane / CPR;                                          // row within a load instruction
     // Chunk this lane fetches for a load instruction whose first row is R0.
@@ -804,7 +823,7 @@ struct DlGemm {
       int64_t cp = N, col0 = static_cast<int64_t>(nb) * BN, ncols = N;
       if (sp > 1) {
         // one part of a split tile: the raw accumulators, [BM][BN]
-        cbase = g.partial + vtile * (BM * BN);
+        cbase = g.partial + pslot * (BM * BN);
         cp = BN, col0 = 0, ncols = BN;
       } else if constexpr (kWgrad) {
         const int64_t m0 = static_cast<int64_t>(row0);
@@ -1040,15 +1059,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   const int nbc = static_cast<int>((N + OC - 1) / OC);
   const int nmb = g.n_mblocks[0];
   const int64_t nt = static_cast<int64_t>(nmb) * nbc;
-  const int sp = eff_splits(g, nt);
+  const SplitCut cut = split_cut(g, nt);
+  const int sp = cut.sp;
   if (sp <= 1) return;  // the GEMM wrote its outputs itself
   bf16_t* C = static_cast<bf16_t*>(g.C);
-  for (int64_t t = blockIdx.x; t < nt; t += gridDim.x) {
+  for (int64_t t = cut.full + blockIdx.x; t < nt; t += gridDim.x) {
     int mb, nb;
     decode_group_tile(g, t, nbc, nmb, mb, nb);
     const int4 blk = g.mblocks[mb];
     const int row0 = blk.y, rows = blk.z;
-    const float* part = g.partial + t * sp * (BM * BN);
+    const float* part = g.partial + (t - cut.full) * sp * (BM * BN);
     for (int q = threadIdx.x; q < rows * OC; q += blockDim.x) {
       const int r = q / OC, oc = q % OC;
       const int64_t col = static_cast<int64_t>(nb) * OC + oc;
@@ -1118,7 +1138,8 @@ size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, in
   // FC1 tiles: 128 output columns; FC2: 192 or 256
   const bool fc1 = max_mb * ((f + 127) / 128) < cus && split_k_parts(d) > 1;
   const bool fc2 = max_mb * ((d + 255) / 256) < cus && split_k_parts(f) > 1;
-  return fc1 || fc2 ? static_cast<size_t>(cus) * 256 * 256 * sizeof(float) : 0;
+  const int64_t bm = regime_block_rows(regime);
+  return fc1 || fc2 ? static_cast<size_t>(cus) * bm * 256 * sizeof(float) : 0;
 }
 
 static int persistent_grid(int64_t max_tiles) {
@@ -1157,7 +1178,9 @@ static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, h
 // Forward FC1/FC2 launch, split along K when even the largest plan has fewer
 // tiles than CUs (few rows and few experts: a decode step of a handful of
 // tokens) and the partial buffer is there; the tiles' parts then run on all
-// CUs and a second kernel sums them.
+// CUs and a second kernel sums them. (Splitting only the last partial round
+// of a large launch was measured too: the halves and thirds of tiles it adds
+// cost as much as the idle CUs they fill.)
 template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* partial, size_t partial_bytes,
                              hipStream_t s) {
@@ -1175,8 +1198,9 @@ static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* p
   hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN, kPacked>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
                      a);
   if (hipError_t err = hipGetLastError()) return err;
-  hipLaunchKernelGGL((splitk_reduce_kernel<mode_gated(kMode), BM, BN, WN>), dim3(static_cast<int>(max_mb * nb)),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL((splitk_reduce_kernel<mode_gated(kMode), BM, BN, WN>),
+                     dim3(static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, cus)))), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 

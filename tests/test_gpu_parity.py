@@ -201,6 +201,7 @@ SPLIT_SHAPES = [
     (3, 512, 2240, 4, 2, 0.0),      # FC2 alone split: 35 K steps in 4 parts
     (600, 2048, 1024, 2, 1, 1.0),   # few experts with many rows: parts of up to 256 rows
     (100, 1024, 1536, 1, 1, 0.0),   # one expert: FC2 in 3 parts
+    (1200, 1024, 4096, 4, 2, 0.0),  # 256-row tiles: FC1 unsplit (384 tiles), FC2 (72 tiles of 192) in 3 parts
 ]
 
 
