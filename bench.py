@@ -430,7 +430,7 @@ def run_one(args, seed: int) -> dict:
                                         inp["sw1"], inp["sw3"], inp["sw2"], ws=ws, return_routing=True)
     else:
         _, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
-                                 ws=ws, return_routing=True)
+                                 ws=ws, return_routing=True, fused=args.fused, packed=packed)
     # shared experts count as S more experts with T rows each
     counts = r["counts"].cpu().tolist() + [cfg.T] * S
     kk = cfg.k + S
