@@ -257,7 +257,7 @@ def test_grouped_ffn_partial_blocks(monkeypatch, regime):
     assert err <= OUT_TOL
 
 
-@pytest.mark.parametrize("gate_cfg", ["8,2,4", "4,4,4", "2,4,8", "lds", ""])
+@pytest.mark.parametrize("gate_cfg", ["8,2,4", "4,4,4", "2,4,8", "lds", "lds2", ""])
 @pytest.mark.parametrize("shape", [(300, 200, 24), (77, 512, 8), (1000, 1024, 64), (500, 832, 48)],
                          ids=lambda s: "T{}_d{}_E{}".format(*s))
 def test_gate_tile_configs_bit_exact(monkeypatch, gate_cfg, shape):
