@@ -369,3 +369,19 @@ def test_full_size_shared_workload():
     err = rel_err(gpu_float(out[torch.from_numpy(toks).cuda()]), routed + shared)
     _say(f"  sampled out rel_err={err:.3e} over {toks.size} tokens")
     assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("path", ["stored", "packed", "fused"])
+def test_empty_batch_forward(path):
+    """T = 0: every layer entry point returns at once, with nothing to compute."""
+    _say(f"case empty batch {path}")
+    d, f, E, k = 256, 256, 8, 2
+    inp = moe_inputs.random_inputs(4, d, f, E, k, "bf16", 0.0, seed=31, device="cuda")
+    dims = moe.Dims(0, d, f, E, k, torch.bfloat16)
+    x0 = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    packed = moe.pack_weights(moe.Dims(4, d, f, E, k, torch.bfloat16), inp["w1"], inp["w3"], inp["w2"]) \
+        if path == "packed" else None
+    out, r = moe.layer_forward(dims, x0, inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                               return_routing=True, fused=path == "fused", packed=packed)
+    torch.cuda.synchronize()
+    assert out.shape == (0, d) and r["topk_idx"].shape == (0, k) and r["perm"].numel() == 0
