@@ -111,7 +111,7 @@ def test_packed_oracle_bar():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_decode_t1", "deepseek_bal", "dbrx_zipf"])
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_decode_t1", "deepseek_bal", "dbrx_zipf", "mixtral_prefill_skew"])
 def test_packed_full_size_bitwise(name):
     cfg = moe_inputs.config(name)
     _say(f"case packed full {name}")
