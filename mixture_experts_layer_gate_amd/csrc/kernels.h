@@ -17,6 +17,11 @@ hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const fl
 // Top-k selection + renormalised softmax weights from logits.
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
                        hipStream_t s);
+// Gate + top-k in one launch for small batches (E <= 16, T * E <= 4096, no
+// forced gate tiling): the same logits, bit for bit, and the same selection.
+bool route_small_ok(int64_t T, int E);
+hipError_t launch_route_small(int dtype, const void* x, const void* wg, const float* bias, float* logits, int64_t T,
+                              int64_t d, int E, int k, int32_t* idx, float* w, hipStream_t s);
 
 // Dispatch. n = T*k assignments, cut into n_chunks chunks of `chunk` assignments.
 void dispatch_chunking(int64_t n, int* chunk, int* n_chunks);

@@ -197,6 +197,10 @@ size_t bwd_ws(const moe_dims_t* dm, void* ws, BwdWs* out) {
 // ---------------- launch sequences (arguments already validated) ----------------
 int do_route(const moe_dims_t* dm, const void* x, const void* wg, const float* bias, float* logits,
              int32_t* idx, float* w, hipStream_t s) {
+  if (route_small_ok(dm->T, dm->E)) {
+    StageScope sc(MOE_STAGE_GATE, s);  // gate and top-k in one launch
+    return hip_status(launch_route_small(dm->dtype, x, wg, bias, logits, dm->T, dm->d, dm->E, dm->k, idx, w, s));
+  }
   {
     StageScope sc(MOE_STAGE_GATE, s);
     if (int st = hip_status(launch_gate_logits(dm->dtype, x, wg, bias, logits, dm->T, dm->d, dm->E, s))) return st;

@@ -345,20 +345,18 @@ hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const fl
 // lower expert index (IEEE compare, so -0 == +0). Weights: softmax over the k
 // selected logits, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
 constexpr int kMaxE = 1024;
+constexpr int kRouteSmallMaxE = 16;  // experts of the one-launch gate + top-k (one wave each)
 constexpr int kPerLane = kMaxE / kWave;
 
 __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int k, int32_t* __restrict__ idx,
-                                                   float* __restrict__ w) {
-  __shared__ float sel_v[4][kMaxE];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wv;
-  if (t >= T) return;
-  const float* row = logits + static_cast<int64_t>(t) * E;
+// Top-k of one token's E logits by one wave (every lane calls it): k rounds
+// of a wave arg-max, then the weights. sel: kMaxE floats of this wave's LDS.
+__device__ __forceinline__ void topk_row(const float* row, int E, int k, int32_t* __restrict__ idx_row,
+                                         float* __restrict__ w_row, float* sel) {
+  const int lane = threadIdx.x & 63;
   float v[kPerLane];
   bool taken[kPerLane];
   const int per = (E + kWave - 1) / kWave;
@@ -391,15 +389,88 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (j == 0) v0 = bv;
     sum += expf(bv - v0);
     if (lane == 0) {
-      idx[static_cast<int64_t>(t) * k + j] = be;
-      sel_v[wv][j] = bv;
+      idx_row[j] = be;
+      sel[j] = bv;
     }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const float inv = 1.0f / sum;
-  for (int j = lane; j < k; j += kWave) w[static_cast<int64_t>(t) * k + j] = expf(sel_v[wv][j] - v0) * inv;
+  for (int j = lane; j < k; j += kWave) w_row[j] = expf(sel[j] - v0) * inv;
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w) {
+  __shared__ float sel_v[4][kMaxE];
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  topk_row(logits + static_cast<int64_t>(t) * E, E, k, idx + static_cast<int64_t>(t) * k,
+           w + static_cast<int64_t>(t) * k, sel_v[wv]);
+}
+
+// Gate and top-k of small batches in one launch: workgroup t holds token t,
+// wave e computes logit (t, e) in the contract order (lane q sums class q,
+// elements q, q + 64, .. in order, then the butterfly over offsets 32 .. 1 and
+// the bias: gate_logits_kernel's order with one class per lane), and wave 0
+// then selects the token's top k from the logits in LDS.
+template <int kDtype>
+__global__ __launch_bounds__(1024) void route_small_kernel(const void* __restrict__ x, const void* __restrict__ wg,
+                                                           const float* __restrict__ bias, float* __restrict__ logits,
+                                                           int T, int d, int E, int k, int32_t* __restrict__ idx,
+                                                           float* __restrict__ w) {
+  __shared__ float srow[kRouteSmallMaxE];
+  __shared__ float sel[kMaxE];
+  const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int64_t xrow = static_cast<int64_t>(t) * d, wrow = static_cast<int64_t>(e) * d;
+  constexpr int U = 8;
+  float acc = 0.0f;
+  int i0 = lane;
+  for (; i0 + (U - 1) * 64 < d; i0 += U * 64) {
+    float xv[U][1], wv[U][1];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      loadG<kDtype, 1>(x, xrow + i0 + u * 64, xv[u]);
+      loadG<kDtype, 1>(wg, wrow + i0 + u * 64, wv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mac<kDtype>(xv[u][0], wv[u][0], acc);
+  }
+  for (; i0 < d; i0 += 64) {
+    float xv[1], wv[1];
+    loadG<kDtype, 1>(x, xrow + i0, xv);
+    loadG<kDtype, 1>(wg, wrow + i0, wv);
+    acc = mac<kDtype>(xv[0], wv[0], acc);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_down(acc, off, 64);
+  if (lane == 0) {
+    const float l = acc + (bias ? bias[e] : 0.0f);
+    srow[e] = l;
+    logits[static_cast<int64_t>(t) * E + e] = l;
+  }
+  __syncthreads();
+  if (e == 0)
+    topk_row(srow, E, k, idx + static_cast<int64_t>(t) * k, w + static_cast<int64_t>(t) * k, sel);
+}
+
+bool route_small_ok(int64_t T, int E) {
+  if (getenv("MOE_GATE_CFG")) return false;  // a forced gate tiling keeps the separate launches
+  return T >= 1 && E <= kRouteSmallMaxE && T * E <= 4096;
+}
+
+hipError_t launch_route_small(int dtype, const void* x, const void* wg, const float* bias, float* logits, int64_t T,
+                              int64_t d, int E, int k, int32_t* idx, float* w, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(route_small_kernel<1>, dim3(static_cast<unsigned>(T)), dim3(64 * E), 0, s, x, wg, bias, logits,
+                       static_cast<int>(T), static_cast<int>(d), E, k, idx, w);
+  else
+    hipLaunchKernelGGL(route_small_kernel<0>, dim3(static_cast<unsigned>(T)), dim3(64 * E), 0, s, x, wg, bias, logits,
+                       static_cast<int>(T), static_cast<int>(d), E, k, idx, w);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
