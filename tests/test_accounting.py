@@ -1,0 +1,84 @@
+"""Host-only checks of the roofline accounting and of the bench command line.
+
+The byte and FLOP counts are recomputed here from the shapes by hand
+(parameter counts times bytes per element), not through the helpers, so a
+dropped term or a wrong factor in the helpers fails a test."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from mixture_experts_layer_gate_amd import roofline as rf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Mixtral-8x22B shape: hidden 6144, expert FFN 16384, 8 experts, top-2
+D, F, E, K = 6144, 16384, 8, 2
+
+
+def test_layer_flops_per_token_mixtral():
+    # per token: the gate touches d*E weights once (multiply + add), each of
+    # the k experts touches its 3*d*f weights once
+    per_token = 2 * D * E + K * 3 * D * F * 2
+    assert rf.layer_flops(1, D, F, E, K) == per_token
+    assert rf.layer_flops(256, D, F, E, K) == 256 * per_token
+    assert abs(per_token / 1e9 - 1.208) < 5e-4
+
+
+def test_fc1_fc2_split_the_ffn():
+    rows = 777
+    assert rf.fc1_flops(rows, D, F) + rf.fc2_flops(rows, D, F) == rf.ffn_flops(rows, D, F)
+    assert rf.fc1_flops(rows, D, F) == 2 * rf.fc2_flops(rows, D, F)
+
+
+def test_layer_bytes_decode_all_active():
+    T = 256
+    weights = E * 3 * D * F * 2          # W1, W3, W2 of every expert, bf16
+    gate = D * E * 2
+    act = 2 * T * D * 2                  # x read once, out written once
+    counts = [T * K // E] * E
+    assert rf.layer_bytes(T, D, F, E, counts) == weights + gate + act
+    assert abs((weights + gate + act) / 1e9 - 4.838) < 1e-3
+
+
+def test_layer_bytes_skip_idle_experts():
+    T = 256
+    full = rf.layer_bytes(T, D, F, E, [64] * E)
+    three_idle = rf.layer_bytes(T, D, F, E, [128, 128, 64, 64, 128, 0, 0, 0])
+    assert full - three_idle == 3 * 3 * D * F * 2
+    assert rf.active_experts([0, 3, 0, 1]) == 2
+
+
+def test_kernel_bytes_add_up_to_the_expert_weights():
+    T = 300
+    counts = [75, 0, 150, 75, 0, 0, 0, 300]
+    a = 4
+    fc1 = rf.fc1_bytes(T, D, F, K, counts)
+    fc2 = rf.fc2_bytes(T, D, F, K, counts)
+    # weights: 2 matrices in FC1, 1 in FC2; activations: x gathered T*k rows,
+    # h written and read back, y written
+    assert fc1 == a * 2 * D * F * 2 + T * K * D * 2 + T * K * F * 2
+    assert fc2 == a * D * F * 2 + T * K * F * 2 + T * K * D * 2
+    assert fc1 + fc2 - (T * K * (D + F) * 2 * 2) == a * 3 * D * F * 2
+
+
+def test_classify_binding():
+    # ridge of the chip in FLOP per byte; bf16 weights give 1 FLOP per byte
+    # per row, so the ridge is also the rows per expert where MFMA takes over
+    ridge = rf.PEAK_MFMA_BF16_FLOPS / rf.PEAK_HBM_BYTES_PER_S
+    assert 300 < ridge < 330
+    decode = rf.classify(rf.layer_flops(256, D, F, E, K), rf.layer_bytes(256, D, F, E, [64] * E))
+    assert decode.bound == "hbm" and decode.floor_s == decode.t_byte_s
+    T = 8192
+    prefill = rf.classify(rf.layer_flops(T, D, F, E, K), rf.layer_bytes(T, D, F, E, [T * K // E] * E))
+    assert prefill.bound == "mfma" and prefill.floor_s == prefill.t_flop_s
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
