@@ -93,6 +93,44 @@ def test_forced_skew_all_tokens_to_k_experts():
     assert r["counts"].cpu().tolist() == [cfg.T] * cfg.k + [0] * (cfg.E - cfg.k)
 
 
+# Exactly tied logits: rows of x that are zero give logit = bias exactly, and
+# the bias repeats values (and holds both -0.0 and +0.0, equal under IEEE
+# comparison). Equal logits go to the lower expert index, on both the one-launch
+# gate + top-k (small batches) and the separate launches.
+@pytest.mark.parametrize("shape", [(96, 128, 128, 8, 3), (700, 256, 128, 8, 3), (300, 256, 128, 32, 4)],
+                         ids=lambda s: "T{}_d{}_f{}_E{}_k{}".format(*s))
+def test_tied_logits_take_the_lower_expert(shape):
+    T, d, f, E, k = shape
+    _say(f"case tied logits {shape}")
+    cfg = moe_inputs.LayerConfig("ties", T, d, f, E, k, "bf16", 0.0)
+    inp = moe_inputs.make_layer_inputs(cfg, 4, "cuda")
+    inp["x"][::3] = 0
+    base = [0.5, 1.0, 1.0, -0.0, 0.0, 1.0, 0.25, 0.5]
+    bias = torch.tensor([base[e % 8] for e in range(E)], dtype=torch.float32)
+    inp["bias"] = bias.cuda()
+    out, r, ref = _full_oracle_check(cfg, inp)
+    idx = r["topk_idx"].cpu().numpy()[::3]
+    want = [e for e in np.argsort(-bias.numpy(), kind="stable")[:k]]
+    assert (idx == np.array(want, dtype=idx.dtype)[None, :]).all()
+    w = r["topk_w"].cpu().numpy()[::3]
+    # tied selected logits: equal weights summing to one
+    if len({float(bias[e]) for e in want}) == 1:
+        np.testing.assert_allclose(w, 1.0 / k, rtol=1e-6)
+
+
+def test_all_logits_tied_pick_the_first_k():
+    cfg = moe_inputs.LayerConfig("allties", 64, 128, 128, 16, 4, "bf16", 0.0)
+    _say("case all logits tied")
+    inp = moe_inputs.make_layer_inputs(cfg, 5, "cuda")
+    inp["x"].zero_()
+    inp["bias"] = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+    out, r, ref = _full_oracle_check(cfg, inp)
+    assert (r["topk_idx"].cpu().numpy() == np.arange(cfg.k)[None, :]).all()
+    np.testing.assert_allclose(r["topk_w"].cpu().numpy(), 1.0 / cfg.k, rtol=1e-6)
+    assert r["counts"].cpu().tolist() == [cfg.T] * cfg.k + [0] * (cfg.E - cfg.k)
+    assert float(np.abs(gpu_float(out)).max()) == 0.0
+
+
 def test_determinism_bitwise():
     cfg = moe_inputs.LayerConfig("det", 777, 256, 256, 32, 4, "bf16", 1.0)
     _say("case determinism")
