@@ -235,7 +235,7 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
                   fused=False, packed=None):
     """The whole layer. With return_routing, also returns the routing arrays as a dict.
     fused=True runs FC1, FC2 and the combine as one persistent launch
-    (moe_layer_forward_fused; bitwise the same result). packed=(w13p, w2p) from
+    (moe_layer_forward_fused; bitwise the same result). packed=(w1p, w3p, w2p) from
     pack_weights reads the stage-order weights instead of w1, w3, w2 (which may
     then be None; moe_layer_forward_packed, bitwise the same result)."""
     lib = load_library()
