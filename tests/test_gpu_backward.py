@@ -131,6 +131,24 @@ def test_backward_small_shapes(shape):
             assert not torch.any(g[name][int(e)]), (name, e)
 
 
+def _random_bwd_shapes(n=16, seed=20261203):
+    """Seeded random shapes: tokens 1..500, d and f multiples of 256 up to 768,
+    1..64 experts, top-1..4, gate bias 0, 1 or 2 times -ln(rank)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        out.append((int(rng.integers(1, 501)), 256 * int(rng.integers(1, 4)), 256 * int(rng.integers(1, 4)),
+                    E, k, float(rng.choice([0.0, 1.0, 2.0]))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_bwd_shapes(), ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
+def test_backward_random_shapes(shape):
+    test_backward_small_shapes(shape)
+
+
 def test_backward_forced_routing():
     """All tokens on experts 0..k-1 (bias +1e4): one expert per slot, the rest empty."""
     T, d, f, E, k = 300, 256, 512, 8, 2
