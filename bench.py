@@ -176,6 +176,40 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 5}), flush=True)
 
 
+def stage_rooflines(cfg, kk: int, counts, elt: int, stage_ms: dict) -> dict:
+    """Each forward stage against the bound of its own work: the gate's fp32
+    multiply-adds against the unpacked fp32 vector peak, FC1 and FC2 against
+    bf16 MFMA or HBM (whichever their algorithmic work binds), the routing and
+    data-movement stages against HBM by the bytes they must move (top-k and
+    dispatch move a few MB at most and are bound by launch latency, so their
+    fractions are small by nature). Where the gate and top-k run as one launch
+    (small batches) the gate entry times both."""
+    from mixture_experts_layer_gate_amd import roofline as rf
+    T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
+    n = T * kk
+    out = {}
+
+    def put(stage, bound, work, peak, unit, scale):
+        ms = stage_ms.get(stage)
+        if not ms:
+            return
+        achieved = work / (ms * 1e-3) / scale
+        out[stage] = {"ms": round(ms, 4), "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                      "unit": unit, "frac": round(achieved / peak, 4)}
+
+    put("gate", "valu", 2 * T * d * E, round(rf.PEAK_VALU_FP32_UNPACKED_FLOPS / 1e12, 1), "TFLOP/s", 1e12)
+    put("topk", "hbm", T * E * 4 + n * 8, 8000.0, "GB/s", 1e9)
+    put("dispatch", "hbm", n * 4 * 2 + n * 8, 8000.0, "GB/s", 1e9)
+    for stage, flops, nbytes in (("fc1", rf.fc1_flops(n, d, f), rf.fc1_bytes(T, d, f, kk, counts, elt)),
+                                 ("fc2", rf.fc2_flops(n, d, f), rf.fc2_bytes(T, d, f, kk, counts, elt))):
+        if rf.classify(flops, nbytes).bound == "hbm":
+            put(stage, "hbm", nbytes, 8000.0, "GB/s", 1e9)
+        else:
+            put(stage, "mfma", flops, 2500.0 if cfg.dtype == "bf16" else 157.3, "TFLOP/s", 1e12)
+    put("combine", "hbm", n * d * elt + T * d * elt + n * 8, 8000.0, "GB/s", 1e9)
+    return out
+
+
 def cpu_baseline(cfg, inp, ntok: int, seed: int = 0):
     """Time the CPU oracle (as it stands) on the first ntok tokens of the same inputs."""
     import numpy as np
@@ -534,6 +568,8 @@ def run_one(args, seed: int) -> dict:
         "ceilings": ceilings,
         "stages_ms": {s: round(v[0] / max(v[1], 1), 4) for s, v in stages.items() if v[1] > 0},
     }
+    if not args.fused:
+        res["stages_roofline"] = stage_rooflines(cfg, kk, counts, elt, res["stages_ms"])
     if not args.no_cpu_baseline:
         ntok = cfg.T if args.cpu_sample_tokens <= 0 else min(cfg.T, args.cpu_sample_tokens)
         res["cpu_baseline"] = cpu_baseline(cfg, inp, ntok, seed)

@@ -19,6 +19,9 @@ PEAK_HBM_BYTES_PER_S = 8.0e12
 PEAK_MFMA_BF16_FLOPS = 2.5e15
 PEAK_MFMA_FP32_FLOPS = 157.3e12
 PEAK_VALU_FP32_FLOPS = 157.3e12
+# fp32 vector FMA without packed instructions (the library is built with packed
+# fp32 off): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz
+PEAK_VALU_FP32_UNPACKED_FLOPS = 256 * 4 * 16 * 2 * 2.4e9
 
 
 def util(topk: int, experts: int, B: float, F: float, b: float) -> float:
