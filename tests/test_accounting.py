@@ -82,3 +82,27 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_stage_rooflines_by_hand():
+    sys.path.insert(0, ROOT)
+    import bench
+    import moe_inputs
+    cfg = moe_inputs.config("mixtral_decode")
+    T, k = cfg.T, cfg.k
+    counts = [T * k // cfg.E] * cfg.E
+    ms = {"gate": 0.01, "fc1": 0.5, "fc2": 0.25, "combine": 0.01, "dispatch": 0.005}
+    out = bench.stage_rooflines(cfg, k, counts, 2, ms)
+    assert set(out) == set(ms)
+    # gate: 2*T*d*E FLOP over 10 us against the unpacked fp32 vector peak
+    gate = 2 * T * D * E / 1e-5 / 1e12
+    assert out["gate"]["achieved"] == pytest.approx(gate, abs=0.01)
+    assert out["gate"]["peak"] == pytest.approx(78.6, abs=0.05)
+    # decode FC1 streams W1 and W3 of all 8 experts: HBM-bound
+    fc1 = (8 * 2 * D * F * 2 + T * K * D * 2 + T * K * F * 2) / 0.5e-3 / 1e9
+    assert out["fc1"]["bound"] == "hbm"
+    assert out["fc1"]["achieved"] == pytest.approx(fc1, abs=0.01)
+    assert out["fc1"]["frac"] == pytest.approx(fc1 / 8000.0, abs=1e-4)
+    assert out["fc2"]["bound"] == "hbm"
+    comb = (T * K * D * 2 + T * D * 2 + T * K * 8) / 1e-5 / 1e9
+    assert out["combine"]["achieved"] == pytest.approx(comb, abs=0.01)
