@@ -11,11 +11,15 @@ moe_layer_forward on the weights as stored.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceilings]
   python bench.py --backward [--workload NAME] ...   (the layer's backward instead)
 
-The default workload is the Mixtral-8x22B-shaped decode layer (T=256, d=6144,
-f=16384, E=8, top-2, bf16, balanced routing). The roofline object covers the
-dominant kernel (the grouped FC1), timed with HIP events recorded around each
-of its launches inside the timed region; the cpu_baseline object times the CPU
-oracle on a bounded sample of the same workload.
+The default workload is the Mixtral-8x22B-shaped prefill layer (T=8192,
+d=6144, f=16384, E=8, top-2, bf16, routing skewed by the gate-logit bias
+1.5*(-ln rank)): the largest single-GPU configuration, MFMA-bound. The
+roofline object covers the dominant kernel (the grouped FC1), timed with HIP
+events recorded around each of its launches inside the timed region; the
+cpu_baseline object times the CPU oracle on a bounded sample of the same
+workload. The line also carries, under "decode", the same measurement of the
+Mixtral-8x22B-shaped decode layer (T=256, balanced routing, HBM-bound), run
+after the main one in the same process (--secondary none skips it).
 """
 from __future__ import annotations
 
@@ -29,12 +33,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 
+DEFAULT_WORKLOAD = "mixtral_prefill_skew"
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="mixtral_decode")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--secondary", default="mixtral_decode",
+                   help="workload measured after the default one and reported under 'decode' "
+                        "(only when --workload is the default; 'none' skips it)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
@@ -147,7 +157,7 @@ def protocol(args):
         runs = []
         for _ in range(2):
             cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--seeds", "0,1,2",
-                   "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-ceilings",
+                   "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-ceilings", "--secondary", "none",
                    "--weights", args.weights]
             out = subprocess.run(cmd, check=True, capture_output=True, text=True).stdout
             runs += [json.loads(l) for l in out.splitlines() if l.startswith("{")]
@@ -198,16 +208,25 @@ def stage_rooflines(cfg, kk: int, counts, elt: int, stage_ms: dict) -> dict:
         out[stage] = {"ms": round(ms, 4), "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                       "unit": unit, "frac": round(achieved / peak, 4)}
 
+    hbm = rf.PEAK_HBM_BYTES_PER_S / 1e9
+    mfma = (rf.PEAK_MFMA_BF16_FLOPS if cfg.dtype == "bf16" else rf.PEAK_MFMA_FP32_FLOPS) / 1e12
     put("gate", "valu", 2 * T * d * E, round(rf.PEAK_VALU_FP32_UNPACKED_FLOPS / 1e12, 1), "TFLOP/s", 1e12)
-    put("topk", "hbm", T * E * 4 + n * 8, 8000.0, "GB/s", 1e9)
-    put("dispatch", "hbm", n * 4 * 2 + n * 8, 8000.0, "GB/s", 1e9)
+    put("topk", "hbm", T * E * 4 + n * 8, hbm, "GB/s", 1e9)
+    put("dispatch", "hbm", n * 4 * 2 + n * 8, hbm, "GB/s", 1e9)
     for stage, flops, nbytes in (("fc1", rf.fc1_flops(n, d, f), rf.fc1_bytes(T, d, f, kk, counts, elt)),
                                  ("fc2", rf.fc2_flops(n, d, f), rf.fc2_bytes(T, d, f, kk, counts, elt))):
         if rf.classify(flops, nbytes).bound == "hbm":
-            put(stage, "hbm", nbytes, 8000.0, "GB/s", 1e9)
+            put(stage, "hbm", nbytes, hbm, "GB/s", 1e9)
         else:
-            put(stage, "mfma", flops, 2500.0 if cfg.dtype == "bf16" else 157.3, "TFLOP/s", 1e12)
-    put("combine", "hbm", n * d * elt + T * d * elt + n * 8, 8000.0, "GB/s", 1e9)
+            put(stage, "mfma", flops, mfma, "TFLOP/s", 1e12)
+    put("combine", "hbm", rf.combine_bytes(T, d, kk, elt), hbm, "GB/s", 1e9)
+    # traffic each stage moves beyond its algorithmic bytes (gathered x rows,
+    # the h and y round trips), per launch
+    ovh = {"fc1": rf.fc1_overhead_bytes(T, d, f, kk, elt), "fc2": rf.fc2_overhead_bytes(T, d, f, kk, elt),
+           "combine": rf.combine_overhead_bytes(T, d, kk, elt)}
+    for stage, b in ovh.items():
+        if stage in out:
+            out[stage]["overhead_bytes"] = b
     return out
 
 
@@ -291,7 +310,24 @@ def main():
         return
     seeds = [int(v) for v in args.seeds.split(",") if v] or [args.seed]
     for seed in seeds:
-        print(json.dumps(run_backward(args, seed) if args.backward else run_one(args, seed)), flush=True)
+        if args.backward:
+            print(json.dumps(run_backward(args, seed)), flush=True)
+            continue
+        res = run_one(args, seed)
+        if args.workload == DEFAULT_WORKLOAD and args.secondary != "none" and not args.seeds:
+            res["decode"] = secondary(args, seed)
+        print(json.dumps(res), flush=True)
+
+
+def secondary(args, seed: int) -> dict:
+    """The same measurement on a second workload (by default the decode-sized,
+    HBM-bound layer), reported beside the main line: its throughput, step time
+    and the roofline of its dominant kernel."""
+    sub = argparse.Namespace(**vars(args))
+    sub.workload, sub.no_cpu_baseline, sub.no_ceilings = args.secondary, True, True
+    r = run_one(sub, seed)
+    keep = ("metric", "value", "unit", "ms_per_step", "dtype", "config", "roofline", "layer", "stages_ms")
+    return {k: r[k] for k in keep}
 
 
 def cpu_baseline_backward(cfg, inp, dout, ntok: int, seed: int = 0):
@@ -373,8 +409,8 @@ def run_backward(args, seed: int) -> dict:
     dom_ms = rec[0] / max(rec[1], 1)
     P = cfg.T * cfg.k
     dom_flops = rf.BACKWARD_GEMM_FLOPS_PER_ROW[dom] * cfg.d * cfg.f * P
-    roof = {"bound": "mfma", "achieved": round(dom_flops / (dom_ms * 1e-3) / 1e12, 1), "peak": 2500.0,
-            "unit": "TFLOP/s"}
+    roof = {"bound": "mfma", "achieved": round(dom_flops / (dom_ms * 1e-3) / 1e12, 1),
+            "peak": rf.PEAK_MFMA_BF16_FLOPS / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
     roof["kernel"] = {"bwd_fc1": "gemm_dl_kernel<FC1 recompute g|u, 256x256>",
@@ -504,23 +540,33 @@ def run_one(args, seed: int) -> dict:
     elt = 2 if cfg.dtype == "bf16" else 4
     n = cfg.T * kk
     fc1_ms = stages[dom][0] / max(stages[dom][1], 1)
+    T, d, f = cfg.T, cfg.d, cfg.f
     if args.fused:
-        # one launch does FC1, FC2 and the combine: FFN FLOP, and all expert weights + x + h + y + out bytes
-        fc1_flops = rf.ffn_flops(n, cfg.d, cfg.f)
-        fc1_bytes = (rf.fc1_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt) +
-                     rf.fc2_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt) + cfg.T * cfg.d * elt)
+        # one launch does FC1, FC2 and the combine: FFN FLOP; all active expert
+        # weights, x once and out once (the h and y round trips are overhead)
+        fc1_flops = rf.ffn_flops(n, d, f)
+        fc1_bytes = (rf.fc1_bytes(T, d, f, kk, counts, elt) + rf.fc2_bytes(T, d, f, kk, counts, elt) +
+                     rf.combine_bytes(T, d, kk, elt))
+        overhead = (rf.fc1_overhead_bytes(T, d, f, kk, elt) + rf.fc2_overhead_bytes(T, d, f, kk, elt) +
+                    rf.combine_overhead_bytes(T, d, kk, elt))
     else:
-        fc1_flops = rf.fc1_flops(n, cfg.d, cfg.f)
-        fc1_bytes = rf.fc1_bytes(cfg.T, cfg.d, cfg.f, kk, counts, elt)
+        fc1_flops = rf.fc1_flops(n, d, f)
+        fc1_bytes = rf.fc1_bytes(T, d, f, kk, counts, elt)
+        overhead = rf.fc1_overhead_bytes(T, d, f, kk, elt)
     cls = rf.classify(fc1_flops, fc1_bytes)
     if cls.bound == "hbm":
         achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.PEAK_HBM_BYTES_PER_S / 1e9,
+                "unit": "GB/s"}
     else:
-        peak = 2500.0 if cfg.dtype == "bf16" else 157.3
+        peak = (rf.PEAK_MFMA_BF16_FLOPS if cfg.dtype == "bf16" else rf.PEAK_MFMA_FP32_FLOPS) / 1e12
         achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["algorithmic"] = {"flop": fc1_flops, "bytes": fc1_bytes, "overhead_bytes": overhead,
+                           "per_unit": ("4*d*f FLOP per sorted row (T*k rows); bytes: W1 and W3 of the active "
+                                        "experts + x once; overhead: the other T*k - T gathered x rows + h written")
+                           if not args.fused else "6*d*f FLOP per sorted row; all active expert weights + x + out"}
     roof["traffic"] = None if args.fused else measured_traffic(cfg.name, "fc1_packed" if use_packed else "fc1")
     big_tile = cfg.dtype == "bf16" and os.environ.get("MOE_GEMM_REGIME", "1") != "0"
     if args.fused:

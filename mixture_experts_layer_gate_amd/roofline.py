@@ -14,7 +14,9 @@ from __future__ import annotations
 from dataclasses import dataclass
 from typing import Iterable, Sequence
 
-# MI355X published peaks (dense, no sparsity)
+# MI355X published peaks (dense, no sparsity). bf16 MFMA: the published 2.5
+# PFLOP/s (256 CUs x 4096 FLOP per clock x 2.4 GHz = 2516.6 TFLOP/s, rounded);
+# every fraction this package reports uses these constants.
 PEAK_HBM_BYTES_PER_S = 8.0e12
 PEAK_MFMA_BF16_FLOPS = 2.5e15
 PEAK_MFMA_FP32_FLOPS = 157.3e12
@@ -80,15 +82,39 @@ def layer_bytes(T: int, d: int, f: int, E: int, counts: Sequence[int], elt: int 
 
 
 def fc1_bytes(T: int, d: int, f: int, k: int, counts: Sequence[int], elt: int = 2) -> int:
-    """FC1 kernel: W1 and W3 of active experts, the T*k gathered x rows, h written."""
+    """Algorithmic bytes of the FC1 kernel: W1 and W3 of the active experts and
+    x read once. The T*k gathered reads of x beyond the first and the h store
+    are implementation traffic (fc1_overhead_bytes)."""
     a = active_experts(counts)
-    return 2 * d * f * elt * a + T * k * d * elt + T * k * f * elt
+    return 2 * d * f * elt * a + T * d * elt
 
 
 def fc2_bytes(T: int, d: int, f: int, k: int, counts: Sequence[int], elt: int = 2) -> int:
-    """FC2 kernel: W2 of active experts, h read, y written."""
+    """Algorithmic bytes of the FC2 kernel: W2 of the active experts. Reading h
+    back and storing y are implementation traffic (fc2_overhead_bytes)."""
     a = active_experts(counts)
-    return d * f * elt * a + T * k * f * elt + T * k * d * elt
+    return d * f * elt * a
+
+
+def fc1_overhead_bytes(T: int, d: int, f: int, k: int, elt: int = 2) -> int:
+    """FC1 traffic beyond the algorithmic bytes: x rows gathered T*k times
+    instead of once, and h [T*k][f] written."""
+    return (T * k - T) * d * elt + T * k * f * elt
+
+
+def fc2_overhead_bytes(T: int, d: int, f: int, k: int, elt: int = 2) -> int:
+    """FC2 traffic beyond the algorithmic bytes: h [T*k][f] read, y [T*k][d] written."""
+    return T * k * f * elt + T * k * d * elt
+
+
+def combine_bytes(T: int, d: int, k: int, elt: int = 2) -> int:
+    """Algorithmic bytes of the combine: out [T][d] written."""
+    return T * d * elt
+
+
+def combine_overhead_bytes(T: int, d: int, k: int, elt: int = 2) -> int:
+    """Combine traffic beyond out: the T*k rows of y read, inv_perm and topk_w (4 bytes each)."""
+    return T * k * d * elt + T * k * 8
 
 
 def kappa(counts: Sequence[int]) -> float:

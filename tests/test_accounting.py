@@ -51,17 +51,24 @@ def test_layer_bytes_skip_idle_experts():
     assert rf.active_experts([0, 3, 0, 1]) == 2
 
 
-def test_kernel_bytes_add_up_to_the_expert_weights():
+def test_kernel_bytes_add_up_to_the_layer_bytes():
     T = 300
     counts = [75, 0, 150, 75, 0, 0, 0, 300]
     a = 4
     fc1 = rf.fc1_bytes(T, D, F, K, counts)
     fc2 = rf.fc2_bytes(T, D, F, K, counts)
-    # weights: 2 matrices in FC1, 1 in FC2; activations: x gathered T*k rows,
-    # h written and read back, y written
-    assert fc1 == a * 2 * D * F * 2 + T * K * D * 2 + T * K * F * 2
-    assert fc2 == a * D * F * 2 + T * K * F * 2 + T * K * D * 2
-    assert fc1 + fc2 - (T * K * (D + F) * 2 * 2) == a * 3 * D * F * 2
+    comb = rf.combine_bytes(T, D, K)
+    # algorithmic: W1 and W3 of the active experts plus x read once (FC1), W2
+    # (FC2), out written once (combine); with the gate weight, the layer's bytes
+    assert fc1 == a * 2 * D * F * 2 + T * D * 2
+    assert fc2 == a * D * F * 2
+    assert comb == T * D * 2
+    assert fc1 + fc2 + comb + D * E * 2 == rf.layer_bytes(T, D, F, E, counts)
+    # implementation traffic, reported apart: x gathered T*k times instead of
+    # once, h written and read back, y written and read back
+    assert rf.fc1_overhead_bytes(T, D, F, K) == (T * K - T) * D * 2 + T * K * F * 2
+    assert rf.fc2_overhead_bytes(T, D, F, K) == T * K * F * 2 + T * K * D * 2
+    assert rf.combine_overhead_bytes(T, D, K) == T * K * D * 2 + T * K * 8
 
 
 def test_classify_binding():
@@ -74,6 +81,18 @@ def test_classify_binding():
     T = 8192
     prefill = rf.classify(rf.layer_flops(T, D, F, E, K), rf.layer_bytes(T, D, F, E, [T * K // E] * E))
     assert prefill.bound == "mfma" and prefill.floor_s == prefill.t_flop_s
+
+
+def test_bench_defaults_to_the_largest_single_gpu_workload():
+    sys.path.insert(0, ROOT)
+    import bench
+    import moe_inputs
+    cfg = moe_inputs.config(bench.DEFAULT_WORKLOAD)
+    # the Mixtral-8x22B prefill layer with skewed routing: T=8192, top-2 of 8
+    assert (cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.dtype, cfg.bias_scale) == (8192, D, F, E, K, "bf16", 1.5)
+    # the largest FLOP count of the single-GPU workloads
+    flops = {n: rf.layer_flops(c.T, c.d, c.f, c.E, c.k) for n, c in moe_inputs.CONFIGS.items()}
+    assert max(flops, key=flops.get) in ("mixtral_prefill_skew", "mixtral_prefill_bal")
 
 
 def test_bench_refuses_more_than_one_gpu():
@@ -98,11 +117,16 @@ def test_stage_rooflines_by_hand():
     gate = 2 * T * D * E / 1e-5 / 1e12
     assert out["gate"]["achieved"] == pytest.approx(gate, abs=0.01)
     assert out["gate"]["peak"] == pytest.approx(78.6, abs=0.05)
-    # decode FC1 streams W1 and W3 of all 8 experts: HBM-bound
-    fc1 = (8 * 2 * D * F * 2 + T * K * D * 2 + T * K * F * 2) / 0.5e-3 / 1e9
+    # decode FC1 streams W1 and W3 of all 8 experts and reads x: HBM-bound
+    fc1 = (8 * 2 * D * F * 2 + T * D * 2) / 0.5e-3 / 1e9
     assert out["fc1"]["bound"] == "hbm"
     assert out["fc1"]["achieved"] == pytest.approx(fc1, abs=0.01)
     assert out["fc1"]["frac"] == pytest.approx(fc1 / 8000.0, abs=1e-4)
+    assert out["fc1"]["overhead_bytes"] == (T * K - T) * D * 2 + T * K * F * 2
+    fc2 = 8 * D * F * 2 / 0.25e-3 / 1e9
     assert out["fc2"]["bound"] == "hbm"
-    comb = (T * K * D * 2 + T * D * 2 + T * K * 8) / 1e-5 / 1e9
+    assert out["fc2"]["achieved"] == pytest.approx(fc2, abs=0.01)
+    # the combine's algorithmic bytes are out written once
+    comb = T * D * 2 / 1e-5 / 1e9
     assert out["combine"]["achieved"] == pytest.approx(comb, abs=0.01)
+    assert out["combine"]["overhead_bytes"] == T * K * D * 2 + T * K * 8
