@@ -141,8 +141,23 @@ int moe_combine(const moe_dims_t* dims, const void* y_sorted, const int32_t* inv
                 const float* topk_w, void* out, void* stream);
 
 /* The whole layer: route -> permute -> grouped FFN -> combine, all on `stream`,
- * with no host synchronisation. logits, topk_idx, topk_w, counts, offsets,
- * perm and inv_perm are optional outputs (NULL = kept in ws). */
+ * with no host synchronisation. The sequence of steps follows the pages: the
+ * gating network picks each token's experts and its routing steps (top-k,
+ * per-expert counts, weight normalisation, scatter into per-expert order) run
+ * before the experts (MegaScale-Infer, "3.2 Big-Picture Architecture" item 2
+ * and "Supporting Implementation Details / Fused Kernels"); each expert's rows
+ * go through FC1 then FC2 in tile-aligned token blocks, and the final top-k
+ * sum is a step of its own (MegaFlux, sections 2.1 and 3.1); the expert is the
+ * SwiGLU FFN of Piper, section III-A.
+ *   x [T][d]; wg [E][d]; bias [E] fp32 or NULL; w1, w3 [E][f][d]; w2 [E][d][f];
+ *   out [T][d] output (dtype of x).
+ * logits, topk_idx, topk_w, counts, offsets, perm and inv_perm are optional
+ * outputs with the layouts of moe_route and moe_permute (NULL = kept in ws).
+ * ws: device workspace of at least moe_workspace_bytes(dims) bytes, 256-byte
+ * aligned, owned by the caller; its contents need not be initialised and are
+ * scratch after the call (moe_layer_plan_layout says where the tile plan is).
+ * Errors: MOE_ERR_INVALID (null or misaligned pointer, bad dims),
+ * MOE_ERR_UNSUPPORTED (shape limits above), MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 int moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
                       const void* w1, const void* w3, const void* w2, void* out,
                       float* logits, int32_t* topk_idx, float* topk_w,
@@ -182,6 +197,34 @@ int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* w
                             const void* w1, const void* w3, const void* w2, void* out, float* logits,
                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                             int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+/* Readiness of the fused launch. Its waits need every workgroup of the grid
+ * resident at once (persistent workgroups, MegaFlux section 2.1);
+ * moe_layer_forward_fused checks the occupancy on the host and returns
+ * MOE_ERR_UNSUPPORTED, enqueueing nothing, when the grid cannot all be
+ * resident. Each wait is still bounded: a workgroup that polled a readiness
+ * counter too long (another kernel holding CUs, for instance) gives up, sets
+ * an error word in the workspace and carries on, so the launch always ends but
+ * its outputs are then wrong. moe_fused_status waits for `stream` and copies
+ * that word of the last moe_layer_forward_fused call on `ws` (same dims) to
+ * *flags (host pointer): 0 = every wait was met, so the outputs are valid;
+ * bit 0 set = some wait gave up, discard the outputs. The word is cleared at
+ * the start of every fused call. T == 0 gives *flags = 0. Errors as for the
+ * workspace checks of moe_layer_forward; MOE_ERR_HIP if the copy fails. */
+int moe_fused_status(const moe_dims_t* dims, const void* ws, size_t ws_bytes, int32_t* flags, void* stream);
+
+/* Where the tile plan of a layer call sits in its workspace (host-only query,
+ * no device work). After moe_layer_forward, _packed, _fused or (with the same
+ * n_shared) _shared on `ws`, bytes [mblocks_offset, + 16 * count) of ws hold
+ * the m-blocks the grouped FFN's tiles covered -- tile-aligned token blocks of
+ * at most moe_ffn_block_rows rows, at most one partial block per expert
+ * (MegaFlux, section 3.1) -- and the int32 at count_offset holds count
+ * (<= *max_mblocks). Each m-block is four int32: expert, first sorted row,
+ * rows, and (first m-block of its tile group << 4) | group size (the runs of
+ * up to 8 m-blocks of one expert the GEMM walks together). n_shared = 0 for
+ * layers without shared experts. MOE_ERR_INVALID for bad dims, a null
+ * output pointer or n_shared out of range. */
+int moe_layer_plan_layout(const moe_dims_t* dims, int n_shared, size_t* mblocks_offset, size_t* count_offset,
+                          int64_t* max_mblocks);
 
 /* Expert weights re-laid in the order the grouped FFN streams them (no
  * arithmetic: a permutation of each expert matrix's bf16 values). The expert
@@ -204,6 +247,17 @@ int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* w
  * + ((k%64)/8 ^ ((n%64)/2)%8), element k%8 of the unit. */
 int moe_pack_weights(const moe_dims_t* dims, const void* w1, const void* w3, const void* w2, void* w1p,
                      void* w3p, void* w2p, void* stream);
+/* moe_pack_weights for weights held in the other orientation, input-major:
+ * w1t, w3t [E][d][f] and w2t [E][f][d], i.e. each expert's gate and up
+ * matrices as d x f and its down matrix as f x d, as Piper section III-A
+ * writes them (w1t[e][i][j] = w1[e][j][i], and so on). The outputs are the
+ * same stage-order tensors w1p, w3p [E][f][d], w2p [E][d][f], bitwise equal to
+ * what moe_pack_weights gives for the [out][in] tensors, so the caller never
+ * transposes. Same limits, ownership and errors as moe_pack_weights (plus
+ * MOE_ERR_UNSUPPORTED when E * d/64 * f/64 >= 2^31); the inputs are
+ * 16-byte aligned device buffers that do not overlap the outputs. */
+int moe_pack_weights_transposed(const moe_dims_t* dims, const void* w1t, const void* w3t, const void* w2t,
+                                void* w1p, void* w3p, void* w2p, void* stream);
 int moe_layer_forward_packed(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
                              const void* w1p, const void* w3p, const void* w2p, void* out, float* logits,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,

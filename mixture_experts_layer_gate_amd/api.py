@@ -28,7 +28,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
            "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_pack_weights",
-           "moe_layer_forward_packed"]
+           "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed"]
 
 
 class MoeError(RuntimeError):
@@ -89,6 +89,10 @@ def load_library():
     lib.moe_layer_forward_fused.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_pack_weights.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P]
     lib.moe_layer_forward_packed.argtypes = lib.moe_layer_forward.argtypes
+    lib.moe_pack_weights_transposed.argtypes = lib.moe_pack_weights.argtypes
+    lib.moe_fused_status.argtypes = [_DP, _P, _S, ctypes.POINTER(ctypes.c_int32), _P]
+    lib.moe_layer_plan_layout.argtypes = [_DP, ctypes.c_int, ctypes.POINTER(_S), ctypes.POINTER(_S),
+                                          ctypes.POINTER(ctypes.c_int64)]
     lib.moe_workspace_bytes_shared.restype = _S
     lib.moe_workspace_bytes_shared.argtypes = [_DP, ctypes.c_int]
     lib.moe_layer_forward_shared.argtypes = [_DP, ctypes.c_int] + [_P] * 18 + [_S, _P]
@@ -101,7 +105,9 @@ def load_library():
     lib.moe_probe_hbm_read.argtypes = [_P, _S, _P, _P]
     lib.moe_probe_mfma.argtypes = [ctypes.c_int, _P, _P]
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-               "moe_layer_forward_shared", "moe_layer_backward", "moe_layer_forward_fused",
+               "moe_layer_forward_shared", "moe_layer_backward", "moe_layer_forward_fused", "moe_fused_status",
+               "moe_layer_plan_layout", "moe_pack_weights", "moe_pack_weights_transposed",
+               "moe_layer_forward_packed",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -229,6 +235,51 @@ def pack_weights(dims: Dims, w1, w3, w2, stream=None):
     _check("moe_pack_weights", lib.moe_pack_weights(ctypes.byref(dims.c()), _ptr(w1), _ptr(w3), _ptr(w2),
                                                     _ptr(w1p), _ptr(w3p), _ptr(w2p), _stream(stream)))
     return w1p, w3p, w2p
+
+
+def pack_weights_transposed(dims: Dims, w1t, w3t, w2t, stream=None):
+    """The stage-order tensors of pack_weights from weights held input-major:
+    w1t, w3t [E][d][f] and w2t [E][f][d]. Returns (w1p, w3p, w2p) of shapes
+    [E][f][d], [E][f][d], [E][d][f]."""
+    lib = load_library()
+    for name, w, shp in (("w1t", w1t, (dims.E, dims.d, dims.f)), ("w3t", w3t, (dims.E, dims.d, dims.f)),
+                         ("w2t", w2t, (dims.E, dims.f, dims.d))):
+        _need(w, name, dims.dtype, shp)
+    dev = w1t.device
+    w1p = torch.empty((dims.E, dims.f, dims.d), dtype=dims.dtype, device=dev)
+    w3p = torch.empty((dims.E, dims.f, dims.d), dtype=dims.dtype, device=dev)
+    w2p = torch.empty((dims.E, dims.d, dims.f), dtype=dims.dtype, device=dev)
+    _check("moe_pack_weights_transposed", lib.moe_pack_weights_transposed(
+        ctypes.byref(dims.c()), _ptr(w1t), _ptr(w3t), _ptr(w2t), _ptr(w1p), _ptr(w3p), _ptr(w2p), _stream(stream)))
+    return w1p, w3p, w2p
+
+
+def fused_status(dims: Dims, ws, stream=None) -> int:
+    """Error word of the last fused layer call on workspace ws (0: every readiness wait was met).
+    Waits for the stream."""
+    v = ctypes.c_int32()
+    _check("moe_fused_status", load_library().moe_fused_status(ctypes.byref(dims.c()), _ptr(ws), ws.numel(),
+                                                                ctypes.byref(v), _stream(stream)))
+    return v.value
+
+
+def plan_layout(dims: Dims, n_shared: int = 0):
+    """(m-block list byte offset, count byte offset, max m-blocks) of the tile plan in a layer workspace."""
+    mo, co, mx = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+    _check("moe_layer_plan_layout", load_library().moe_layer_plan_layout(
+        ctypes.byref(dims.c()), n_shared, ctypes.byref(mo), ctypes.byref(co), ctypes.byref(mx)))
+    return mo.value, co.value, mx.value
+
+
+def read_plan(dims: Dims, ws, n_shared: int = 0) -> torch.Tensor:
+    """The m-blocks [count][4] (int32: expert, first sorted row, rows, group info) that the
+    last layer call on ws covered, as a host tensor. Synchronises the device."""
+    mo, co, mx = plan_layout(dims, n_shared)
+    torch.cuda.synchronize()
+    count = int(ws[co:co + 4].cpu().view(torch.int32)[0])
+    if not 0 <= count <= mx:
+        raise RuntimeError(f"m-block count {count} outside [0, {mx}]")
+    return ws[mo:mo + 16 * count].cpu().view(torch.int32).view(count, 4).clone()
 
 
 def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False,

@@ -953,16 +953,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // group takes an FC2 tile only after all of its FC1 tiles are taken, every
 // taken FC1 tile belongs to a running workgroup that finishes it without
 // waiting, and likewise for FC2 tiles under the combine; the grid is a
-// multiple of 8, so every group has workgroups. Each wait is bounded: past
-// the limit the workgroup sets an error word and goes on (the results are
-// then wrong, never a hang). Producers publish with a device-scope release
+// multiple of 8, so every group has workgroups. This needs every workgroup of
+// the grid resident at once (the host checks the occupancy before the launch).
+// Each wait is bounded: past spin_limit polls the workgroup sets bit 0 of the
+// error word and goes on (the results are then wrong, never a hang; the host
+// reads the word through moe_fused_status). Producers publish with a device-scope release
 // (their stores reach the point of coherence of every XCD's L2); consumers
 // take a device-scope acquire before reading.
 // sync words: [0..7] next tile of each group, [8] FC2 tiles stored,
-// [9] error flags, [16 + mb] FC1 tiles of m-block mb stored.
+// [kFusedErrorWord] error flags, [16 + mb] FC1 tiles of m-block mb stored.
 constexpr int kFusedSyncHead = 16;
 [[maybe_unused]] constexpr int kCombineTokens = 8;  // tokens per combine block
-[[maybe_unused]] constexpr int kSpinLimit = 1 << 22;  // polls of a readiness counter before giving up
 
 struct FusedFfnArgs {
   GemmArgs fc1, fc2;
@@ -972,17 +973,19 @@ struct FusedFfnArgs {
   int64_t T, d;
   int k, n_shared;
   int32_t* sync;
+  int spin_limit;  // polls of a readiness counter before giving up; < 0: give up at once
 };
 
-__device__ __forceinline__ void wait_count(int32_t* counter, int target, int32_t* err) {
+__device__ __forceinline__ void wait_count(int32_t* counter, int target, int32_t* err, int spin_limit) {
   if (threadIdx.x == 0) {
     int spins = 0;
     while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
+      if (spins >= spin_limit) {
         __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
+      __builtin_amdgcn_s_sleep(2);
+      ++spins;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
@@ -1012,7 +1015,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
   const int64_t nc = (a.T + kCombineTokens - 1) / kCombineTokens;
   const int nbc1 = static_cast<int>((a.fc1.N + 127) / 128);  // FC1 tiles per m-block
   int32_t* fc2_done = a.sync + 8;
-  int32_t* err = a.sync + 9;
+  int32_t* err = a.sync + kFusedErrorWord;
   int32_t* done1 = a.sync + kFusedSyncHead;
   // group x = blockIdx.x % 8 owns, in every round of G tiles, tiles
   // x*W .. x*W + W-1 (W = G / 8): its share of n tiles, and its j-th tile
@@ -1030,10 +1033,10 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
     if (j < s1) {
       F1::tile(a.fc1, lds, nth(j), [](int) {}, [&](int mb) { publish(done1 + mb); });
     } else if (j < s1 + s2) {
-      F2::tile(a.fc2, lds, nth(j - s1), [&](int mb) { wait_count(done1 + mb, nbc1, err); },
+      F2::tile(a.fc2, lds, nth(j - s1), [&](int mb) { wait_count(done1 + mb, nbc1, err, a.spin_limit); },
                [&](int) { publish(fc2_done); });
     } else if (j < s1 + s2 + sc) {
-      wait_count(fc2_done, static_cast<int>(n2), err);
+      wait_count(fc2_done, static_cast<int>(n2), err, a.spin_limit);
       const int64_t t0 = nth(j - s1 - s2) * kCombineTokens;
       const int64_t nt = a.T - t0 < kCombineTokens ? a.T - t0 : kCombineTokens;
       const int64_t nvec = a.d / 8;
@@ -1104,6 +1107,56 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* w, u3
     const int64_t row = (u / (512 * nk)) * 64 + rr;  // row of the [E*N][K] matrix
     out[u] = *reinterpret_cast<const u32x4_t*>(w + row * K + kt * 64 + 8 * (s ^ ((rr / 2) % 8)));
   }
+}
+
+// The same stage order from an expert-weight tensor stored input-major,
+// Wt [E][K][N] (the d x f / f x d orientation of the expert matrices): one
+// workgroup per 8 KiB block b = (e * N/64 + g) * K/64 + kt of the output. It
+// reads the 64 x 64 sub-matrix Wt[e][64kt ..][64g ..] with coalesced 16-byte
+// row loads into LDS, then writes the block's 512 units in order, unit
+// rr * 8 + s gathering elements 8 * (s ^ ((rr / 2) % 8)) .. +7 of K for output
+// row 64g + rr from an LDS column.
+__global__ __launch_bounds__(256) void pack_weights_t_kernel(const uint16_t* wt, u32x4_t* out, int64_t N, int64_t K) {
+  __shared__ uint16_t t[64][66];  // [k][n]; the 2-element pad spreads a column over the banks
+  const int64_t ng = N / 64, nk = K / 64;
+  const int64_t b = blockIdx.x;
+  const int64_t kt = b % nk, g = (b / nk) % ng, e = b / (nk * ng);
+  const uint16_t* src = wt + (e * K + kt * 64) * N + g * 64;
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    const int r = c / 8, q = c % 8;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(r) * N + q * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[r][q * 8 + 2 * i] = static_cast<uint16_t>(v[i] & 0xffffu);
+      t[r][q * 8 + 2 * i + 1] = static_cast<uint16_t>(v[i] >> 16);
+    }
+  }
+  __syncthreads();
+  u32x4_t* dst = out + b * 512;
+  for (int u = threadIdx.x; u < 512; u += 256) {
+    const int sl = u % 8, rr = u / 8;
+    const int k0 = 8 * (sl ^ ((rr / 2) % 8));
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = static_cast<uint32_t>(t[k0 + 2 * i][rr]) | (static_cast<uint32_t>(t[k0 + 2 * i + 1][rr]) << 16);
+    dst[u] = v;
+  }
+}
+
+hipError_t launch_pack_weights_t(const void* w1t, const void* w3t, const void* w2t, void* w1p, void* w3p, void* w2p,
+                                 int64_t E, int64_t d, int64_t f, hipStream_t s) {
+  const void* src[3] = {w1t, w3t, w2t};
+  void* dst[3] = {w1p, w3p, w2p};
+  // (N, K) of each matrix: W1 and W3 map d inputs to f outputs, W2 f inputs to d outputs
+  const int64_t ndim[3] = {f, f, d}, kdim[3] = {d, d, f};
+  for (int m = 0; m < 3; ++m) {
+    const int64_t blocks = E * (ndim[m] / 64) * (kdim[m] / 64);
+    hipLaunchKernelGGL(pack_weights_t_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src[m]), static_cast<u32x4_t*>(dst[m]), ndim[m], kdim[m]);
+    if (hipError_t err = hipGetLastError()) return err;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_pack_weights(const void* w1, const void* w3, const void* w2, void* w1p, void* w3p, void* w2p,
@@ -1305,12 +1358,38 @@ hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, con
 
 size_t fused_sync_words(int64_t max_mb) { return static_cast<size_t>(kFusedSyncHead + max_mb); }
 
-// FC1, FC2 and combine in one launch (bf16). The sync words must be zero on
-// entry. FC2 tiles are 256 or, under the same rule as launch_fc2, 192 columns wide.
+// Grid and FC2 tile width of the fused launch: a multiple of 8 workgroups
+// (every tile group must have workgroups), at most one per CU; FC2 tiles 256
+// or, under the same rule as launch_fc2, 192 columns wide.
+static void fused_shape(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, int64_t* grid, bool* narrow) {
+  const int64_t cus = device_cu_count();
+  *narrow = false;
+  if (est_mb * ((d + 255) / 256) < 2 * cus) {
+    const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
+    const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
+    *narrow = t192 < t256;
+  }
+  int64_t g = std::min<int64_t>(max_mb * ((f + 127) / 128), cus) / 8 * 8;
+  *grid = g < 8 ? 8 : g;
+}
+
+bool ffn_fused_coresident(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f) {
+  int64_t grid;
+  bool narrow;
+  fused_shape(max_mb, est_mb, d, f, &grid, &narrow);
+  int per_cu = 0;
+  const hipError_t e =
+      narrow ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_fused_kernel<192, 4, 2>, 512, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_fused_kernel<256, 2, 4>, 512, 0);
+  return e == hipSuccess && static_cast<int64_t>(per_cu) * device_cu_count() >= grid;
+}
+
+// FC1, FC2 and combine in one launch (bf16). The sync words must be zero on entry.
 hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
                             const void* w2, void* h, void* y, const int4* mblocks, const int32_t* n_mblocks,
                             int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
-                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, hipStream_t s) {
+                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, int spin_limit,
+                            hipStream_t s) {
   FusedFfnArgs a{};
   a.fc1 = GemmArgs{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f, T * k, sh.w1, sh.w3,
                    sh.n > 0 ? sh.E_routed : INT32_MAX};
@@ -1324,16 +1403,10 @@ hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T
   a.k = k;
   a.n_shared = sh.n;
   a.sync = sync;
-  const int64_t cus = device_cu_count();
-  bool narrow = false;
-  if (est_mb * ((d + 255) / 256) < 2 * cus) {
-    const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
-    const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
-    narrow = t192 < t256;
-  }
-  // a multiple of 8 workgroups (every tile group must have workgroups), at most one per CU
-  int64_t grid = std::min<int64_t>(max_mb * ((f + 127) / 128), cus) / 8 * 8;
-  if (grid < 8) grid = 8;
+  a.spin_limit = spin_limit;
+  int64_t grid;
+  bool narrow;
+  fused_shape(max_mb, est_mb, d, f, &grid, &narrow);
   if (narrow)
     hipLaunchKernelGGL((ffn_fused_kernel<192, 4, 2>), dim3(grid), dim3(512), 0, s, a);
   else

@@ -77,17 +77,27 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
 // re-laid within its own E x N x K footprint (bf16, N, K multiples of 64).
 hipError_t launch_pack_weights(const void* w1, const void* w3, const void* w2, void* w1p, void* w3p, void* w2p,
                                int64_t E, int64_t d, int64_t f, hipStream_t s);
+// The same stage order from input-major weights w1t, w3t [E][d][f], w2t [E][f][d].
+hipError_t launch_pack_weights_t(const void* w1t, const void* w3t, const void* w2t, void* w1p, void* w3p, void* w2p,
+                                 int64_t E, int64_t d, int64_t f, hipStream_t s);
 // bytes of the split-K partial buffer a forward FFN of this shape can use (0:
 // its launches never split)
 size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, int64_t f);
 
 // FC1, FC2 and the combine in one persistent launch with device-side
-// readiness counters (bf16). sync: fused_sync_words(max_mb) int32, zero on entry.
+// readiness counters (bf16). sync: fused_sync_words(max_mb) int32, zero on
+// entry; word kFusedErrorWord gets bit 0 set when a readiness wait gave up
+// after spin_limit polls (< 0: at once).
 size_t fused_sync_words(int64_t max_mb);
+constexpr int kFusedErrorWord = 9;
+constexpr int kFusedSpinLimit = 1 << 22;
+// every workgroup of the fused launch for this shape can be resident at once
+bool ffn_fused_coresident(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f);
 hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
                             const void* w2, void* h, void* y, const int4* mblocks, const int32_t* n_mblocks,
                             int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
-                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, hipStream_t s);
+                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, int spin_limit,
+                            hipStream_t s);
 
 // Weighted combine.
 // With n_shared > 0, out[t] also adds y[T*k + s*T + t] for s ascending.

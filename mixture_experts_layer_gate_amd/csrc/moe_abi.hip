@@ -111,15 +111,19 @@ int64_t ffn_rows(const moe_dims_t* dm, int n_shared) { return dm->T * dm->k + st
 struct FfnWs {
   int4* mblocks; int32_t* n_mblocks; void* h; int64_t max_mb; int32_t* sync;
   float* partial; size_t partial_bytes;  // split-K parts of FC1/FC2 tiles (none when no launch can split)
+  size_t mblocks_off, n_mblocks_off, sync_off;  // byte offsets of the pieces from the start of this region
 };
 int gemm_regime(const moe_dims_t* dm);
 size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   Carver c(ws);
   FfnWs r{};
   r.max_mb = max_mblocks(ffn_rows(dm, n_shared), dm->E + n_shared);
+  r.mblocks_off = c.off;
   r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
+  r.n_mblocks_off = c.off;
   r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
   r.h = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->f);
+  r.sync_off = c.off;
   r.sync = c.take<int32_t>(sizeof(int32_t) * fused_sync_words(r.max_mb));  // fused FFN's readiness counters
   r.partial_bytes = splitk_partial_bytes(dm->dtype, gemm_regime(dm), r.max_mb, dm->d, dm->f);
   r.partial = r.partial_bytes ? c.take<float>(r.partial_bytes) : nullptr;
@@ -130,6 +134,7 @@ size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
 struct LayerWs {
   float* logits; int32_t* idx; float* w; int32_t* counts; int32_t* offsets; int32_t* perm;
   int32_t* inv; void* y; void* sub;  // sub: start of the permute / ffn scratch (shared)
+  size_t sub_off;                    // byte offset of sub from the start of the workspace
 };
 size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out, int n_shared = 0) {
   Carver c(ws);
@@ -145,6 +150,7 @@ size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out, int n_shared = 0) 
   r.y = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->d);
   const size_t pws = permute_ws(dm, nullptr, nullptr), fws = ffn_ws(dm, nullptr, nullptr, n_shared);
   const size_t sub = pws > fws ? pws : fws;
+  r.sub_off = c.off;
   r.sub = c.take<char>(sub);
   if (out) *out = r;
   return c.off;
@@ -315,16 +321,24 @@ int bwd_shape_ok(const moe_dims_t* dm) {
 
 // The layer: route, dispatch, grouped FFN over the routed (and shared) rows, combine.
 // FC1, FC2 and combine as one persistent launch (the plan already in fw).
+// Polls of a readiness counter before the fused launch gives up (the
+// MOE_FUSED_SPIN_LIMIT environment switch overrides it; a negative value makes
+// every wait give up at once, which tests use to check that the failure is reported).
+int fused_spin_limit() {
+  if (const char* env = getenv("MOE_FUSED_SPIN_LIMIT")) return atoi(env);
+  return kFusedSpinLimit;
+}
+
 int do_ffn_fused(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* inv_perm,
                  const float* topk_w, const void* w1, const void* w3, const void* w2, void* y, void* out,
                  const FfnWs& fw, const SharedExperts& sh, hipStream_t s) {
+  const int64_t est_mb = expected_mblocks(dm, 256, fw.max_mb, sh.n);
   if (int st = hip_status(launch_fill_zero(reinterpret_cast<float*>(fw.sync),
                                            static_cast<int64_t>(fused_sync_words(fw.max_mb)), s)))
     return st;
   StageScope sc(MOE_STAGE_FFN_FUSED, s);
   return hip_status(launch_ffn_fused(x, perm, dm->k, dm->T, w1, w3, w2, fw.h, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
-                                     expected_mblocks(dm, 256, fw.max_mb, sh.n), dm->d, dm->f, inv_perm, topk_w, out,
-                                     fw.sync, sh, s));
+                                     est_mb, dm->d, dm->f, inv_perm, topk_w, out, fw.sync, sh, fused_spin_limit(), s));
 }
 
 int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, const void* wg, const float* bias,
@@ -341,6 +355,12 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
   if (fused && dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
   if (ws_bytes < layer_ws(dm, nullptr, nullptr, sh.n)) return MOE_ERR_WORKSPACE;
+  if (fused) {
+    // the fused launch's readiness waits need every workgroup resident at once
+    const int64_t max_mb = max_mblocks(ffn_rows(dm, sh.n), dm->E + sh.n);
+    if (!ffn_fused_coresident(max_mb, expected_mblocks(dm, 256, max_mb, sh.n), dm->d, dm->f))
+      return MOE_ERR_UNSUPPORTED;
+  }
   LayerWs lw{};
   layer_ws(dm, ws, &lw, sh.n);
   if (!logits) logits = lw.logits;
@@ -503,6 +523,18 @@ int moe_pack_weights(const moe_dims_t* dm, const void* w1, const void* w3, const
       launch_pack_weights(w1, w3, w2, w1p, w3p, w2p, dm->E, dm->d, dm->f, static_cast<hipStream_t>(stream)));
 }
 
+int moe_pack_weights_transposed(const moe_dims_t* dm, const void* w1t, const void* w3t, const void* w2t, void* w1p,
+                                void* w3p, void* w2p, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (int st = ffn_shape_ok(dm)) return st;
+  if (!ok16(w1t) || !ok16(w3t) || !ok16(w2t) || !ok16(w1p) || !ok16(w3p) || !ok16(w2p)) return MOE_ERR_INVALID;
+  // one workgroup per 8 KiB output block: the block count of one matrix must fit the grid
+  if (int64_t(dm->E) * (dm->d / 64) * (dm->f / 64) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(
+      launch_pack_weights_t(w1t, w3t, w2t, w1p, w3p, w2p, dm->E, dm->d, dm->f, static_cast<hipStream_t>(stream)));
+}
+
 int moe_layer_forward_packed(const moe_dims_t* dm, const void* x, const void* wg, const float* bias, const void* w1p,
                              const void* w3p, const void* w2p, void* out, float* logits, int32_t* topk_idx,
                              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
@@ -519,6 +551,41 @@ int moe_layer_forward_fused(const moe_dims_t* dm, const void* x, const void* wg,
                             int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
                    perm, inv_perm, ws, ws_bytes, stream, true);
+}
+
+int moe_fused_status(const moe_dims_t* dm, const void* ws, size_t ws_bytes, int32_t* flags, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (!flags) return MOE_ERR_INVALID;
+  *flags = 0;
+  if (dm->T == 0) return MOE_OK;  // the layer call enqueued nothing
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < layer_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  LayerWs lw{};
+  layer_ws(dm, const_cast<void*>(ws), &lw);
+  FfnWs fw{};
+  ffn_ws(dm, lw.sub, &fw);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, fw.sync + kFusedErrorWord, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_ERR_HIP;
+  *flags = v;
+  return MOE_OK;
+}
+
+int moe_layer_plan_layout(const moe_dims_t* dm, int n_shared, size_t* mblocks_offset, size_t* count_offset,
+                          int64_t* max_mblocks_out) {
+  if (int st = check_dims(dm)) return st;
+  if (n_shared < 0 || dm->E + n_shared > 1024 || !mblocks_offset || !count_offset || !max_mblocks_out)
+    return MOE_ERR_INVALID;
+  LayerWs lw{};
+  layer_ws(dm, nullptr, &lw, n_shared);
+  FfnWs fw{};
+  ffn_ws(dm, nullptr, &fw, n_shared);
+  *mblocks_offset = lw.sub_off + fw.mblocks_off;
+  *count_offset = lw.sub_off + fw.n_mblocks_off;
+  *max_mblocks_out = fw.max_mb;
+  return MOE_OK;
 }
 
 size_t moe_workspace_bytes_shared(const moe_dims_t* dm, int n_shared) {

@@ -87,3 +87,67 @@ def assert_routing_equal(gpu: dict, ref: dict, names=("logits", "topk_idx", "cou
 def make_case(cfg, seed=0, device="cuda"):
     inp = moe_inputs.make_layer_inputs(cfg, seed, device)
     return inp
+
+
+class OneExpert:
+    """A single expert's matrix presented as a one-expert stack (shape [1, ...], index 0)."""
+
+    def __init__(self, m: np.ndarray):
+        self.m = m
+        self.shape = (1,) + tuple(m.shape)
+
+    def __getitem__(self, e):
+        assert int(e) == 0
+        return self.m
+
+
+def oracle_outputs_threaded(h: dict, w1, w3, w2, idx, w, tokens, k: int, dtype: str, threads=16):
+    """out[t] for the listed tokens (all tokens when tokens is None), computed by the oracle's
+    own functions: each expert's rows through oracle.expert_ffn_sorted (one call per expert,
+    the experts spread over threads), then oracle.combine over the (token, slot) rows.
+    w1, w3, w2: host arrays [E][...] in the oracle's format. Returns float64 [len(tokens), d]."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    T = idx.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    sel = idx[tokens]                                  # [n, k] experts of the sampled tokens
+    # assignment a = r*k + j of sampled token r, slot j; its row of x is tokens[r]
+    flat = sel.reshape(-1).astype(np.int64)
+    x_rows = h["x"][tokens]
+    y = np.zeros((flat.size, x_rows.shape[1]), np.float64)
+
+    def one(e):
+        a = np.flatnonzero(flat == e)                  # assignments of expert e, in order
+        ye = oracle.expert_ffn_sorted(x_rows, a.astype(np.int32), np.array([0, a.size], np.int32),
+                                      OneExpert(w1[e]), OneExpert(w3[e]), OneExpert(w2[e]), k, dtype)
+        y[a] = ye
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, sorted(set(flat.tolist()))))
+    inv = np.arange(flat.size, dtype=np.int32)        # row r*k + j holds (token r, slot j)
+    return oracle.combine(y, inv, np.asarray(w)[tokens], k)
+
+
+def check_plan(blocks: np.ndarray, counts, offsets, beta: int, n_rows: int):
+    """Invariants of a tile plan (MegaFlux, section 3.1): every sorted row of every expert
+    is covered by exactly one m-block of that expert, every block has 1..beta rows and at
+    most one per expert has fewer than beta, the rows add up to n_rows, and the tile-group
+    field names a run of at most 8 m-blocks of one expert that contains the block."""
+    blocks = np.asarray(blocks, np.int64).reshape(-1, 4)
+    counts = np.asarray(counts, np.int64)
+    offsets = np.asarray(offsets, np.int64)
+    E = counts.size
+    assert blocks[:, 2].sum() == n_rows, "rows do not add up to T*k"
+    cover = np.zeros(n_rows, np.int64)
+    partial = np.zeros(E, np.int64)
+    for i, (e, r0, rows, info) in enumerate(blocks.tolist()):
+        assert 0 <= e < E, f"block {i}: expert {e}"
+        assert 1 <= rows <= beta, f"block {i}: {rows} rows"
+        assert offsets[e] <= r0 and r0 + rows <= offsets[e + 1], f"block {i} leaves expert {e}'s rows"
+        cover[r0:r0 + rows] += 1
+        partial[e] += rows < beta
+        m0, gs = info >> 4, info & 15
+        assert 1 <= gs <= 8 and m0 <= i < m0 + gs <= len(blocks), f"block {i}: group ({m0}, {gs})"
+        assert (blocks[m0:m0 + gs, 0] == e).all(), f"block {i}: group spans experts"
+    assert (cover == 1).all(), f"rows covered {cover.min()}..{cover.max()} times"
+    assert (partial <= 1).all(), f"experts with {partial.max()} partial blocks"
+    assert len(blocks) == sum(-(-int(c) // beta) for c in counts)

@@ -201,3 +201,52 @@ def test_layer_backward_validation():
     need = lib.moe_backward_workspace_bytes(ctypes.byref(_dims(**good)))
     assert need > lib.moe_backward_workspace_bytes(ctypes.byref(_dims(**{**good, "T": 1})))
     assert lib.moe_backward_workspace_bytes(ctypes.byref(_dims(k=0))) == 0
+
+
+def test_plan_layout_inside_the_workspace():
+    """The tile plan's m-block list and count lie inside the layer workspace, 16- and
+    4-byte aligned, and the list holds the most m-blocks any plan of the shape can have:
+    ceil(T*k / 128) + min(T*k, E) (at most one partial block per active expert)."""
+    lib = moe.load_library()
+    for kw, n_shared in ((dict(), 0), (dict(T=8192, d=6144, f=16384, E=8, k=2), 0),
+                         (dict(T=4096, d=7168, f=2048, E=256, k=8), 0), (dict(T=300, E=16, k=4), 2)):
+        dm = _dims(**kw)
+        mo, co, mx = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+        assert lib.moe_layer_plan_layout(ctypes.byref(dm), n_shared, ctypes.byref(mo), ctypes.byref(co),
+                                         ctypes.byref(mx)) == 0
+        rows = dm.T * dm.k + n_shared * dm.T
+        experts = dm.E + n_shared
+        assert mx.value == -(-rows // 128) + min(rows, experts)
+        size = (lib.moe_workspace_bytes(ctypes.byref(dm)) if n_shared == 0
+                else lib.moe_workspace_bytes_shared(ctypes.byref(dm), n_shared))
+        assert mo.value % 16 == 0 and co.value % 4 == 0
+        assert mo.value + 16 * mx.value <= co.value + 4 <= size
+    bad = ctypes.c_size_t()
+    assert lib.moe_layer_plan_layout(ctypes.byref(_dims(k=0)), 0, ctypes.byref(bad), ctypes.byref(bad),
+                                     ctypes.byref(ctypes.c_int64())) == 1
+    assert lib.moe_layer_plan_layout(ctypes.byref(_dims()), 0, None, ctypes.byref(bad),
+                                     ctypes.byref(ctypes.c_int64())) == 1
+    assert lib.moe_layer_plan_layout(ctypes.byref(_dims()), 1017, ctypes.byref(bad), ctypes.byref(bad),
+                                     ctypes.byref(ctypes.c_int64())) == 1
+
+
+@needs_no_gpu
+def test_fused_status_validation():
+    """moe_fused_status checks its arguments on the host; an empty batch reads nothing."""
+    lib = moe.load_library()
+    flags = ctypes.c_int32(7)
+    assert lib.moe_fused_status(ctypes.byref(_dims()), A, 1 << 30, None, None) == 1
+    assert lib.moe_fused_status(ctypes.byref(_dims()), A, 16, ctypes.byref(flags), None) == 3
+    assert lib.moe_fused_status(ctypes.byref(_dims()), A + 64, 1 << 30, ctypes.byref(flags), None) == 1
+    assert lib.moe_fused_status(ctypes.byref(_dims(T=0)), None, 0, ctypes.byref(flags), None) == 0
+    assert flags.value == 0
+
+
+@needs_no_gpu
+def test_pack_weights_transposed_validation():
+    lib = moe.load_library()
+    dm = _dims()
+    assert lib.moe_pack_weights_transposed(ctypes.byref(_dims(dtype=0)), A, A, A, A, A, A, None) == 2
+    assert lib.moe_pack_weights_transposed(ctypes.byref(_dims(d=100)), A, A, A, A, A, A, None) == 2
+    assert lib.moe_pack_weights_transposed(ctypes.byref(dm), None, A, A, A, A, A, None) == 1
+    assert lib.moe_pack_weights_transposed(ctypes.byref(dm), A, A, A, A, A, A + 2, None) == 1

@@ -50,6 +50,8 @@ def _both(cfg_or_shape, seed=0):
         out, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], ws=ws,
                                    return_routing=True, fused=True)
         torch.cuda.synchronize()
+        # every readiness wait of the launch was met: its outputs are valid
+        assert moe.fused_status(dims, ws) == 0
         outs.append(out.clone())
     return inp, ref, outs, r
 
@@ -88,6 +90,33 @@ def test_fused_full_size_bitwise(name):
     for o in outs:
         assert torch.equal(o, ref)
     _say("  bitwise equal to the separate launches, twice")
+
+
+def test_fused_reports_a_wait_that_gave_up(monkeypatch):
+    """A readiness wait that gives up is reported through moe_fused_status. The failure is
+    forced from the host: MOE_FUSED_SPIN_LIMIT=-1 makes every wait that finds its counter
+    short give up at once (the kernel then reads operands that may not be stored yet, so
+    only the status is checked); a normal call on the same workspace clears the word again
+    and gives the separate launches' bits."""
+    shape = (1000, 512, 1024, 8, 2, 0.0)
+    _say(f"case fused wait failure reported {shape}")
+    T, d, f, E, k, s = shape
+    inp = moe_inputs.random_inputs(T, d, f, E, k, "bf16", s, 3, device="cuda")
+    dims = moe.Dims(T, d, f, E, k, torch.bfloat16)
+    ref = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    ws = moe.make_workspace(dims)
+    args = (dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    monkeypatch.setenv("MOE_FUSED_SPIN_LIMIT", "-1")
+    flags = []
+    for _ in range(3):  # some combine block waits on FC2 tiles still running in every launch of this size
+        moe.layer_forward(*args, ws=ws, fused=True)
+        flags.append(moe.fused_status(dims, ws))
+    _say(f"  status words with no waiting: {flags}")
+    assert any(v & 1 for v in flags)
+    monkeypatch.delenv("MOE_FUSED_SPIN_LIMIT")
+    out = moe.layer_forward(*args, ws=ws, fused=True)
+    assert moe.fused_status(dims, ws) == 0
+    assert torch.equal(out, ref)
 
 
 def test_fused_rejects_fp32():

@@ -122,3 +122,55 @@ def test_packed_full_size_bitwise(name):
     got = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], None, None, None, packed=packed)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+TRANSPOSED_SHAPES = [
+    # T, d, f, E, k: d and f of every multiple of 64 the two matrices' blocks can take
+    (300, 192, 320, 3, 2),
+    (64, 1024, 2048, 8, 2),
+    (7, 7168, 2048, 4, 2),    # the DeepSeek-V3 expert shape: W2 blocks from 2048-wide rows
+]
+
+
+@pytest.mark.parametrize("shape", TRANSPOSED_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}".format(*s))
+def test_pack_from_input_major_weights(shape):
+    """moe_pack_weights_transposed on the d x f / f x d orientation ([E][d][f], [E][f][d]) gives
+    the same stage-order bytes as moe_pack_weights on the [out][in] tensors, and the packed
+    layer computes the stored-weight layer's bits."""
+    T, d, f, E, k = shape
+    _say(f"case pack transposed {shape}")
+    inp = moe_inputs.random_inputs(T, d, f, E, k, "bf16", 1.0, seed=24, device="cuda")
+    dims = moe.Dims(T, d, f, E, k, torch.bfloat16)
+    a = moe.pack_weights(dims, inp["w1"], inp["w3"], inp["w2"])
+    w1t, w3t, w2t = (inp[n].transpose(1, 2).contiguous() for n in ("w1", "w3", "w2"))
+    b = moe.pack_weights_transposed(dims, w1t, w3t, w2t)
+    torch.cuda.synchronize()
+    for name, pa, pb in zip(("w1", "w3", "w2"), a, b):
+        assert torch.equal(pa.view(torch.int16), pb.view(torch.int16)), name
+    if T * d * f <= 300 * 192 * 320:
+        for name, pb in zip(("w1", "w3", "w2"), b):
+            assert np.array_equal(to_numpy(pb, "bf16"), _layout(to_numpy(inp[name], "bf16"))), name
+    ref = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    got = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], None, None, None, packed=b)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.timeout(600)
+def test_pack_from_input_major_weights_full_size():
+    """The Mixtral-8x22B prefill layer from input-major weights: packed bytes and layer output
+    bitwise equal to those from the [out][in] tensors."""
+    cfg = moe_inputs.config("mixtral_prefill_skew")
+    _say("case pack transposed full mixtral_prefill_skew")
+    inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    dims = moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype)
+    a = moe.pack_weights(dims, inp["w1"], inp["w3"], inp["w2"])
+    w1t, w3t, w2t = (inp[n].transpose(1, 2).contiguous() for n in ("w1", "w3", "w2"))
+    b = moe.pack_weights_transposed(dims, w1t, w3t, w2t)
+    torch.cuda.synchronize()
+    for name, pa, pb in zip(("w1", "w3", "w2"), a, b):
+        assert torch.equal(pa.view(torch.int16), pb.view(torch.int16)), name
+    got_a = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], None, None, None, packed=a)
+    got_b = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], None, None, None, packed=b)
+    torch.cuda.synchronize()
+    assert torch.equal(got_a, got_b)

@@ -3,7 +3,9 @@
 Bar: routing indices, counts, offsets, permutations and gate logits bit-exact;
 combine weights within 1e-5 relative; outputs within max |g - r| / max(|r|, rms(r))
 <= 2e-2. Small shapes are compared element by element over every output; the
-full-size workloads compare all routing arrays and a sample of output rows.
+full-size workloads compare all routing arrays, check the GPU's tile plan
+against its invariants, and compare every output row (decode and DBRX shapes)
+or one token per m-block (prefill and DeepSeek shapes).
 """
 import sys
 
@@ -15,8 +17,8 @@ import moe_inputs
 import oracle
 import mixture_experts_layer_gate_amd as moe
 from conftest import to_numpy
-from parity import (OUT_TOL, LazyExperts, assert_routing_equal, gpu_float, host_inputs, oracle_routing,
-                    rel_err)
+from parity import (OUT_TOL, LazyExperts, assert_routing_equal, check_plan, gpu_float, host_inputs,
+                    oracle_outputs_threaded, oracle_routing, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -344,35 +346,56 @@ def test_shared_experts_layer(monkeypatch, shape, path):
     assert err <= OUT_TOL
 
 
-FULL = ["mixtral_decode", "mixtral_decode_t1", "mixtral_decode_t16", "dbrx_bal", "dbrx_zipf", "mixtral_prefill_skew", "mixtral_prefill_bal",
-        "deepseek_skew", "deepseek_bal"]
+# Full-size workloads. Routing arrays and gate logits are compared bit for bit;
+# the tile plan the GPU used is read back from the workspace and checked against
+# the plan invariants; outputs are compared element by element with the oracle
+# on every row where the oracle takes seconds (decode and DBRX shapes), and at the
+# prefill and DeepSeek shapes on every column of one token per m-block of the
+# GPU's own plan (the token of the block's last row), so that every active
+# expert, every m-block and every partial block is checked.
+FULL_EVERY_ROW = ["mixtral_decode", "mixtral_decode_t1", "mixtral_decode_t16", "dbrx_bal", "dbrx_zipf"]
+FULL_PER_MBLOCK = ["mixtral_prefill_skew", "mixtral_prefill_bal", "deepseek_skew", "deepseek_bal"]
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", FULL)
+def _host(t, dtype):
+    return to_numpy(t, dtype)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL_EVERY_ROW + FULL_PER_MBLOCK)
 def test_full_size_workload(name):
     cfg = moe_inputs.config(name)
     _say(f"case full {name}: generating inputs on the GPU")
     inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
+    dims = _dims(cfg)
+    ws = moe.make_workspace(dims)
     torch.cuda.synchronize()
     _say("  running the layer")
-    out, r = _run_layer(cfg, inp)
+    out, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], ws=ws,
+                               return_routing=True)
+    torch.cuda.synchronize()
+    plan = moe.read_plan(dims, ws).numpy()
     h = host_inputs(inp, cfg.dtype)
     _say("  oracle routing")
     ref = oracle_routing(h, cfg.k, cfg.dtype)
     assert_routing_equal(r, ref)
     counts = ref["counts"]
     _say(f"  routing bit-exact; counts min {counts.min()} max {counts.max()} active {(counts > 0).sum()}")
-    # sampled output rows: first, last and a spread, fewer when experts are many
-    nsamp = 8 if cfg.E > 64 else 24
-    toks = np.unique(np.linspace(0, cfg.T - 1, nsamp).astype(np.int64))
-    w1, w3, w2 = (LazyExperts(inp[n], cfg.dtype) for n in ("w1", "w3", "w2"))
-    ro = oracle.token_outputs(h["x"], ref["topk_idx"], ref["topk_w"], w1, w3, w2, toks, cfg.dtype)
-    got = gpu_float(out[torch.from_numpy(toks).cuda()])
-    err = rel_err(got, ro)
-    _say(f"  sampled out rel_err={err:.3e} over {toks.size} tokens")
-    assert err <= OUT_TOL
+    beta = moe.ffn_block_rows(dims)
+    check_plan(plan, counts, ref["offsets"], beta, cfg.T * cfg.k)
+    _say(f"  plan: {len(plan)} m-blocks of <= {beta} rows, invariants hold")
     assert torch.isfinite(out.float()).all()
+    w1, w3, w2 = (_host(inp[n], cfg.dtype) for n in ("w1", "w3", "w2"))
+    if name in FULL_EVERY_ROW:
+        toks = None
+    else:
+        last_rows = plan[:, 1] + plan[:, 2] - 1
+        toks = np.unique(ref["perm"][last_rows] // cfg.k)
+    want = oracle_outputs_threaded(h, w1, w3, w2, ref["topk_idx"], ref["topk_w"], toks, cfg.k, cfg.dtype)
+    got = gpu_float(out) if toks is None else gpu_float(out[torch.from_numpy(toks).cuda()])
+    err = rel_err(got, want)
+    _say(f"  out rel_err={err:.3e} over {got.shape[0]} of {cfg.T} tokens, all {cfg.d} columns")
+    assert err <= OUT_TOL
 
 
 def test_measurement_probes_run():
