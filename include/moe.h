@@ -63,7 +63,8 @@ typedef enum {
   MOE_ERR_INVALID = 1,      /* null pointer, bad shape, misaligned pointer */
   MOE_ERR_UNSUPPORTED = 2,  /* valid shape the GPU path does not run (see limits) */
   MOE_ERR_WORKSPACE = 3,    /* ws_bytes below what the call needs */
-  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+  MOE_ERR_HIP = 4,          /* a HIP launch or runtime call failed */
+  MOE_ERR_SCRATCH = 5       /* moe_layer_forward_noalloc: the shape needs more than its static scratch */
 } moe_status_t;
 
 typedef struct {
@@ -163,6 +164,25 @@ int moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg, con
                       float* logits, int32_t* topk_idx, float* topk_w,
                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same launches, arguments (minus ws and ws_bytes), outputs and bits as
+ * moe_layer_forward, with the workspace taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. The call allocates nothing: no hipMalloc or
+ * allocating library routine. Shapes whose workspace
+ * (moe_workspace_bytes) exceeds that size are refused with MOE_ERR_SCRATCH
+ * before anything is enqueued; 64 MiB covers a Mixtral-8x22B-shaped decode
+ * step of up to several hundred tokens. Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (on different streams, or
+ * from different threads) race and give undefined results; serialise them.
+ * The first call on a device looks up the array's address there. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+                              const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, void* stream);
 
 /* Shared (always-active) experts: a layer whose tokens each also pass through
  * n_shared SwiGLU experts of the same sizes outside the routing (Piper, Table III

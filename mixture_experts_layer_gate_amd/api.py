@@ -28,7 +28,11 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
            "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_pack_weights",
-           "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed"]
+           "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed",
+           "moe_layer_forward_noalloc"]
+
+# Bytes of the static scratch moe_layer_forward_noalloc uses (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -93,6 +97,7 @@ def load_library():
     lib.moe_fused_status.argtypes = [_DP, _P, _S, ctypes.POINTER(ctypes.c_int32), _P]
     lib.moe_layer_plan_layout.argtypes = [_DP, ctypes.c_int, ctypes.POINTER(_S), ctypes.POINTER(_S),
                                           ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_layer_forward_noalloc.argtypes = [_DP] + [_P] * 15
     lib.moe_workspace_bytes_shared.restype = _S
     lib.moe_workspace_bytes_shared.argtypes = [_DP, ctypes.c_int]
     lib.moe_layer_forward_shared.argtypes = [_DP, ctypes.c_int] + [_P] * 18 + [_S, _P]
@@ -107,7 +112,7 @@ def load_library():
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
                "moe_layer_forward_shared", "moe_layer_backward", "moe_layer_forward_fused", "moe_fused_status",
                "moe_layer_plan_layout", "moe_pack_weights", "moe_pack_weights_transposed",
-               "moe_layer_forward_packed",
+               "moe_layer_forward_packed", "moe_layer_forward_noalloc",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -280,6 +285,27 @@ def read_plan(dims: Dims, ws, n_shared: int = 0) -> torch.Tensor:
     if not 0 <= count <= mx:
         raise RuntimeError(f"m-block count {count} outside [0, {mx}]")
     return ws[mo:mo + 16 * count].cpu().view(torch.int32).view(count, 4).clone()
+
+
+def layer_forward_noalloc(dims: Dims, x, wg, bias, w1, w3, w2, out, routing=None, stream=None):
+    """moe_layer_forward_noalloc: the layer with the library's static scratch as workspace.
+    out and the optional routing outputs (a dict of preallocated tensors under the names
+    layer_forward(..., return_routing=True) returns) are the caller's; nothing is allocated."""
+    lib = load_library()
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    _need(wg, "wg", dims.dtype, (dims.E, dims.d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (dims.E,))
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    _need(out, "out", dims.dtype, (dims.T, dims.d))
+    g = (routing or {}).get
+    _check("moe_layer_forward_noalloc", lib.moe_layer_forward_noalloc(
+        ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+        _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")), _ptr(g("counts")), _ptr(g("offsets")),
+        _ptr(g("perm")), _ptr(g("inv_perm")), _stream(stream)))
+    return out
 
 
 def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False,

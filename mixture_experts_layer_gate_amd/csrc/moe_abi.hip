@@ -158,6 +158,33 @@ size_t layer_ws(const moe_dims_t* dm, void* ws, LayerWs* out, int n_shared = 0) 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// ---------------- static scratch of the allocation-free entry point ----------------
+// One copy of this array per GPU the library runs on, held until the process
+// ends. Host code never passes its name to a kernel or a copy (on the host the
+// name is only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current, on the first moe_layer_forward_noalloc call there.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % kAlign == 0, "whole 256-byte pieces");
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+  std::mutex mu;
+  void* ptr[64] = {};
+} g_scratch;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch.ptr[dev] = p;
+  }
+  *out = g_scratch.ptr[dev];
+  return MOE_OK;
+}
+
 // Backward scratch. P = T*k sorted rows; pp = padded columns of the transposed
 // activations (every expert's rows rounded up to a multiple of 64).
 struct BwdWs {
@@ -430,6 +457,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "shape not supported by the GPU path (needs d % 64 == 0, f % 64 == 0, and x, h and one expert matrix under 4 GiB)";
     case MOE_ERR_WORKSPACE: return "workspace too small (see moe_workspace_bytes)";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_SCRATCH: return "the call needs more scratch than moe_layer_forward_noalloc's static buffer holds (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -511,6 +539,20 @@ int moe_layer_forward(const moe_dims_t* dm, const void* x, const void* wg, const
                       int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
                    perm, inv_perm, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_noalloc(const moe_dims_t* dm, const void* x, const void* wg, const float* bias,
+                              const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  // the workspace moe_layer_forward would need must fit the static scratch
+  if (layer_ws(dm, nullptr, nullptr) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (int st = scratch_address(&ws)) return st;
+  return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
+                   perm, inv_perm, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_pack_weights(const moe_dims_t* dm, const void* w1, const void* w3, const void* w2, void* w1p, void* w3p,

@@ -250,3 +250,23 @@ def test_pack_weights_transposed_validation():
     assert lib.moe_pack_weights_transposed(ctypes.byref(_dims(d=100)), A, A, A, A, A, A, None) == 2
     assert lib.moe_pack_weights_transposed(ctypes.byref(dm), None, A, A, A, A, A, None) == 1
     assert lib.moe_pack_weights_transposed(ctypes.byref(dm), A, A, A, A, A, A + 2, None) == 1
+
+
+@needs_no_gpu
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    """moe_layer_forward_noalloc refuses, before any device call, a shape whose workspace
+    exceeds the static scratch (MOE_ERR_SCRATCH = 5), and bad dims first."""
+    lib = moe.load_library()
+
+    def call(**kw):
+        return lib.moe_layer_forward_noalloc(ctypes.byref(_dims(**kw)), A, A, None, A, A, A, A, None, None, None,
+                                             None, None, None, None, None)
+    prefill = dict(T=8192, d=6144, f=16384, E=8, k=2)
+    assert lib.moe_workspace_bytes(ctypes.byref(_dims(**prefill))) > api.NOALLOC_SCRATCH_BYTES
+    assert call(**prefill) == 5
+    assert call(k=0) == 1
+    assert call(T=0) == 0
+    assert b"static" in lib.moe_status_string(5)
+    # a decode step of the Mixtral-8x22B shape fits
+    assert lib.moe_workspace_bytes(ctypes.byref(_dims(T=256, d=6144, f=16384, E=8, k=2))) <= \
+        api.NOALLOC_SCRATCH_BYTES
