@@ -59,15 +59,37 @@ struct StageScope {
 };
 
 // ---------------- validation ----------------
+// a * b * c < lim, computed without overflow (a, b, c >= 0)
+bool product_below(int64_t a, int64_t b, int64_t c, int64_t lim) {
+  return static_cast<__int128>(a) * b * c < static_cast<__int128>(lim);
+}
+
 int check_dims(const moe_dims_t* dm) {
   if (!dm) return MOE_ERR_INVALID;
   if (dm->T < 0 || dm->d < 1 || dm->f < 1) return MOE_ERR_INVALID;
   if (dm->d >= (int64_t(1) << 31) || dm->f >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
   if (dm->k < 1 || dm->E < dm->k || dm->E > 1024) return MOE_ERR_INVALID;
   if (dm->dtype != MOE_DTYPE_F32 && dm->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  // T*k and T*E below 2^31 (k, E >= 1, so T first: the products then fit in 64 bits)
+  if (dm->T >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
   if (dm->T * dm->k >= (int64_t(1) << 31) || dm->T * dm->E >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
+  // every workspace piece ([T*k][max(d, f)] fp32 at most, and the backward's
+  // transposed activations) stays far inside size_t
+  const int64_t wide = dm->d > dm->f ? dm->d : dm->f;
+  if (!product_below(dm->T * dm->k + 64 * int64_t(dm->E) + 64, 2 * wide, 8, int64_t(1) << 60)) return MOE_ERR_INVALID;
   return MOE_OK;
 }
+// shared experts: 1 <= n_shared, E + n_shared <= 1024, T * (k + n_shared) < 2^31 and
+// the workspace pieces of those rows inside size_t (dims already checked)
+int check_shared(const moe_dims_t* dm, int n_shared) {
+  if (n_shared < 1 || dm->E + n_shared > 1024) return MOE_ERR_INVALID;
+  const int64_t rows = dm->T * (dm->k + int64_t(n_shared)), wide = dm->d > dm->f ? dm->d : dm->f;
+  if (rows >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
+  if (!product_below(rows + 64 * int64_t(dm->E + n_shared) + 64, 2 * wide, 8, int64_t(1) << 60))
+    return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
 int elt_bytes(const moe_dims_t* dm) { return dm->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 bool ok16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool ok4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
@@ -326,8 +348,8 @@ int ffn_shape_ok(const moe_dims_t* dm, int n_shared = 0) {
   // offsets, and points padding rows one row past the end of x (or of a
   // 256-row block of h), so those ends plus one row must stay below 4 GiB too
   const int64_t lim = int64_t(1) << 32, eb = elt_bytes(dm);
-  if ((dm->T + 1) * dm->d * eb >= lim || dm->f * dm->d * eb >= lim || ffn_rows(dm, n_shared) * dm->f * eb >= lim ||
-      257 * dm->f * eb >= lim)
+  if (!product_below(dm->T + 1, dm->d, eb, lim) || !product_below(dm->f, dm->d, eb, lim) ||
+      !product_below(ffn_rows(dm, n_shared), dm->f, eb, lim) || !product_below(257, dm->f, eb, lim))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -340,8 +362,8 @@ int bwd_shape_ok(const moe_dims_t* dm) {
   // operands (x and dout rows, g|u and dg|du rows of a block), and the
   // transposed activations [2f][pp]
   const int64_t lim = int64_t(1) << 32, P = dm->T * dm->k, pp = (P + 63) / 64 * 64 + 64 * int64_t(dm->E);
-  if (2 * dm->f * dm->d * 2 >= lim || 257 * 2 * dm->f * 2 >= lim || 2 * dm->f * pp * 2 >= lim ||
-      dm->d * pp * 2 >= lim)
+  if (!product_below(2 * dm->f, dm->d, 2, lim) || !product_below(257 * 2, dm->f, 2, lim) ||
+      !product_below(2 * dm->f, pp, 2, lim) || !product_below(dm->d, pp, 2, lim))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -618,8 +640,9 @@ int moe_fused_status(const moe_dims_t* dm, const void* ws, size_t ws_bytes, int3
 int moe_layer_plan_layout(const moe_dims_t* dm, int n_shared, size_t* mblocks_offset, size_t* count_offset,
                           int64_t* max_mblocks_out) {
   if (int st = check_dims(dm)) return st;
-  if (n_shared < 0 || dm->E + n_shared > 1024 || !mblocks_offset || !count_offset || !max_mblocks_out)
-    return MOE_ERR_INVALID;
+  if (!mblocks_offset || !count_offset || !max_mblocks_out) return MOE_ERR_INVALID;
+  if (n_shared != 0)
+    if (int st = check_shared(dm, n_shared)) return st;
   LayerWs lw{};
   layer_ws(dm, nullptr, &lw, n_shared);
   FfnWs fw{};
@@ -631,7 +654,7 @@ int moe_layer_plan_layout(const moe_dims_t* dm, int n_shared, size_t* mblocks_of
 }
 
 size_t moe_workspace_bytes_shared(const moe_dims_t* dm, int n_shared) {
-  if (check_dims(dm) != MOE_OK || n_shared < 1 || dm->E + n_shared > 1024) return 0;
+  if (check_dims(dm) != MOE_OK || check_shared(dm, n_shared) != MOE_OK) return 0;
   return layer_ws(dm, nullptr, nullptr, n_shared);
 }
 
@@ -641,8 +664,7 @@ int moe_layer_forward_shared(const moe_dims_t* dm, int n_shared, const void* x, 
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws,
                              size_t ws_bytes, void* stream) {
   if (int st = check_dims(dm)) return st;
-  if (n_shared < 1 || dm->E + n_shared > 1024 || dm->T * (dm->k + int64_t(n_shared)) >= (int64_t(1) << 31))
-    return MOE_ERR_INVALID;
+  if (int st = check_shared(dm, n_shared)) return st;
   if (dm->T > 0 && (!ok16(sw1) || !ok16(sw3) || !ok16(sw2))) return MOE_ERR_INVALID;
   SharedExperts sh;
   sh.n = n_shared;
