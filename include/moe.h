@@ -202,17 +202,21 @@ int moe_layer_forward_shared(const moe_dims_t* dims, int n_shared, const void* x
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* The same layer with FC1, FC2 and the combine in one persistent launch
- * (route and dispatch run before it as usual). Workgroups take tiles from one
- * device-side sequence (FC1 tiles, then FC2 tiles, then blocks of 8 tokens
- * for the combine); an FC2 tile starts once every FC1 tile of its block of
- * rows is stored, the combine once every FC2 tile is, tracked by readiness
- * counters in the workspace instead of kernel boundaries (the next step of
- * the pages' megakernel design: MegaFlux, section 2.1, MegaMoE's tiled
- * FC1/FC2). The arithmetic is that of moe_layer_forward tile for tile, so
- * the outputs are bitwise equal. bf16 only (MOE_ERR_UNSUPPORTED otherwise);
- * other arguments, limits and the workspace size (moe_workspace_bytes) as
- * moe_layer_forward. */
+/* The same layer in one persistent launch. Workgroups take tiles from
+ * device-side sequences: route tiles (one token: its logits, top-k and
+ * weights), then, once the workgroup that stored the last route tile has run
+ * the dispatch and written the tile plan, FC1 tiles, FC2 tiles and blocks of
+ * 8 tokens for the combine; an FC2 tile starts once every FC1 tile of its
+ * block of rows is stored, the combine once every FC2 tile is, tracked by
+ * readiness counters in the workspace instead of kernel boundaries
+ * (MegaScale-Infer, "Fused Kernels": the small routing steps fused; MegaFlux,
+ * section 2.1: MegaMoE's tiled FC1/FC2 in one persistent kernel). Route and
+ * dispatch run inside the launch when E <= 64 and T*k <= 65536 (else as
+ * separate launches before it; the MOE_FUSED_FRONT=0 environment switch
+ * forces that). The arithmetic is that of moe_layer_forward tile for tile,
+ * so the outputs and routing arrays are bitwise equal. bf16 only
+ * (MOE_ERR_UNSUPPORTED otherwise); other arguments, limits and the workspace
+ * size (moe_workspace_bytes) as moe_layer_forward. */
 int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
                             const void* w1, const void* w3, const void* w2, void* out, float* logits,
                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -227,9 +231,11 @@ int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* w
  * its outputs are then wrong. moe_fused_status waits for `stream` and copies
  * that word of the last moe_layer_forward_fused call on `ws` (same dims) to
  * *flags (host pointer): 0 = every wait was met, so the outputs are valid;
- * bit 0 set = some wait gave up, discard the outputs. The word is cleared at
- * the start of every fused call. T == 0 gives *flags = 0. Errors as for the
- * workspace checks of moe_layer_forward; MOE_ERR_HIP if the copy fails. */
+ * nonzero = some wait gave up, discard the outputs (bit 0: a wait for FC1 or
+ * FC2 tiles; bit 1: a wait for the tile plan, after which that workgroup left
+ * the launch). The word is cleared at the start of every fused call. T == 0
+ * gives *flags = 0. Errors as for the workspace checks of moe_layer_forward;
+ * MOE_ERR_HIP if the copy fails. */
 int moe_fused_status(const moe_dims_t* dims, const void* ws, size_t ws_bytes, int32_t* flags, void* stream);
 
 /* Where the tile plan of a layer call sits in its workspace (host-only query,

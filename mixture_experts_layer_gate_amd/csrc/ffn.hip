@@ -21,7 +21,9 @@
 
 #include "combine_vec.h"
 #include "common.h"
+#include "dispatch_block.h"
 #include "kernels.h"
+#include "route_vec.h"
 
 namespace moe {
 
@@ -961,8 +963,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // (their stores reach the point of coherence of every XCD's L2); consumers
 // take a device-scope acquire before reading.
 // sync words: [0..7] next tile of each group, [8] FC2 tiles stored,
-// [kFusedErrorWord] error flags, [16 + mb] FC1 tiles of m-block mb stored.
+// [kFusedErrorWord] error flags, [10] next route tile, [11] route tiles
+// stored, [12] plan ready, [13] m-block count of the plan, [16 + mb] FC1
+// tiles of m-block mb stored.
+//
+// Route and dispatch as the launch's first phases (front): workgroups first
+// take route tiles (one token each: its E logits in the contract order, one
+// wave per expert, then its top k and weights, the same device code as the
+// small-batch route kernel); the workgroup that stores the last route tile then
+// runs the one-workgroup dispatch and tile plan (the same device code as the
+// dispatch kernel) and publishes the plan; every other workgroup waits for it
+// before the FFN phases. The dispatch places every expert's rows and writes
+// the plan in one pass, so readiness per expert would arrive at the same
+// moment as the plan. A workgroup whose wait for the plan gives up exits
+// without touching the plan (error bit 1): the plan's words may still be
+// changing, and the m-block list drives the FFN tiles' addresses.
 constexpr int kFusedSyncHead = 16;
+constexpr int kSyncRouteNext = 10, kSyncRouteDone = 11, kSyncPlanReady = 12, kSyncPlanCount = 13;
 [[maybe_unused]] constexpr int kCombineTokens = 8;  // tokens per combine block
 
 struct FusedFfnArgs {
@@ -974,22 +991,43 @@ struct FusedFfnArgs {
   int k, n_shared;
   int32_t* sync;
   int spin_limit;  // polls of a readiness counter before giving up; < 0: give up at once
+  // front phases (route and dispatch in the launch): front = 1; fc1/fc2's
+  // n_mblocks then point at sync[kSyncPlanCount]
+  int front, E;
+  const void* wg;
+  const float* bias;
+  float* logits;
+  int32_t *topk_idx, *counts, *offsets, *perm_out, *inv_perm_out, *n_mblocks_ws;
+  float* topk_w_out;
+  int4* mblocks_out;
+  int64_t max_mb;
 };
 
-__device__ __forceinline__ void wait_count(int32_t* counter, int target, int32_t* err, int spin_limit) {
+// Waits (thread 0 polls, the workgroup then meets at a barrier) until *counter
+// reaches target; past spin_limit polls it sets `bit` in the error word and
+// gives up. Returns whether the target was reached, the same in every thread
+// (through `flag`, an LDS word no other part of the workgroup uses meanwhile).
+__device__ __forceinline__ bool wait_count(int32_t* counter, int target, int32_t* err, int spin_limit, int* flag,
+                                           int bit = 1) {
   if (threadIdx.x == 0) {
     int spins = 0;
+    int met = 1;
     while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (spins >= spin_limit) {
-        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        met = 0;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
       ++spins;
     }
+    *flag = met;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+  const bool ok = *flag != 0;
+  __syncthreads();  // every thread has read the flag before a later wait rewrites it
+  return ok;
 }
 
 // Every wave waits until its stores are complete in its XCD's L2, then one
@@ -1002,6 +1040,62 @@ __device__ __forceinline__ void publish(int32_t* counter) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// publish() that also tells whether this workgroup's increment brought the
+// counter to `target` (the same answer in every thread).
+__device__ __forceinline__ bool publish_last(int32_t* counter, int target, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == target - 1;
+  __syncthreads();
+  const bool last = *flag != 0;
+  __syncthreads();
+  return last;
+}
+
+// Front phases of the fused launch: route tiles, then the dispatch by the
+// workgroup that stores the last route tile, then the plan. Returns false if
+// this workgroup gave up waiting for the plan (it must then stay away from it).
+__device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
+  int64_t* s_tile = reinterpret_cast<int64_t*>(lds);
+  int* s_flag = reinterpret_cast<int*>(lds + 8);
+  float* srow = reinterpret_cast<float*>(lds + 64);        // [<= 64] logits of the token
+  float* sel = reinterpret_cast<float*>(lds + 512);        // [<= 64] selected logits
+  int32_t* wsum = reinterpret_cast<int32_t*>(lds + 1024);  // [8]
+  int32_t(*wh)[kMaxExperts] = reinterpret_cast<int32_t(*)[kMaxExperts]>(lds + 2048);  // [8][1024]
+  int32_t* err = a.sync + kFusedErrorWord;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (;;) {
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *s_tile = __hip_atomic_fetch_add(a.sync + kSyncRouteNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t t = *s_tile;
+    __syncthreads();
+    if (t >= a.T) break;
+    for (int e = wv; e < a.E; e += 8) {
+      const float l = gate_logit_wave<1>(a.fc1.A, a.wg, a.bias, t, e, a.d);
+      if (lane == 0) {
+        srow[e] = l;
+        a.logits[t * a.E + e] = l;
+      }
+    }
+    __syncthreads();
+    if (wv == 0) topk_row(srow, a.E, a.k, a.topk_idx + t * a.k, a.topk_w_out + t * a.k, sel);
+    if (publish_last(a.sync + kSyncRouteDone, static_cast<int>(a.T), s_flag)) {
+      // every route tile is stored: this workgroup dispatches
+      if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+      dispatch_block<512>(a.topk_idx, a.T * a.k, a.E, a.counts, a.offsets, a.perm_out, a.inv_perm_out, 256, a.max_mb,
+                          a.mblocks_out, a.sync + kSyncPlanCount, wh, wsum);
+      __syncthreads();
+      if (threadIdx.x == 0) *a.n_mblocks_ws = a.sync[kSyncPlanCount];  // where a layer call leaves the count
+      publish(a.sync + kSyncPlanReady);
+    }
+  }
+  return wait_count(a.sync + kSyncPlanReady, 1, err, a.spin_limit, s_flag, 2);
+}
+
 template <int BN2, int WM2, int WN2>
 __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1011,6 +1105,8 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
   constexpr int LDS = F1::LDS_BYTES > F2::LDS_BYTES ? F1::LDS_BYTES : F2::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[LDS];
   int64_t* s_tile = reinterpret_cast<int64_t*>(lds);  // the tile buffers are free between tiles
+  int* s_flag = reinterpret_cast<int*>(lds + 16);     // (free whenever a wait runs: before a tile's loads)
+  if (a.front && !fused_front(a, lds)) return;
   const int64_t n1 = F1::tiles(a.fc1), n2 = F2::tiles(a.fc2);
   const int64_t nc = (a.T + kCombineTokens - 1) / kCombineTokens;
   const int nbc1 = static_cast<int>((a.fc1.N + 127) / 128);  // FC1 tiles per m-block
@@ -1033,10 +1129,10 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
     if (j < s1) {
       F1::tile(a.fc1, lds, nth(j), [](int) {}, [&](int mb) { publish(done1 + mb); });
     } else if (j < s1 + s2) {
-      F2::tile(a.fc2, lds, nth(j - s1), [&](int mb) { wait_count(done1 + mb, nbc1, err, a.spin_limit); },
+      F2::tile(a.fc2, lds, nth(j - s1), [&](int mb) { wait_count(done1 + mb, nbc1, err, a.spin_limit, s_flag); },
                [&](int) { publish(fc2_done); });
     } else if (j < s1 + s2 + sc) {
-      wait_count(fc2_done, static_cast<int>(n2), err, a.spin_limit);
+      wait_count(fc2_done, static_cast<int>(n2), err, a.spin_limit, s_flag);
       const int64_t t0 = nth(j - s1 - s2) * kCombineTokens;
       const int64_t nt = a.T - t0 < kCombineTokens ? a.T - t0 : kCombineTokens;
       const int64_t nvec = a.d / 8;
@@ -1384,12 +1480,19 @@ bool ffn_fused_coresident(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f) 
   return e == hipSuccess && static_cast<int64_t>(per_cu) * device_cu_count() >= grid;
 }
 
-// FC1, FC2 and combine in one launch (bf16). The sync words must be zero on entry.
+bool fused_front_ok(int64_t T, int E, int k) {
+  if (const char* env = getenv("MOE_FUSED_FRONT"))
+    if (env[0] == '0') return false;
+  return T >= 1 && E <= 64 && T * k <= kFusedMaxAssign;
+}
+
+// (Route, dispatch,) FC1, FC2 and combine in one launch (bf16). The sync words
+// must be zero on entry.
 hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
-                            const void* w2, void* h, void* y, const int4* mblocks, const int32_t* n_mblocks,
+                            const void* w2, void* h, void* y, int4* mblocks, int32_t* n_mblocks,
                             int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
                             const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, int spin_limit,
-                            hipStream_t s) {
+                            const FusedFront& front, hipStream_t s) {
   FusedFfnArgs a{};
   a.fc1 = GemmArgs{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f, T * k, sh.w1, sh.w3,
                    sh.n > 0 ? sh.E_routed : INT32_MAX};
@@ -1404,6 +1507,25 @@ hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T
   a.n_shared = sh.n;
   a.sync = sync;
   a.spin_limit = spin_limit;
+  if (front.on) {
+    // the launch routes and dispatches first; its FFN phases read the plan's
+    // count from the sync words
+    a.front = 1;
+    a.E = front.E;
+    a.wg = front.wg;
+    a.bias = front.bias;
+    a.logits = front.logits;
+    a.topk_idx = front.topk_idx;
+    a.topk_w_out = front.topk_w;
+    a.counts = front.counts;
+    a.offsets = front.offsets;
+    a.perm_out = front.perm;
+    a.inv_perm_out = front.inv_perm;
+    a.mblocks_out = mblocks;
+    a.n_mblocks_ws = n_mblocks;
+    a.max_mb = max_mb;
+    a.fc1.n_mblocks = a.fc2.n_mblocks = sync + kSyncPlanCount;
+  }
   int64_t grid;
   bool narrow;
   fused_shape(max_mb, est_mb, d, f, &grid, &narrow);

@@ -93,11 +93,29 @@ constexpr int kFusedErrorWord = 9;
 constexpr int kFusedSpinLimit = 1 << 22;
 // every workgroup of the fused launch for this shape can be resident at once
 bool ffn_fused_coresident(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f);
+// Route and dispatch as the fused launch's first phases (bf16, no shared
+// experts, E <= 64, T*k <= kFusedMaxAssign): the launch then writes the
+// routing outputs and the plan itself, and the m-block count ends up at
+// n_mblocks as after a dispatch launch.
+struct FusedFront {
+  bool on = false;
+  const void* wg = nullptr;
+  const float* bias = nullptr;
+  float* logits = nullptr;
+  int32_t* topk_idx = nullptr;
+  float* topk_w = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* perm = nullptr;
+  int32_t* inv_perm = nullptr;
+  int E = 0;
+};
+bool fused_front_ok(int64_t T, int E, int k);
 hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
-                            const void* w2, void* h, void* y, const int4* mblocks, const int32_t* n_mblocks,
+                            const void* w2, void* h, void* y, int4* mblocks, int32_t* n_mblocks,
                             int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
                             const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, int spin_limit,
-                            hipStream_t s);
+                            const FusedFront& front, hipStream_t s);
 
 // Weighted combine.
 // With n_shared > 0, out[t] also adds y[T*k + s*T + t] for s ascending.

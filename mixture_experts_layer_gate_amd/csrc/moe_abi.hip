@@ -380,14 +380,15 @@ int fused_spin_limit() {
 
 int do_ffn_fused(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* inv_perm,
                  const float* topk_w, const void* w1, const void* w3, const void* w2, void* y, void* out,
-                 const FfnWs& fw, const SharedExperts& sh, hipStream_t s) {
+                 const FfnWs& fw, const SharedExperts& sh, hipStream_t s, const FusedFront& front = FusedFront{}) {
   const int64_t est_mb = expected_mblocks(dm, 256, fw.max_mb, sh.n);
   if (int st = hip_status(launch_fill_zero(reinterpret_cast<float*>(fw.sync),
                                            static_cast<int64_t>(fused_sync_words(fw.max_mb)), s)))
     return st;
   StageScope sc(MOE_STAGE_FFN_FUSED, s);
   return hip_status(launch_ffn_fused(x, perm, dm->k, dm->T, w1, w3, w2, fw.h, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
-                                     est_mb, dm->d, dm->f, inv_perm, topk_w, out, fw.sync, sh, fused_spin_limit(), s));
+                                     est_mb, dm->d, dm->f, inv_perm, topk_w, out, fw.sync, sh, fused_spin_limit(), front,
+                                     s));
 }
 
 int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, const void* wg, const float* bias,
@@ -420,10 +421,26 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
   if (!perm) perm = lw.perm;
   if (!inv_perm) inv_perm = lw.inv;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
   const int64_t n = dm->T * dm->k;
   FfnWs fw{};
   ffn_ws(dm, lw.sub, &fw, sh.n);
+  if (fused && sh.n == 0 && fused_front_ok(dm->T, dm->E, dm->k)) {
+    // route and dispatch as the fused launch's first phases
+    FusedFront front;
+    front.on = true;
+    front.wg = wg;
+    front.bias = bias;
+    front.logits = logits;
+    front.topk_idx = topk_idx;
+    front.topk_w = topk_w;
+    front.counts = counts;
+    front.offsets = offsets;
+    front.perm = perm;
+    front.inv_perm = inv_perm;
+    front.E = dm->E;
+    return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s, front);
+  }
+  if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
   if (use_fused_dispatch(n)) {
     // histogram, scan, scatter (and, without shared experts, the tile plan) in one launch
     const bool plan_inline = sh.n == 0;

@@ -1,5 +1,7 @@
-"""The fused FFN launch (moe_layer_forward_fused): FC1, FC2 and the combine in one
-persistent kernel with device-side readiness counters.
+"""The fused launch (moe_layer_forward_fused): route and dispatch (for E <= 64),
+FC1, FC2 and the combine in one persistent kernel with device-side readiness
+counters; MOE_FUSED_FRONT=0 keeps route and dispatch as separate launches before
+it, and both forms are tested.
 
 Its tiles do exactly the arithmetic of moe_layer_forward's separate launches
 when those do not split K (MOE_SPLIT_K=0), so the bar is bitwise equality with that path (itself held to the oracle in
@@ -17,16 +19,20 @@ import moe_inputs
 import oracle
 import mixture_experts_layer_gate_amd as moe
 from conftest import to_numpy
-from parity import OUT_TOL, gpu_float, rel_err
+from parity import OUT_TOL, check_plan, gpu_float, rel_err
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True)
-def _whole_k(monkeypatch):
+@pytest.fixture(autouse=True, params=["front", "ffn_only"])
+def _whole_k(monkeypatch, request):
     # the fused kernel never splits K; the separate launches it is compared with
     # bit for bit must not either
     monkeypatch.setenv("MOE_SPLIT_K", "0")
+    if request.param == "ffn_only":
+        monkeypatch.setenv("MOE_FUSED_FRONT", "0")
+    else:
+        monkeypatch.delenv("MOE_FUSED_FRONT", raising=False)
 
 
 def _say(msg):
@@ -43,7 +49,8 @@ def _both(cfg_or_shape, seed=0):
         T, d, f, E, k, s = cfg_or_shape
         inp = moe_inputs.random_inputs(T, d, f, E, k, "bf16", s, seed, device="cuda")
     dims = moe.Dims(T, d, f, E, k, torch.bfloat16)
-    ref = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    ref, r_ref = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                   return_routing=True)
     ws = moe.make_workspace(dims)
     outs = []
     for _ in range(2):
@@ -52,7 +59,13 @@ def _both(cfg_or_shape, seed=0):
         torch.cuda.synchronize()
         # every readiness wait of the launch was met: its outputs are valid
         assert moe.fused_status(dims, ws) == 0
+        # the routing arrays (computed in the launch itself, or before it) are the separate launches' bits
+        for key in r_ref:
+            assert torch.equal(r[key], r_ref[key]), key
         outs.append(out.clone())
+    # the tile plan the fused launch used, where a layer call leaves it
+    plan = moe.read_plan(dims, ws).numpy()
+    check_plan(plan, r_ref["counts"].cpu().numpy(), r_ref["offsets"].cpu().numpy(), 256, T * k)
     return inp, ref, outs, r
 
 
@@ -96,8 +109,9 @@ def test_fused_reports_a_wait_that_gave_up(monkeypatch):
     """A readiness wait that gives up is reported through moe_fused_status. The failure is
     forced from the host: MOE_FUSED_SPIN_LIMIT=-1 makes every wait that finds its counter
     short give up at once (the kernel then reads operands that may not be stored yet, so
-    only the status is checked); a normal call on the same workspace clears the word again
-    and gives the separate launches' bits."""
+    only the status is checked; with route and dispatch in the launch, a workgroup that gives
+    up waiting for the plan leaves the launch at once); a normal call on the same workspace
+    clears the word again and gives the separate launches' bits."""
     shape = (1000, 512, 1024, 8, 2, 0.0)
     _say(f"case fused wait failure reported {shape}")
     T, d, f, E, k, s = shape
@@ -112,7 +126,7 @@ def test_fused_reports_a_wait_that_gave_up(monkeypatch):
         moe.layer_forward(*args, ws=ws, fused=True)
         flags.append(moe.fused_status(dims, ws))
     _say(f"  status words with no waiting: {flags}")
-    assert any(v & 1 for v in flags)
+    assert any(v != 0 for v in flags)
     monkeypatch.delenv("MOE_FUSED_SPIN_LIMIT")
     out = moe.layer_forward(*args, ws=ws, fused=True)
     assert moe.fused_status(dims, ws) == 0
