@@ -59,11 +59,11 @@ def parse():
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured HBM-read and MFMA ceilings (diagnostic, about a second)")
     p.add_argument("--fused", action="store_true",
-                   help="time moe_layer_forward_fused (FC1, FC2 and combine in one persistent launch)")
+                   help="time the one-launch layer (moe_layer_forward_fused, or _fused_packed with packed weights)")
     p.add_argument("--weights", choices=["auto", "packed", "stored"], default="auto",
                    help="packed: moe_layer_forward_packed on the expert weights re-laid once in stage order "
                         "(moe_pack_weights, timed apart, not part of a step); stored: moe_layer_forward on the "
-                        "weights as stored; auto: packed for bf16 layers without shared experts, unless --fused")
+                        "weights as stored; auto: packed for bf16 layers without shared experts")
     p.add_argument("--backward", action="store_true",
                    help="time the layer's backward (moe_layer_backward) instead of the forward")
     p.add_argument("--copy-probe", action="store_true",
@@ -472,16 +472,13 @@ def run_one(args, seed: int) -> dict:
     stream = torch.cuda.current_stream()
 
     S = cfg.n_shared
-    use_packed = args.weights == "packed" or (
-        args.weights == "auto" and cfg.dtype == "bf16" and not S and not args.fused)
+    use_packed = args.weights == "packed" or (args.weights == "auto" and cfg.dtype == "bf16" and not S)
     if S:
         if args.fused or use_packed:
             raise SystemExit("the fused FFN launch and the packed weights cover layers without shared experts")
         ws = torch.empty(moe.workspace_bytes_shared(dims, S), dtype=torch.uint8, device=dev)
     packed, pack_ms = None, None
     if use_packed:
-        if args.fused:
-            raise SystemExit("the fused FFN launch reads the weights as stored")
         pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         pe0.record(stream)
         packed = moe.pack_weights(dims, inp["w1"], inp["w3"], inp["w2"], stream=stream)
@@ -570,7 +567,8 @@ def run_one(args, seed: int) -> dict:
     roof["traffic"] = None if args.fused else measured_traffic(cfg.name, "fc1_packed" if use_packed else "fc1")
     big_tile = cfg.dtype == "bf16" and os.environ.get("MOE_GEMM_REGIME", "1") != "0"
     if args.fused:
-        roof["kernel"] = "ffn_fused_kernel (FC1 + SiLU*mul, FC2, combine; one launch)"
+        roof["kernel"] = ("ffn_fused_kernel (route, dispatch, FC1 + SiLU*mul, FC2, combine; one launch"
+                          f"{'; stage-order weights' if use_packed else ''})")
     elif big_tile:
         rows = moe.ffn_block_rows(moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype))
         roof["kernel"] = (f"gemm_dl_kernel<gated, {rows}x256{', stage-order weights' if use_packed else ''}> "

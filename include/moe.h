@@ -206,17 +206,22 @@ int moe_layer_forward_shared(const moe_dims_t* dims, int n_shared, const void* x
  * device-side sequences: route tiles (one token: its logits, top-k and
  * weights), then, once the workgroup that stored the last route tile has run
  * the dispatch and written the tile plan, FC1 tiles, FC2 tiles and blocks of
- * 8 tokens for the combine; an FC2 tile starts once every FC1 tile of its
+ * 512 output vectors for the combine (a batch of at most 16 logits, T*E <=
+ * 16, is routed and dispatched by every workgroup for itself, with no wait);
+ * an FC2 tile starts once every FC1 tile of its
  * block of rows is stored, the combine once every FC2 tile is, tracked by
  * readiness counters in the workspace instead of kernel boundaries
  * (MegaScale-Infer, "Fused Kernels": the small routing steps fused; MegaFlux,
  * section 2.1: MegaMoE's tiled FC1/FC2 in one persistent kernel). Route and
  * dispatch run inside the launch when E <= 64 and T*k <= 65536 (else as
  * separate launches before it; the MOE_FUSED_FRONT=0 environment switch
- * forces that). The arithmetic is that of moe_layer_forward tile for tile,
- * so the outputs and routing arrays are bitwise equal. bf16 only
- * (MOE_ERR_UNSUPPORTED otherwise); other arguments, limits and the workspace
- * size (moe_workspace_bytes) as moe_layer_forward. */
+ * forces that). The tiles are those of moe_layer_forward: the same rows per
+ * block, FC2 tile width and, for decode-sized batches with fewer tiles than
+ * compute units, the same split of K (the workgroup that stores a split
+ * tile's last part sums the parts in the same order), so the outputs and
+ * routing arrays are bitwise equal. bf16 only (MOE_ERR_UNSUPPORTED
+ * otherwise); other arguments, limits and the workspace size
+ * (moe_workspace_bytes) as moe_layer_forward. */
 int moe_layer_forward_fused(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
                             const void* w1, const void* w3, const void* w2, void* out, float* logits,
                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -288,6 +293,14 @@ int moe_layer_forward_packed(const moe_dims_t* dims, const void* x, const void* 
                              const void* w1p, const void* w3p, const void* w2p, void* out, float* logits,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                              int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+/* moe_layer_forward_fused reading packed weights (moe_pack_weights): the one
+ * persistent launch of moe_layer_forward_fused with the weight loads of
+ * moe_layer_forward_packed; bitwise the same outputs as both. Arguments,
+ * limits, workspace, errors and moe_fused_status as moe_layer_forward_fused. */
+int moe_layer_forward_fused_packed(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+                                   const void* w1p, const void* w3p, const void* w2p, void* out, float* logits,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- backward pass ----
  * Gradients of the layer for a scalar loss whose gradient with respect to

@@ -29,7 +29,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
            "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_pack_weights",
            "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed",
-           "moe_layer_forward_noalloc"]
+           "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed"]
 
 # Bytes of the static scratch moe_layer_forward_noalloc uses (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h).
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -93,6 +93,7 @@ def load_library():
     lib.moe_layer_forward_fused.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_pack_weights.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P]
     lib.moe_layer_forward_packed.argtypes = lib.moe_layer_forward.argtypes
+    lib.moe_layer_forward_fused_packed.argtypes = lib.moe_layer_forward.argtypes
     lib.moe_pack_weights_transposed.argtypes = lib.moe_pack_weights.argtypes
     lib.moe_fused_status.argtypes = [_DP, _P, _S, ctypes.POINTER(ctypes.c_int32), _P]
     lib.moe_layer_plan_layout.argtypes = [_DP, ctypes.c_int, ctypes.POINTER(_S), ctypes.POINTER(_S),
@@ -112,7 +113,7 @@ def load_library():
     for fn in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
                "moe_layer_forward_shared", "moe_layer_backward", "moe_layer_forward_fused", "moe_fused_status",
                "moe_layer_plan_layout", "moe_pack_weights", "moe_pack_weights_transposed",
-               "moe_layer_forward_packed", "moe_layer_forward_noalloc",
+               "moe_layer_forward_packed", "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed",
                "moe_timing_enable", "moe_timing_disable", "moe_timing_read", "moe_probe_hbm_read", "moe_probe_mfma"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -311,10 +312,11 @@ def layer_forward_noalloc(dims: Dims, x, wg, bias, w1, w3, w2, out, routing=None
 def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream=None, return_routing=False,
                   fused=False, packed=None):
     """The whole layer. With return_routing, also returns the routing arrays as a dict.
-    fused=True runs FC1, FC2 and the combine as one persistent launch
-    (moe_layer_forward_fused; bitwise the same result). packed=(w1p, w3p, w2p) from
-    pack_weights reads the stage-order weights instead of w1, w3, w2 (which may
-    then be None; moe_layer_forward_packed, bitwise the same result)."""
+    fused=True runs the layer as one persistent launch (moe_layer_forward_fused;
+    bitwise the same result). packed=(w1p, w3p, w2p) from pack_weights reads the
+    stage-order weights instead of w1, w3, w2 (which may then be None;
+    moe_layer_forward_packed, or with fused=True moe_layer_forward_fused_packed;
+    bitwise the same result)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", dims.dtype, (dims.T, dims.d))
@@ -322,8 +324,6 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
     if bias is not None:
         _need(bias, "bias", torch.float32, (dims.E,))
     if packed is not None:
-        if fused:
-            raise ValueError("the fused launch reads the weights as stored")
         w1, w3, w2 = packed
     for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
                          ("w2", w2, (dims.E, dims.d, dims.f))):
@@ -342,8 +342,9 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
              "inv_perm": torch.empty(n, dtype=torch.int32, device=dev)}
     ws, nws = _ws(dims, ws)
     g = r.get
-    fn = "moe_layer_forward_packed" if packed is not None else (
-        "moe_layer_forward_fused" if fused else "moe_layer_forward")
+    fn = {(False, False): "moe_layer_forward", (False, True): "moe_layer_forward_packed",
+          (True, False): "moe_layer_forward_fused", (True, True): "moe_layer_forward_fused_packed"}[
+        (bool(fused), packed is not None)]
     _check(fn, getattr(lib, fn)(
         ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
         _ptr(g("logits")), _ptr(g("topk_idx")), _ptr(g("topk_w")), _ptr(g("counts")), _ptr(g("offsets")),

@@ -938,6 +938,45 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 #endif
 }
 
+// Second half of a split launch for split tile t (t >= cut.full): per output
+// element, the sum of its parts in part order, then what the GEMM's bf16
+// epilogue applies: SiLU(g) * u for FC1 (a wave's TN accumulator columns hold
+// TN/2 gate columns then the TN/2 up columns of the same outputs), bf16
+// rounding. Threads tid, tid + nthr, ... of the caller share the tile.
+template <bool kGated, int BM, int BN, int WN>
+__device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, SplitCut cut, int nbc, int nmb,
+                                                  int tid, int nthr) {
+  constexpr int OC = kGated ? BN / 2 : BN;  // output columns of a tile
+  constexpr int TN = BN / WN;
+  const int64_t N = g.N;
+  const int sp = cut.sp;
+  bf16_t* C = static_cast<bf16_t*>(g.C);
+  int mb, nb;
+  decode_group_tile(g, t, nbc, nmb, mb, nb);
+  const int4 blk = g.mblocks[mb];
+  const int row0 = blk.y, rows = blk.z;
+  const float* part = g.partial + (t - cut.full) * sp * (BM * BN);
+  // (an opaque copy of the thread index keeps the compiler from hoisting this
+  // loop's index arithmetic out of a caller's tile loop, where it would hold
+  // registers through the GEMM)
+  asm volatile("" : "+v"(tid));
+  for (int q = tid; q < rows * OC; q += nthr) {
+    const int r = q / OC, oc = q % OC;
+    const int64_t col = static_cast<int64_t>(nb) * OC + oc;
+    if (col >= N) continue;
+    const int pc = kGated ? (oc / (TN / 2)) * TN + oc % (TN / 2) : oc;
+    const float* src = part + r * BN + pc;
+    float a = src[0];
+    float b = kGated ? src[TN / 2] : 0.f;
+    for (int p = 1; p < sp; ++p) {
+      a += src[p * (BM * BN)];
+      if constexpr (kGated) b += src[p * (BM * BN) + TN / 2];
+    }
+    const float v = kGated ? silu_mul(a, b) : a;
+    C[static_cast<int64_t>(row0 + r) * N + col] = static_cast<bf16_t>(f32_to_bf16_bits(v));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Fused expert FFN: FC1 tiles, FC2 tiles and the combine in one persistent
 // launch, with device-side readiness counters in place of kernel boundaries
@@ -948,8 +987,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // Tiles are handed out by atomic counters, one per group of workgroups
 // b = x (mod 8) (the workgroups of one XCD): group x takes, in order, its share
 // of the FC1 tiles, then its share of the FC2 tiles, then its share of the
-// combine's token blocks, each share being the tiles the separate launches'
-// XCD-aware numbering gives that XCD (so neighbouring tiles meet in one L2).
+// combine's blocks (512 16-byte vectors of the output, one per thread), each
+// share being the tiles the separate launches' XCD-aware numbering gives that
+// XCD (so neighbouring tiles meet in one L2).
 // An FC2 tile waits until every FC1 tile of its m-block has been stored; a
 // combine block waits until every FC2 tile has. No launch can deadlock: a
 // group takes an FC2 tile only after all of its FC1 tiles are taken, every
@@ -964,8 +1004,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // take a device-scope acquire before reading.
 // sync words: [0..7] next tile of each group, [8] FC2 tiles stored,
 // [kFusedErrorWord] error flags, [10] next route tile, [11] route tiles
-// stored, [12] plan ready, [13] m-block count of the plan, [16 + mb] FC1
-// tiles of m-block mb stored.
+// stored, [12] plan ready, [13] m-block count of the plan, [14] split FC1
+// tiles summed, [16 + mb] FC1 tiles of m-block mb stored, then
+// [16 + max_mb + i] parts stored of split FC1 tile i and
+// [16 + max_mb + kMaxSplitTiles + i] of split FC2 tile i.
+//
+// Few-tile launches (a decode step: fewer tiles than CUs) split K exactly as
+// the separate launches do (the same cut of the same tile list, the parts'
+// fp32 accumulators in the same slots of the partial buffer): the workgroup
+// that stores a split tile's last part sums the parts in part order and
+// applies the epilogue (the separate launches' reduce, the same device code),
+// then counts the tile as stored. FC1 and FC2 parts share the partial buffer,
+// so an FC2 part starts only once every split FC1 tile has been summed. Tile
+// rows (128 for batches with few rows per expert, else 256), FC2 tile width
+// and the weight layout (as stored or in stage order) follow the separate
+// launches too, so the fused launch's outputs are bitwise theirs.
 //
 // Route and dispatch as the launch's first phases (front): workgroups first
 // take route tiles (one token each: its E logits in the contract order, one
@@ -977,10 +1030,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // the plan in one pass, so readiness per expert would arrive at the same
 // moment as the plan. A workgroup whose wait for the plan gives up exits
 // without touching the plan (error bit 1): the plan's words may still be
-// changing, and the m-block list drives the FFN tiles' addresses.
+// changing, and the m-block list drives the FFN tiles' addresses. A batch of
+// at most kLocalRouteLogits logits (a decode step of a token or two) is
+// instead routed and dispatched by every workgroup for itself, which costs a
+// few logits per workgroup and no wait at all.
 constexpr int kFusedSyncHead = 16;
-constexpr int kSyncRouteNext = 10, kSyncRouteDone = 11, kSyncPlanReady = 12, kSyncPlanCount = 13;
-[[maybe_unused]] constexpr int kCombineTokens = 8;  // tokens per combine block
+[[maybe_unused]] constexpr int kSyncRouteNext = 10, kSyncRouteDone = 11, kSyncPlanReady = 12, kSyncPlanCount = 13,
+              kSyncSplit1Done = 14;
+// split tiles of one phase: fewer than the split target (the CU count)
+constexpr int kMaxSplitTiles = 1024;
+// combine units: 512 consecutive 8-column vectors of the [T][d] output (one per thread)
+[[maybe_unused]] constexpr int kCombineVecs = 512;
+// batches of at most this many logits (T * E) are routed by every workgroup itself
+[[maybe_unused]] constexpr int kLocalRouteLogits = 16;
+// elements per lane whose loads a front logit issues at once (a 6144-wide
+// logit in two round trips; the registers are free before the FFN phases)
+[[maybe_unused]] constexpr int kFrontLoads = 48;
 
 struct FusedFfnArgs {
   GemmArgs fc1, fc2;
@@ -1001,6 +1066,7 @@ struct FusedFfnArgs {
   float* topk_w_out;
   int4* mblocks_out;
   int64_t max_mb;
+  int block_rows;  // rows per m-block of the plan (the tile rows)
 };
 
 // Waits (thread 0 polls, the workgroup then meets at a barrier) until *counter
@@ -1018,7 +1084,9 @@ __device__ __forceinline__ bool wait_count(int32_t* counter, int target, int32_t
         met = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      // about a microsecond between polls: hundreds of workgroups polling one
+      // line at a shorter interval slow the tiles they wait for (measured)
+      __builtin_amdgcn_s_sleep(32);
       ++spins;
     }
     *flag = met;
@@ -1053,10 +1121,56 @@ __device__ __forceinline__ bool publish_last(int32_t* counter, int target, int* 
   return last;
 }
 
+// Front phases of a batch of at most kLocalRouteLogits logits: every workgroup
+// computes all of them, the top-k and the dispatch itself (the same device
+// code, so the same bits), keeping the top-k in LDS, and writes the routing
+// arrays and the plan, so no workgroup waits for another; the copies are
+// identical, and each workgroup reads back only what it wrote. Workgroup 0
+// alone writes the logits.
+__device__ __forceinline__ void fused_front_local(const FusedFfnArgs& a, char* lds) {
+  float* srow = reinterpret_cast<float*>(lds + 64);          // [T * E <= 16] logits
+  int32_t* sidx = reinterpret_cast<int32_t*>(lds + 256);     // [T * k <= 16] top-k experts
+  float* sw = reinterpret_cast<float*>(lds + 384);           // [T * k] their weights
+  int32_t* wsum = reinterpret_cast<int32_t*>(lds + 512);     // [8]
+  float* sel = reinterpret_cast<float*>(lds + 1024);         // [8 waves][64]
+  int32_t(*wh)[kMaxExperts] = reinterpret_cast<int32_t(*)[kMaxExperts]>(lds + 4096);  // [8][1024]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nl = static_cast<int>(a.T) * a.E, nk = static_cast<int>(a.T) * a.k;
+  for (int p = wv; p < nl; p += 8) {
+    const float l = gate_logit_wave<1, kFrontLoads>(a.fc1.A, a.wg, a.bias, p / a.E, p % a.E, a.d);
+    if (lane == 0) {
+      srow[p] = l;
+      if (blockIdx.x == 0) a.logits[p] = l;
+    }
+  }
+  __syncthreads();
+  for (int t = wv; t < a.T; t += 8) topk_row(srow + t * a.E, a.E, a.k, sidx + t * a.k, sw + t * a.k, sel + wv * 64);
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < nk) {
+    a.topk_idx[threadIdx.x] = sidx[threadIdx.x];
+    a.topk_w_out[threadIdx.x] = sw[threadIdx.x];
+  }
+  dispatch_block<512>(sidx, nk, a.E, a.counts, a.offsets, a.perm_out, a.inv_perm_out, a.block_rows, a.max_mb,
+                      a.mblocks_out, a.sync + kSyncPlanCount, wh, wsum);
+  // this workgroup's stores are complete, then its L1 is dropped: the FFN
+  // phases read the plan, perm and weights back from memory
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (blockIdx.x == 0) *a.n_mblocks_ws = a.sync[kSyncPlanCount];
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
 // Front phases of the fused launch: route tiles, then the dispatch by the
 // workgroup that stores the last route tile, then the plan. Returns false if
 // this workgroup gave up waiting for the plan (it must then stay away from it).
 __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
+  if (a.T * a.E <= kLocalRouteLogits) {
+    fused_front_local(a, lds);
+    return true;
+  }
   int64_t* s_tile = reinterpret_cast<int64_t*>(lds);
   int* s_flag = reinterpret_cast<int*>(lds + 8);
   float* srow = reinterpret_cast<float*>(lds + 64);        // [<= 64] logits of the token
@@ -1074,7 +1188,7 @@ __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
     __syncthreads();
     if (t >= a.T) break;
     for (int e = wv; e < a.E; e += 8) {
-      const float l = gate_logit_wave<1>(a.fc1.A, a.wg, a.bias, t, e, a.d);
+      const float l = gate_logit_wave<1, kFrontLoads>(a.fc1.A, a.wg, a.bias, t, e, a.d);
       if (lane == 0) {
         srow[e] = l;
         a.logits[t * a.E + e] = l;
@@ -1086,8 +1200,8 @@ __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
       // every route tile is stored: this workgroup dispatches
       if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __syncthreads();
-      dispatch_block<512>(a.topk_idx, a.T * a.k, a.E, a.counts, a.offsets, a.perm_out, a.inv_perm_out, 256, a.max_mb,
-                          a.mblocks_out, a.sync + kSyncPlanCount, wh, wsum);
+      dispatch_block<512>(a.topk_idx, a.T * a.k, a.E, a.counts, a.offsets, a.perm_out, a.inv_perm_out, a.block_rows,
+                          a.max_mb, a.mblocks_out, a.sync + kSyncPlanCount, wh, wsum);
       __syncthreads();
       if (threadIdx.x == 0) *a.n_mblocks_ws = a.sync[kSyncPlanCount];  // where a layer call leaves the count
       publish(a.sync + kSyncPlanReady);
@@ -1096,23 +1210,49 @@ __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
   return wait_count(a.sync + kSyncPlanReady, 1, err, a.spin_limit, s_flag, 2);
 }
 
-template <int BN2, int WM2, int WN2>
+// A value every lane holds the same, moved to scalar registers (the compiler
+// cannot tell that a word read from LDS is uniform).
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// After storing a split tile's part: whether this workgroup stored the tile's
+// last part (then, after an acquire, it sees every part).
+__device__ __forceinline__ bool last_part(int32_t* counter, int parts, int* flag) {
+  if (!publish_last(counter, parts, flag)) return false;
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+  return true;
+}
+
+template <int BM, int BN2, int WM2, int WN2, bool kPacked>
 __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using F1 = DlGemm<kModeFc1, 256, 256, 2, 4>;
-  using F2 = DlGemm<kModeFc2, 256, BN2, WM2, WN2>;
+  using F1 = DlGemm<kModeFc1, BM, 256, 2, 4, kPacked>;
+  using F2 = DlGemm<kModeFc2, BM, BN2, WM2, WN2, kPacked>;
   static_assert(F1::NT == 512 && F2::NT == 512, "both tile forms use 8 waves");
   constexpr int LDS = F1::LDS_BYTES > F2::LDS_BYTES ? F1::LDS_BYTES : F2::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[LDS];
   int64_t* s_tile = reinterpret_cast<int64_t*>(lds);  // the tile buffers are free between tiles
   int* s_flag = reinterpret_cast<int*>(lds + 16);     // (free whenever a wait runs: before a tile's loads)
   if (a.front && !fused_front(a, lds)) return;
-  const int64_t n1 = F1::tiles(a.fc1), n2 = F2::tiles(a.fc2);
-  const int64_t nc = (a.T + kCombineTokens - 1) / kCombineTokens;
+  const int nmb = a.fc1.n_mblocks[0];
   const int nbc1 = static_cast<int>((a.fc1.N + 127) / 128);  // FC1 tiles per m-block
+  const int nbc2 = static_cast<int>((a.fc2.N + BN2 - 1) / BN2);
+  const int64_t nt1 = static_cast<int64_t>(nmb) * nbc1, nt2 = static_cast<int64_t>(nmb) * nbc2;
+  const SplitCut c1 = split_cut(a.fc1, nt1), c2 = split_cut(a.fc2, nt2);
+  // units: whole tiles, then the parts of the split tiles (DlGemm's virtual tiles)
+  const int64_t n1 = c1.full + (nt1 - c1.full) * c1.sp, n2 = c2.full + (nt2 - c2.full) * c2.sp;
+  const int64_t nvec = a.d / 8;
+  const int64_t nc = (a.T * nvec + kCombineVecs - 1) / kCombineVecs;
   int32_t* fc2_done = a.sync + 8;
   int32_t* err = a.sync + kFusedErrorWord;
   int32_t* done1 = a.sync + kFusedSyncHead;
+  int32_t* parts1 = done1 + a.max_mb;
+  int32_t* parts2 = parts1 + kMaxSplitTiles;
   // group x = blockIdx.x % 8 owns, in every round of G tiles, tiles
   // x*W .. x*W + W-1 (W = G / 8): its share of n tiles, and its j-th tile
   const int64_t G = gridDim.x, W = G / 8, x = blockIdx.x % 8;
@@ -1124,20 +1264,48 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
     if (threadIdx.x == 0)
       *s_tile = __hip_atomic_fetch_add(a.sync + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int64_t j = *s_tile;
+    const int64_t j = uniform(*s_tile);  // the same in every lane: scalar registers
     __syncthreads();  // every thread has read it before the tile's loads refill the buffers
     if (j < s1) {
-      F1::tile(a.fc1, lds, nth(j), [](int) {}, [&](int mb) { publish(done1 + mb); });
+      const int64_t v = nth(j);
+      F1::tile(a.fc1, lds, v, [](int) {}, [&](int mb) {
+        if (v < c1.full) {
+          publish(done1 + mb);
+        } else {
+          const int64_t t = c1.full + (v - c1.full) / c1.sp;
+          if (last_part(parts1 + (t - c1.full), c1.sp, s_flag)) {
+            reduce_split_tile<true, BM, 256, 4>(a.fc1, t, c1, nbc1, nmb, threadIdx.x, 512);
+            publish(done1 + mb);
+            publish(a.sync + kSyncSplit1Done);
+          }
+        }
+      });
     } else if (j < s1 + s2) {
-      F2::tile(a.fc2, lds, nth(j - s1), [&](int mb) { wait_count(done1 + mb, nbc1, err, a.spin_limit, s_flag); },
-               [&](int) { publish(fc2_done); });
+      const int64_t v = nth(j - s1);
+      const bool part = v >= c2.full;
+      F2::tile(a.fc2, lds, v,
+               [&](int mb) {
+                 wait_count(done1 + mb, nbc1, err, a.spin_limit, s_flag);
+                 // the partial buffer is free once every split FC1 tile is summed
+                 if (part && c1.sp > 1)
+                   wait_count(a.sync + kSyncSplit1Done, static_cast<int>(nt1 - c1.full), err, a.spin_limit, s_flag);
+               },
+               [&](int) {
+                 if (!part) {
+                   publish(fc2_done);
+                 } else {
+                   const int64_t t = c2.full + (v - c2.full) / c2.sp;
+                   if (last_part(parts2 + (t - c2.full), c2.sp, s_flag)) {
+                     reduce_split_tile<false, BM, BN2, WN2>(a.fc2, t, c2, nbc2, nmb, threadIdx.x, 512);
+                     publish(fc2_done);
+                   }
+                 }
+               });
     } else if (j < s1 + s2 + sc) {
-      wait_count(fc2_done, static_cast<int>(n2), err, a.spin_limit, s_flag);
-      const int64_t t0 = nth(j - s1 - s2) * kCombineTokens;
-      const int64_t nt = a.T - t0 < kCombineTokens ? a.T - t0 : kCombineTokens;
-      const int64_t nvec = a.d / 8;
-      for (int64_t q = threadIdx.x; q < nt * nvec; q += 512)
-        combine_vec<1>(a.fc2.C, a.inv_perm, a.topk_w, a.out, a.d, a.k, a.T * a.k, a.n_shared, a.T, t0 + q / nvec,
+      wait_count(fc2_done, static_cast<int>(nt2), err, a.spin_limit, s_flag);
+      const int64_t q = nth(j - s1 - s2) * kCombineVecs + threadIdx.x;
+      if (q < a.T * nvec)
+        combine_vec<1>(a.fc2.C, a.inv_perm, a.topk_w, a.out, a.d, a.k, a.T * a.k, a.n_shared, a.T, q / nvec,
                        q % nvec);
     } else {
       break;
@@ -1146,44 +1314,16 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
 #endif
 }
 
-// Second half of a split launch: per output element of every split tile, the
-// sum of its parts in part order, then what the GEMM's bf16 epilogue applies:
-// SiLU(g) * u for FC1 (a wave's TN accumulator columns hold TN/2 gate columns
-// then the TN/2 up columns of the same outputs), bf16 rounding.
 template <bool kGated, int BM, int BN, int WN>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
-  constexpr int OC = kGated ? BN / 2 : BN;  // output columns of a tile
-  constexpr int TN = BN / WN;
-  const int64_t N = g.N;
-  const int nbc = static_cast<int>((N + OC - 1) / OC);
+  constexpr int OC = kGated ? BN / 2 : BN;
+  const int nbc = static_cast<int>((g.N + OC - 1) / OC);
   const int nmb = g.n_mblocks[0];
   const int64_t nt = static_cast<int64_t>(nmb) * nbc;
   const SplitCut cut = split_cut(g, nt);
-  const int sp = cut.sp;
-  if (sp <= 1) return;  // the GEMM wrote its outputs itself
-  bf16_t* C = static_cast<bf16_t*>(g.C);
-  for (int64_t t = cut.full + blockIdx.x; t < nt; t += gridDim.x) {
-    int mb, nb;
-    decode_group_tile(g, t, nbc, nmb, mb, nb);
-    const int4 blk = g.mblocks[mb];
-    const int row0 = blk.y, rows = blk.z;
-    const float* part = g.partial + (t - cut.full) * sp * (BM * BN);
-    for (int q = threadIdx.x; q < rows * OC; q += blockDim.x) {
-      const int r = q / OC, oc = q % OC;
-      const int64_t col = static_cast<int64_t>(nb) * OC + oc;
-      if (col >= N) continue;
-      const int pc = kGated ? (oc / (TN / 2)) * TN + oc % (TN / 2) : oc;
-      const float* src = part + r * BN + pc;
-      float a = src[0];
-      float b = kGated ? src[TN / 2] : 0.f;
-      for (int p = 1; p < sp; ++p) {
-        a += src[p * (BM * BN)];
-        if constexpr (kGated) b += src[p * (BM * BN) + TN / 2];
-      }
-      const float v = kGated ? silu_mul(a, b) : a;
-      C[static_cast<int64_t>(row0 + r) * N + col] = static_cast<bf16_t>(f32_to_bf16_bits(v));
-    }
-  }
+  if (cut.sp <= 1) return;  // the GEMM wrote its outputs itself
+  for (int64_t t = cut.full + blockIdx.x; t < nt; t += gridDim.x)
+    reduce_split_tile<kGated, BM, BN, WN>(g, t, cut, nbc, nmb, threadIdx.x, blockDim.x);
 }
 
 // Stage order of one expert-weight tensor W [E][N][K] (bf16, N and K multiples
@@ -1330,20 +1470,31 @@ static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, h
 // CUs and a second kernel sums them. (Splitting only the last partial round
 // of a large launch was measured too: the halves and thirds of tiles it adds
 // cost as much as the idle CUs they fill.)
+// Whether a forward launch over up to max_mb m-blocks x nb column blocks
+// (tiles of tile_floats fp32 accumulators) splits K, given a partial buffer of
+// partial_bytes (0: none), and if so its split fields in a. The fused launch
+// takes the same decision, so its tiles split the same way.
+static bool fwd_split(GemmArgs& a, int64_t max_mb, int64_t nb, int64_t tile_floats, float* partial,
+                      size_t partial_bytes) {
+  const int64_t cus = device_cu_count();
+  const int parts = split_k_parts(a.K);
+  const int64_t cap = static_cast<int64_t>(partial_bytes / (sizeof(float) * tile_floats));
+  if (partial_bytes == 0 || parts < 2 || max_mb * nb >= cus || max_mb * nb * 2 > cap) return false;
+  a.partial = partial;
+  a.splits = parts;
+  a.split_target = static_cast<int>(cus);
+  a.partial_cap = static_cast<int>(cap);
+  return true;
+}
+
 template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* partial, size_t partial_bytes,
                              hipStream_t s) {
   const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
   const int64_t nb = (ncols + cols - 1) / cols;
   const int64_t cus = device_cu_count();
-  const int parts = split_k_parts(a.K);
-  const int64_t cap = static_cast<int64_t>(partial_bytes / (sizeof(float) * BM * BN));
-  if (partial == nullptr || parts < 2 || max_mb * nb >= cus || max_mb * nb * 2 > cap)
+  if (!fwd_split(a, max_mb, nb, static_cast<int64_t>(BM) * BN, partial, partial_bytes))
     return launch_big<kMode, BM, BN, WM, WN, kPacked>(a, max_mb, ncols, s);
-  a.partial = partial;
-  a.splits = parts;
-  a.split_target = static_cast<int>(cus);
-  a.partial_cap = static_cast<int>(cap);
   hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN, kPacked>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
                      a);
   if (hipError_t err = hipGetLastError()) return err;
@@ -1376,23 +1527,25 @@ hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm,
   return hipGetLastError();
 }
 
+// Few m-blocks (decode-sized batches, weight streaming): 256-column FC2 tiles
+// can leave CUs idle (Mixtral-8x22B decode: 8 x 24 tiles for 256 CUs);
+// 192-column tiles (8 x 32 there, one per CU) are taken when their rounds of
+// tiles cost less for the expected number of m-blocks. Regime 2 keeps 256.
+static bool fc2_narrow(int regime, int64_t est_mb, int64_t d) {
+  const int64_t cus = device_cu_count();
+  if (regime == 2 || est_mb * ((d + 255) / 256) >= 2 * cus) return false;
+  const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
+  const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
+  return t192 < t256;
+}
+
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
                       const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d,
              0, sh.w2, nullptr, sh.n > 0 ? sh.E_routed : INT32_MAX};
   if (dtype == 1 && regime >= 1) {
-    // Few m-blocks (decode-sized batches, weight streaming): 256-column tiles
-    // can leave CUs idle (Mixtral-8x22B decode: 8 x 24 tiles for 256 CUs);
-    // 192-column tiles (8 x 32 there, one per CU) are taken when their rounds
-    // of tiles cost less for the expected number of m-blocks. Regime 2 keeps 256.
-    const int64_t cus = device_cu_count();
-    bool narrow = false;
-    if (regime != 2 && est_mb * ((d + 255) / 256) < 2 * cus) {
-      const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
-      const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
-      narrow = t192 < t256;
-    }
+    const bool narrow = fc2_narrow(regime, est_mb, d);
     if (packed) {  // W2 in stage order (pack_weights_kernel)
       if (regime == 3)
         return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s)
@@ -1452,32 +1605,63 @@ hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, con
   return hipGetLastError();
 }
 
-size_t fused_sync_words(int64_t max_mb) { return static_cast<size_t>(kFusedSyncHead + max_mb); }
-
-// Grid and FC2 tile width of the fused launch: a multiple of 8 workgroups
-// (every tile group must have workgroups), at most one per CU; FC2 tiles 256
-// or, under the same rule as launch_fc2, 192 columns wide.
-static void fused_shape(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, int64_t* grid, bool* narrow) {
-  const int64_t cus = device_cu_count();
-  *narrow = false;
-  if (est_mb * ((d + 255) / 256) < 2 * cus) {
-    const int64_t t256 = (est_mb * ((d + 255) / 256) + cus - 1) / cus * 256;
-    const int64_t t192 = (est_mb * ((d + 191) / 192) + cus - 1) / cus * 192;
-    *narrow = t192 < t256;
-  }
-  int64_t g = std::min<int64_t>(max_mb * ((f + 127) / 128), cus) / 8 * 8;
-  *grid = g < 8 ? 8 : g;
+size_t fused_sync_words(int64_t max_mb) {
+  return static_cast<size_t>(kFusedSyncHead + max_mb + 2 * kMaxSplitTiles);
 }
 
-bool ffn_fused_coresident(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f) {
-  int64_t grid;
-  bool narrow;
-  fused_shape(max_mb, est_mb, d, f, &grid, &narrow);
+// One form of the fused kernel: launched (per_cu null) or its occupancy queried.
+template <int BM, int BN2, int WM2, int WN2, bool kPacked>
+static hipError_t fused_form(const FusedFfnArgs* a, int grid, hipStream_t s, int* per_cu) {
+  if (per_cu)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, ffn_fused_kernel<BM, BN2, WM2, WN2, kPacked>, 512, 0);
+  hipLaunchKernelGGL((ffn_fused_kernel<BM, BN2, WM2, WN2, kPacked>), dim3(grid), dim3(512), 0, s, *a);
+  return hipGetLastError();
+}
+
+template <bool kPacked>
+static hipError_t fused_form_rows(bool rows128, bool narrow, const FusedFfnArgs* a, int grid, hipStream_t s,
+                                  int* per_cu) {
+  // the separate launches' tile forms (launch_fc1, launch_fc2)
+  if (rows128)
+    return narrow ? fused_form<128, 192, 2, 4, kPacked>(a, grid, s, per_cu)
+                  : fused_form<128, 256, 2, 4, kPacked>(a, grid, s, per_cu);
+  return narrow ? fused_form<256, 192, 4, 2, kPacked>(a, grid, s, per_cu)
+                : fused_form<256, 256, 2, 4, kPacked>(a, grid, s, per_cu);
+}
+
+// Tile form, split fields and grid of a fused launch (args a with fc1/fc2
+// set): the separate launches' choices for the same regime, a multiple of 8
+// workgroups (every tile group must have workgroups), at most one per CU, all
+// CUs when a phase splits.
+struct FusedShape {
+  bool rows128, narrow;
+  int grid;
+};
+static FusedShape fused_shape(FusedFfnArgs& a, int regime, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                              float* partial, size_t partial_bytes) {
+  FusedShape sh{};
+  sh.rows128 = regime == 3;
+  sh.narrow = fc2_narrow(regime, est_mb, d);
+  const int64_t bm = sh.rows128 ? 128 : 256, bn2 = sh.narrow ? 192 : 256;
+  const bool sp1 = fwd_split(a.fc1, max_mb, (f + 127) / 128, bm * 256, partial, partial_bytes);
+  const bool sp2 = fwd_split(a.fc2, max_mb, (d + bn2 - 1) / bn2, bm * bn2, partial, partial_bytes);
+  const int64_t cus = device_cu_count();
+  const int64_t g = (sp1 || sp2 ? cus : std::min<int64_t>(max_mb * ((f + 127) / 128), cus)) / 8 * 8;
+  sh.grid = static_cast<int>(g < 8 ? 8 : g);
+  return sh;
+}
+
+bool ffn_fused_coresident(int regime, bool packed, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                          size_t partial_bytes) {
+  FusedFfnArgs a{};
+  a.fc1.K = d;
+  a.fc2.K = f;
+  // (the buffer's size decides whether a phase splits; its address is not needed here)
+  const FusedShape sh = fused_shape(a, regime, max_mb, est_mb, d, f, nullptr, partial_bytes);
   int per_cu = 0;
-  const hipError_t e =
-      narrow ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_fused_kernel<192, 4, 2>, 512, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_fused_kernel<256, 2, 4>, 512, 0);
-  return e == hipSuccess && static_cast<int64_t>(per_cu) * device_cu_count() >= grid;
+  const hipError_t e = packed ? fused_form_rows<true>(sh.rows128, sh.narrow, &a, sh.grid, nullptr, &per_cu)
+                              : fused_form_rows<false>(sh.rows128, sh.narrow, &a, sh.grid, nullptr, &per_cu);
+  return e == hipSuccess && static_cast<int64_t>(per_cu) * device_cu_count() >= sh.grid;
 }
 
 bool fused_front_ok(int64_t T, int E, int k) {
@@ -1488,10 +1672,11 @@ bool fused_front_ok(int64_t T, int E, int k) {
 
 // (Route, dispatch,) FC1, FC2 and combine in one launch (bf16). The sync words
 // must be zero on entry.
-hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
-                            const void* w2, void* h, void* y, int4* mblocks, int32_t* n_mblocks,
-                            int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
-                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, int spin_limit,
+hipError_t launch_ffn_fused(int regime, bool packed, const void* x, const int32_t* perm, int k, int64_t T,
+                            const void* w1, const void* w3, const void* w2, void* h, void* y, int4* mblocks,
+                            int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                            const int32_t* inv_perm, const float* topk_w, void* out, int32_t* sync,
+                            const SharedExperts& sh, float* partial, size_t partial_bytes, int spin_limit,
                             const FusedFront& front, hipStream_t s) {
   FusedFfnArgs a{};
   a.fc1 = GemmArgs{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f, T * k, sh.w1, sh.w3,
@@ -1507,6 +1692,8 @@ hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T
   a.n_shared = sh.n;
   a.sync = sync;
   a.spin_limit = spin_limit;
+  a.max_mb = max_mb;
+  a.block_rows = regime_block_rows(regime);
   if (front.on) {
     // the launch routes and dispatches first; its FFN phases read the plan's
     // count from the sync words
@@ -1523,17 +1710,11 @@ hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T
     a.inv_perm_out = front.inv_perm;
     a.mblocks_out = mblocks;
     a.n_mblocks_ws = n_mblocks;
-    a.max_mb = max_mb;
     a.fc1.n_mblocks = a.fc2.n_mblocks = sync + kSyncPlanCount;
   }
-  int64_t grid;
-  bool narrow;
-  fused_shape(max_mb, est_mb, d, f, &grid, &narrow);
-  if (narrow)
-    hipLaunchKernelGGL((ffn_fused_kernel<192, 4, 2>), dim3(grid), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((ffn_fused_kernel<256, 2, 4>), dim3(grid), dim3(512), 0, s, a);
-  return hipGetLastError();
+  const FusedShape fs = fused_shape(a, regime, max_mb, est_mb, d, f, partial, partial_bytes);
+  return packed ? fused_form_rows<true>(fs.rows128, fs.narrow, &a, fs.grid, s, nullptr)
+                : fused_form_rows<false>(fs.rows128, fs.narrow, &a, fs.grid, s, nullptr);
 }
 
 }  // namespace moe

@@ -85,14 +85,17 @@ hipError_t launch_pack_weights_t(const void* w1t, const void* w3t, const void* w
 size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, int64_t f);
 
 // FC1, FC2 and the combine in one persistent launch with device-side
-// readiness counters (bf16). sync: fused_sync_words(max_mb) int32, zero on
-// entry; word kFusedErrorWord gets bit 0 set when a readiness wait gave up
-// after spin_limit polls (< 0: at once).
+// readiness counters (bf16), with the tile form, weight layout (packed: stage
+// order) and K split that launch_fc1 / launch_fc2 take for the same regime
+// and partial buffer. sync: fused_sync_words(max_mb) int32, zero on entry;
+// word kFusedErrorWord gets bit 0 set when a readiness wait gave up after
+// spin_limit polls (< 0: at once).
 size_t fused_sync_words(int64_t max_mb);
 constexpr int kFusedErrorWord = 9;
-constexpr int kFusedSpinLimit = 1 << 22;
+constexpr int kFusedSpinLimit = 1 << 18;  // polls about a microsecond apart: a quarter of a second
 // every workgroup of the fused launch for this shape can be resident at once
-bool ffn_fused_coresident(int64_t max_mb, int64_t est_mb, int64_t d, int64_t f);
+bool ffn_fused_coresident(int regime, bool packed, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                          size_t partial_bytes);
 // Route and dispatch as the fused launch's first phases (bf16, no shared
 // experts, E <= 64, T*k <= kFusedMaxAssign): the launch then writes the
 // routing outputs and the plan itself, and the m-block count ends up at
@@ -111,10 +114,11 @@ struct FusedFront {
   int E = 0;
 };
 bool fused_front_ok(int64_t T, int E, int k);
-hipError_t launch_ffn_fused(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
-                            const void* w2, void* h, void* y, int4* mblocks, int32_t* n_mblocks,
-                            int64_t max_mb, int64_t est_mb, int64_t d, int64_t f, const int32_t* inv_perm,
-                            const float* topk_w, void* out, int32_t* sync, const SharedExperts& sh, int spin_limit,
+hipError_t launch_ffn_fused(int regime, bool packed, const void* x, const int32_t* perm, int k, int64_t T,
+                            const void* w1, const void* w3, const void* w2, void* h, void* y, int4* mblocks,
+                            int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
+                            const int32_t* inv_perm, const float* topk_w, void* out, int32_t* sync,
+                            const SharedExperts& sh, float* partial, size_t partial_bytes, int spin_limit,
                             const FusedFront& front, hipStream_t s);
 
 // Weighted combine.

@@ -378,17 +378,23 @@ int fused_spin_limit() {
   return kFusedSpinLimit;
 }
 
+// The fused launch's regime: the separate launches' (the small-tile regime 0,
+// forced through the environment only, becomes the 256-row one).
+int fused_regime(const moe_dims_t* dm) { return layer_regime(dm, true); }
+
 int do_ffn_fused(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* inv_perm,
                  const float* topk_w, const void* w1, const void* w3, const void* w2, void* y, void* out,
-                 const FfnWs& fw, const SharedExperts& sh, hipStream_t s, const FusedFront& front = FusedFront{}) {
-  const int64_t est_mb = expected_mblocks(dm, 256, fw.max_mb, sh.n);
+                 const FfnWs& fw, const SharedExperts& sh, hipStream_t s, bool packed,
+                 const FusedFront& front = FusedFront{}) {
+  const int regime = fused_regime(dm);
+  const int64_t est_mb = expected_mblocks(dm, regime_block_rows(regime), fw.max_mb, sh.n);
   if (int st = hip_status(launch_fill_zero(reinterpret_cast<float*>(fw.sync),
                                            static_cast<int64_t>(fused_sync_words(fw.max_mb)), s)))
     return st;
   StageScope sc(MOE_STAGE_FFN_FUSED, s);
-  return hip_status(launch_ffn_fused(x, perm, dm->k, dm->T, w1, w3, w2, fw.h, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
-                                     est_mb, dm->d, dm->f, inv_perm, topk_w, out, fw.sync, sh, fused_spin_limit(), front,
-                                     s));
+  return hip_status(launch_ffn_fused(regime, packed, x, perm, dm->k, dm->T, w1, w3, w2, fw.h, y, fw.mblocks,
+                                     fw.n_mblocks, fw.max_mb, est_mb, dm->d, dm->f, inv_perm, topk_w, out, fw.sync, sh,
+                                     fw.partial, fw.partial_bytes, fused_spin_limit(), front, s));
 }
 
 int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, const void* wg, const float* bias,
@@ -407,8 +413,12 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
   if (ws_bytes < layer_ws(dm, nullptr, nullptr, sh.n)) return MOE_ERR_WORKSPACE;
   if (fused) {
     // the fused launch's readiness waits need every workgroup resident at once
-    const int64_t max_mb = max_mblocks(ffn_rows(dm, sh.n), dm->E + sh.n);
-    if (!ffn_fused_coresident(max_mb, expected_mblocks(dm, 256, max_mb, sh.n), dm->d, dm->f))
+    FfnWs sz{};
+    ffn_ws(dm, nullptr, &sz, sh.n);
+    const int regime = fused_regime(dm);
+    if (!ffn_fused_coresident(regime, packed, sz.max_mb,
+                              expected_mblocks(dm, regime_block_rows(regime), sz.max_mb, sh.n), dm->d, dm->f,
+                              sz.partial_bytes))
       return MOE_ERR_UNSUPPORTED;
   }
   LayerWs lw{};
@@ -438,7 +448,7 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
     front.perm = perm;
     front.inv_perm = inv_perm;
     front.E = dm->E;
-    return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s, front);
+    return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s, packed, front);
   }
   if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
   if (use_fused_dispatch(n)) {
@@ -447,7 +457,8 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
     {
       StageScope sc(MOE_STAGE_DISPATCH, s);
       if (int st = hip_status(launch_dispatch_fused(topk_idx, n, dm->E, counts, offsets, perm, inv_perm,
-                                                    fused ? 256 : regime_block_rows(layer_regime(dm, packed)), fw.max_mb,
+                                                    regime_block_rows(fused ? fused_regime(dm) : layer_regime(dm, packed)),
+                                                    fw.max_mb,
                                                     plan_inline ? fw.mblocks : nullptr,
                                                     plan_inline ? fw.n_mblocks : nullptr, s)))
         return st;
@@ -455,11 +466,11 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
     if (fused) {
       if (!plan_inline) {
         StageScope sc(MOE_STAGE_PLAN, s);
-        if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, 256, fw.mblocks, fw.n_mblocks, s,
-                                            sh.n, dm->T)))
+        if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, regime_block_rows(fused_regime(dm)),
+                                            fw.mblocks, fw.n_mblocks, s, sh.n, dm->T)))
           return st;
       }
-      return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s);
+      return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s, packed);
     }
     if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, plan_inline, sh, packed)) return st;
   } else {
@@ -469,11 +480,11 @@ int run_layer(const moe_dims_t* dm, const SharedExperts& sh, const void* x, cons
     if (fused) {
       {
         StageScope sc(MOE_STAGE_PLAN, s);
-        if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, 256, fw.mblocks, fw.n_mblocks, s,
-                                            sh.n, dm->T)))
+        if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, regime_block_rows(fused_regime(dm)),
+                                            fw.mblocks, fw.n_mblocks, s, sh.n, dm->T)))
           return st;
       }
-      return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s);
+      return do_ffn_fused(dm, x, perm, inv_perm, topk_w, w1, w3, w2, lw.y, out, fw, sh, s, packed);
     }
     if (int st = do_ffn(dm, x, perm, counts, offsets, w1, w3, w2, lw.y, fw, s, false, sh, packed)) return st;
   }
@@ -632,6 +643,14 @@ int moe_layer_forward_fused(const moe_dims_t* dm, const void* x, const void* wg,
                             int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(dm, SharedExperts{}, x, wg, bias, w1, w3, w2, out, logits, topk_idx, topk_w, counts, offsets,
                    perm, inv_perm, ws, ws_bytes, stream, true);
+}
+
+int moe_layer_forward_fused_packed(const moe_dims_t* dm, const void* x, const void* wg, const float* bias,
+                                   const void* w1p, const void* w3p, const void* w2p, void* out, float* logits,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  return run_layer(dm, SharedExperts{}, x, wg, bias, w1p, w3p, w2p, out, logits, topk_idx, topk_w, counts, offsets,
+                   perm, inv_perm, ws, ws_bytes, stream, true, true);
 }
 
 int moe_fused_status(const moe_dims_t* dm, const void* ws, size_t ws_bytes, int32_t* flags, void* stream) {

@@ -53,13 +53,14 @@ __device__ __forceinline__ float mac(float x, float w, float acc) {
 
 // Logit (t, e) computed by one wave in the contract order: lane q sums class q
 // (elements q, q + 64, .. in order), then the butterfly over offsets 32 .. 1
-// and the bias. Every lane calls it; lane 0 holds the logit.
-template <int kDtype>
+// and the bias. Every lane calls it; lane 0 holds the logit. The loads of U
+// elements per lane are issued before their multiply-adds: a logit of a
+// small batch is a chain of d / (64 U) memory round trips.
+template <int kDtype, int U = 32>
 __device__ __forceinline__ float gate_logit_wave(const void* __restrict__ x, const void* __restrict__ wg,
                                                  const float* __restrict__ bias, int64_t t, int e, int64_t d) {
   const int lane = threadIdx.x & 63;
   const int64_t xrow = t * d, wrow = static_cast<int64_t>(e) * d;
-  constexpr int U = 8;
   float acc = 0.0f;
   int64_t i0 = lane;
   for (; i0 + (U - 1) * 64 < d; i0 += U * 64) {

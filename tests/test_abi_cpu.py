@@ -134,6 +134,12 @@ def test_packed_validation():
     assert fwd(w1p=None) == 1
     assert fwd(wsb=1024) == 3
     assert fwd(dims=_dims(T=0)) == 0
+    ffwd = lambda dims=dm, w1p=A, wsb=1 << 40: lib.moe_layer_forward_fused_packed(  # noqa: E731
+        ctypes.byref(dims), A, A, None, w1p, A, A, A, None, None, None, None, None, None, None, A, wsb, None)
+    assert ffwd(dims=_dims(dtype=0)) == 2
+    assert ffwd(w1p=None) == 1
+    assert ffwd(wsb=1024) == 3
+    assert ffwd(dims=_dims(T=0)) == 0
 
 
 @needs_no_gpu

@@ -3,11 +3,16 @@ FC1, FC2 and the combine in one persistent kernel with device-side readiness
 counters; MOE_FUSED_FRONT=0 keeps route and dispatch as separate launches before
 it, and both forms are tested.
 
-Its tiles do exactly the arithmetic of moe_layer_forward's separate launches
-when those do not split K (MOE_SPLIT_K=0), so the bar is bitwise equality with that path (itself held to the oracle in
+Its tiles do exactly the arithmetic of moe_layer_forward's separate launches:
+the same rows per block, FC2 tile width, weight layout and, for launches with
+fewer tiles than compute units, the same split of K, whose parts the workgroup
+storing the last one sums in the separate reduce's order. So the bar is
+bitwise equality with that path (itself held to the oracle in
 test_gpu_parity.py), checked twice in a row on the same buffers (a missed
 wait or a stale read would show up as a difference), plus the oracle bar on
-small shapes directly.
+small shapes directly. Shapes with split FC1 and FC2 tiles (FC2 parts then
+wait for every split FC1 tile to be summed) run in both tile regimes, and once
+with splitting turned off on both sides.
 """
 import sys
 
@@ -25,10 +30,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True, params=["front", "ffn_only"])
-def _whole_k(monkeypatch, request):
-    # the fused kernel never splits K; the separate launches it is compared with
-    # bit for bit must not either
-    monkeypatch.setenv("MOE_SPLIT_K", "0")
+def _front(monkeypatch, request):
+    monkeypatch.delenv("MOE_SPLIT_K", raising=False)
     if request.param == "ffn_only":
         monkeypatch.setenv("MOE_FUSED_FRONT", "0")
     else:
@@ -40,7 +43,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _both(cfg_or_shape, seed=0):
+def _both(cfg_or_shape, seed=0, packed=False):
     if isinstance(cfg_or_shape, str):
         cfg = moe_inputs.config(cfg_or_shape)
         inp = moe_inputs.make_layer_inputs(cfg, seed, "cuda")
@@ -49,13 +52,14 @@ def _both(cfg_or_shape, seed=0):
         T, d, f, E, k, s = cfg_or_shape
         inp = moe_inputs.random_inputs(T, d, f, E, k, "bf16", s, seed, device="cuda")
     dims = moe.Dims(T, d, f, E, k, torch.bfloat16)
+    pk = moe.pack_weights(dims, inp["w1"], inp["w3"], inp["w2"]) if packed else None
     ref, r_ref = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
-                                   return_routing=True)
+                                   return_routing=True, packed=pk)
     ws = moe.make_workspace(dims)
     outs = []
     for _ in range(2):
         out, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], ws=ws,
-                                   return_routing=True, fused=True)
+                                   return_routing=True, fused=True, packed=pk)
         torch.cuda.synchronize()
         # every readiness wait of the launch was met: its outputs are valid
         assert moe.fused_status(dims, ws) == 0
@@ -65,7 +69,7 @@ def _both(cfg_or_shape, seed=0):
         outs.append(out.clone())
     # the tile plan the fused launch used, where a layer call leaves it
     plan = moe.read_plan(dims, ws).numpy()
-    check_plan(plan, r_ref["counts"].cpu().numpy(), r_ref["offsets"].cpu().numpy(), 256, T * k)
+    check_plan(plan, r_ref["counts"].cpu().numpy(), r_ref["offsets"].cpu().numpy(), moe.ffn_block_rows(dims), T * k)
     return inp, ref, outs, r
 
 
@@ -94,15 +98,55 @@ def test_fused_small_bitwise_and_oracle(shape):
     assert err <= OUT_TOL
 
 
+SPLIT_SHAPES = [
+    # T, d, f, E, k, bias scale: fewer tiles than CUs, K of 1024 or more
+    (1, 1024, 1024, 8, 2, 0.0),      # 128-row tiles, FC1 and FC2 split
+    (300, 1024, 1024, 4, 2, 1.0),    # 256-row tiles, FC1 and FC2 split
+    (16, 2048, 4096, 8, 2, 0.0),     # FC1 whole, FC2 in 4 parts of 16 K steps
+    (5, 1536, 1024, 16, 4, 2.0),     # FC1 in 3 parts, FC2 in 2
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
+def test_fused_split_k_bitwise_and_oracle(shape):
+    test_fused_small_bitwise_and_oracle(shape)
+
+
+def test_fused_whole_k_when_splitting_is_off(monkeypatch):
+    """MOE_SPLIT_K=0 turns splitting off for both forms alike."""
+    monkeypatch.setenv("MOE_SPLIT_K", "0")
+    test_fused_small_bitwise_and_oracle(SPLIT_SHAPES[0])
+
+
+@pytest.mark.parametrize("shape", [SPLIT_SHAPES[0], SPLIT_SHAPES[1], FUSED_SHAPES[1], FUSED_SHAPES[5]],
+                         ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
+def test_fused_packed_bitwise(shape):
+    """moe_layer_forward_fused_packed against moe_layer_forward_packed."""
+    _say(f"case fused packed {shape}")
+    _, ref, outs, _ = _both(shape, packed=True)
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill_skew", "dbrx_zipf", "deepseek_skew",
-                                  "deepseek_bal"])
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_decode_t1", "mixtral_decode_t16", "mixtral_prefill_skew",
+                                  "dbrx_zipf", "deepseek_skew", "deepseek_bal"])
 def test_fused_full_size_bitwise(name):
     _say(f"case fused full {name}")
     _, ref, outs, _ = _both(name)
     for o in outs:
         assert torch.equal(o, ref)
     _say("  bitwise equal to the separate launches, twice")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_decode_t1", "mixtral_prefill_skew"])
+def test_fused_packed_full_size_bitwise(name):
+    _say(f"case fused packed full {name}")
+    _, ref, outs, _ = _both(name, packed=True)
+    for o in outs:
+        assert torch.equal(o, ref)
+    _say("  bitwise equal to the separate packed launches, twice")
 
 
 def test_fused_reports_a_wait_that_gave_up(monkeypatch):
