@@ -453,12 +453,80 @@ struct DlGemm {
     return c.full + (nt - c.full) * c.sp;
   }
 
+  // Forward tiles of a workgroup can be chained: the last K steps of one tile
+  // issue the first loads of the next (into the buffers those steps free), and
+  // its epilogue stores straight from registers, so the next tile starts with
+  // its first stages already in LDS or in flight. The next tile's load offsets
+  // then stay in registers through the whole K loop, which only the 128-row
+  // forms have room for (the 256-row ones would spill inside the loop).
+  static constexpr bool kChain = (kMode == kModeFc1 || kMode == kModeFc2) && BM == 128;
+
+  // Where a tile's operands come from: its place in the launch, its K steps
+  // and the buffer descriptors and per-lane offsets of its A and B loads.
+  struct Desc {
+    int64_t tile, pslot;
+    int sp, part, mb, nb, e, row0, rows, kt0, nk;
+    __amdgpu_buffer_rsrc_t ars, brs0, brs1;
+    uint32_t aoff[AI], boff[BI];
+  };
+
   template <class Pre, class Post>
   __device__ static __forceinline__ void tile(const GemmArgs& g, char* lds, int64_t vtile, Pre pre, Post post) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    Desc t;
+    describe(g, vtile, t);
+    pre(t.mb);  // the tile's operands are ready (fused kernels wait here)
+    run_tile(g, lds, t, t, 0, 0, false, post);
+#endif
+  }
+
+  static constexpr int PH = (RPI / R256) % CPR;  // swizzle phase step per load instruction (0 or 4)
+  // Chunk a lane fetches for a load instruction whose first row is R0 (a
+  // multiple of RPI): f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR, and
+  // R0 / R256 mod CPR is 0 for 64-byte rows and 0 or 4 for 128-byte rows
+  // (alternating with the instruction index: r0_phase).
+  __device__ static __forceinline__ uint32_t chunk_off(int lane, int r0_phase) {
+    return static_cast<uint32_t>(((lane % CPR) ^ ((r0_phase + (lane / CPR) / R256) % CPR)) * 16);
+  }
+  // Forward weights (FC1, FC2; as stored or in stage order): the offset of the
+  // 16 bytes load instruction i of wave wv fetches for column block nb.
+  // Weights as stored, or (kPacked) in the stage order of pack_weights_kernel:
+  // the 64-row group g of an expert's matrix is K / 64 blocks of 8 KiB, block
+  // kt holding rows 64g.. x K elements 64kt.. already swizzled as the LDS
+  // stage expects, so the lane of stage row r and slot c reads 16 bytes at
+  // (g * K/64 + kt) * 8192 + (r % 64) * 128 + c * 16. The stage's column
+  // block starts on a multiple of 64 rows, so r % 64 is the row's place in
+  // its group and the swizzle matches.
+  __device__ static __forceinline__ uint32_t fwd_b_off(const GemmArgs& g, int nb, int i, int wv, int lane) {
+    const int64_t K = g.K, N = g.N;
+    const int r = (wv * BI + i) * RPI + lane / CPR;
+    int64_t n;
+    if constexpr (kGated)
+      n = static_cast<int64_t>(nb) * (BN / 2) + (r % (BN / 2));
+    else
+      n = static_cast<int64_t>(nb) * BN + r;
+    if constexpr (kPacked) {
+      int64_t grp = n / 64;
+      if (grp >= N / 64) grp = N / 64 - 1;  // column tail: a valid group, never stored
+      return static_cast<uint32_t>(grp * (K / 64) * 8192 + (r % 64) * 128 + (lane % CPR) * 16);
+    } else {
+      if (n >= N) n = N - 1;  // column tail: computed on a valid row, never stored
+      return static_cast<uint32_t>(n * K * 2) + chunk_off(lane, ((wv * BI + i) * PH) % CPR);
+    }
+  }
+  // A rows of a block read in place (FC2 and the other non-gathered forms):
+  // row r of `rows` at pitch ap; rows past the end get an offset at the
+  // descriptor's size (the load returns zeros and makes no memory request).
+  __device__ static __forceinline__ uint32_t plain_a_off(int64_t ap, int rows, int i, int wv, int lane) {
+    const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * ap * 2);
+    const int r = (wv * AI + i) * RPI + lane / CPR;
+    return r < rows ? static_cast<uint32_t>(r * ap * 2) + chunk_off(lane, ((wv * AI + i) * PH) % CPR) : hb;
+  }
+
+  __device__ static __forceinline__ void describe(const GemmArgs& g, int64_t vtile, Desc& d) {
+#if defined(__HIP_DEVICE_COMPILE__)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
-    const int wm = wv / WN, wn = wv % WN;
     const int64_t K = g.K, N = g.N;
     const int nbc = kGated ? static_cast<int>((N + BN / 2 - 1) / (BN / 2)) : static_cast<int>((N + BN - 1) / BN);
     // weight gradients: every expert has M / BM m-blocks of output rows
@@ -480,15 +548,7 @@ struct DlGemm {
     }
     int kt0 = 0;
     const int lrow = lane / CPR;                                          // row within a load instruction
-    // Chunk this lane fetches for a load instruction whose first row is R0.
-    // R0 is a multiple of RPI; f(R0 + lrow) = (R0 / R256 + lrow / R256) mod CPR,
-    // and R0 / R256 mod CPR is 0 for 64-byte rows and 0 or 4 for 128-byte rows
-    // (alternating with the instruction index, which the code passes in).
-    auto chunk_off = [&](int r0_phase) -> uint32_t {
-      return static_cast<uint32_t>(((lane % CPR) ^ ((r0_phase + lrow / R256) % CPR)) * 16);
-    };
-    constexpr int PH = (RPI / R256) % CPR;  // phase step per load instruction (0 or 4)
-    const int fsw = ((lane & 15) / R256) % CPR;                           // read-side swizzle of row (lane & 15)
+    auto chunk_off = [&](int r0_phase) -> uint32_t { return DlGemm::chunk_off(lane, r0_phase); };
     // x spans T*K*2 bytes (< 2^32, checked on the host)
     const uint32_t a_bytes = mode_gather(kMode) ? static_cast<uint32_t>(g.T * K * 2) : 0u;
 
@@ -545,13 +605,9 @@ struct DlGemm {
         const uint32_t hb = static_cast<uint32_t>(static_cast<int64_t>(rows) * ap * 2);
         ars = make_rsrc(static_cast<const char*>(g.A) + (static_cast<int64_t>(row0) * ap + g.a_col0) * 2, hb);
 #pragma unroll
-        for (int i = 0; i < AI; ++i) {
-          const int r = (wv * AI + i) * RPI + lrow;
-          aoff[i] = r < rows ? static_cast<uint32_t>(r * ap * 2) + chunk_off(((wv * AI + i) * PH) % CPR) : hb;
-        }
+        for (int i = 0; i < AI; ++i) aoff[i] = plain_a_off(ap, rows, i, wv, lane);
       }
     }
-    pre(mb);  // the tile's operands are ready (fused kernels wait here)
 
     // B: weight rows of expert e (gated: first half W1, second half W3, same
     // columns); weight gradients: rows of the transposed operand, K window of expert e.
@@ -582,34 +638,55 @@ struct DlGemm {
                   chunk_off(((wv * BI + i) * PH) % CPR);
       }
     } else {
-      // Weights as stored, or (kPacked) in the stage order of pack_weights_kernel:
-      // the 64-row group g of an expert's matrix is K / 64 blocks of 8 KiB, block
-      // kt holding rows 64g.. x K elements 64kt.. already swizzled as the LDS
-      // stage expects, so the lane of stage row r and slot c reads 16 bytes at
-      // (g * K/64 + kt) * 8192 + (r % 64) * 128 + c * 16. The stage's column
-      // block starts on a multiple of 64 rows, so r % 64 is the row's place in
-      // its group and the swizzle matches.
+      // forward weights (fwd_b_off)
       const int64_t ebytes = N * K * 2;
       brs0 = make_rsrc(expert_base(g, g.B0, g.S0, e, ebytes), static_cast<uint32_t>(ebytes));
       brs1 = kGated ? make_rsrc(expert_base(g, g.B1, g.S1, e, ebytes), static_cast<uint32_t>(ebytes)) : brs0;
 #pragma unroll
-      for (int i = 0; i < BI; ++i) {
-        const int r = (wv * BI + i) * RPI + lrow;
-        int64_t n;
-        if constexpr (kGated)
-          n = static_cast<int64_t>(nb) * (BN / 2) + (r % (BN / 2));
-        else
-          n = static_cast<int64_t>(nb) * BN + r;
-        if constexpr (kPacked) {
-          int64_t grp = n / 64;
-          if (grp >= N / 64) grp = N / 64 - 1;  // column tail: a valid group, never stored
-          boff[i] = static_cast<uint32_t>(grp * (K / 64) * 8192 + (r % 64) * 128 + (lane % CPR) * 16);
-        } else {
-          if (n >= N) n = N - 1;  // column tail: computed on a valid row, never stored
-          boff[i] = static_cast<uint32_t>(n * K * 2) + chunk_off(((wv * BI + i) * PH) % CPR);
-        }
-      }
+      for (int i = 0; i < BI; ++i) boff[i] = fwd_b_off(g, nb, i, wv, lane);
     }
+
+    d.tile = tile;
+    d.pslot = pslot;
+    d.sp = sp;
+    d.part = part;
+    d.mb = mb;
+    d.nb = nb;
+    d.e = e;
+    d.row0 = row0;
+    d.rows = rows;
+    d.kt0 = kt0;
+    d.nk = nk;
+    d.ars = ars;
+    d.brs0 = brs0;
+    d.brs1 = brs1;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) d.aoff[i] = aoff[i];
+#pragma unroll
+    for (int i = 0; i < BI; ++i) d.boff[i] = boff[i];
+#endif
+  }
+
+  // The K loop and epilogue of tile t. s0: index of the tile's first K step in
+  // the workgroup's sequence of steps (step s uses A buffer s % 2 and B buffer
+  // s % NBB). warm: the previous tile's last steps already issued t's first
+  // loads. nx: the next tile, whose first nx_nk steps' loads this tile's last
+  // steps issue (nx_nk = 0: none; those steps then load nothing).
+  template <class Post>
+  __device__ static __forceinline__ void run_tile(const GemmArgs& g, char* lds, const Desc& t, const Desc& nx,
+                                                  int nx_nk, int s0, bool warm, Post post) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
+    const int wm = wv / WN, wn = wv % WN;
+    const int64_t N = g.N;
+    const int fsw = ((lane & 15) / R256) % CPR;  // read-side swizzle of row (lane & 15)
+    const int64_t pslot = t.pslot;
+    const int sp = t.sp, mb = t.mb, nb = t.nb, e = t.e, row0 = t.row0, rows = t.rows, kt0 = t.kt0, nk = t.nk;
+    const bool chained = kChain && nx_nk > 0;
+    const __amdgpu_buffer_rsrc_t ars = t.ars, brs0 = t.brs0, brs1 = t.brs1;
+    const uint32_t(&aoff)[AI] = t.aoff;
+    const uint32_t(&boff)[BI] = t.boff;
 
     f32x4_t acc[MI16][NJ16];
 #pragma unroll
@@ -628,6 +705,18 @@ struct DlGemm {
     auto issue_a = [&](int slot, int kt) {
       const bool real = kt < nk;
       char* sa = lds + slot * A_ST;
+      if constexpr (kChain) {
+        // past the tile's end: step kt - nk of the next tile, if any
+        const int kn = kt - nk;
+        const bool ahead = !real && chained && kn < nx_nk;
+        const __amdgpu_buffer_rsrc_t rs = real ? ars : (ahead ? nx.ars : nul);
+        const uint32_t koff = static_cast<uint32_t>(real ? kt0 + kt : (ahead ? nx.kt0 + kn : 0)) * RB;
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sa + (wv * AI + i) * 1024),
+                                                   16, real ? aoff[i] : nx.aoff[i], koff, 0, 0);
+        return;
+      }
       const uint32_t koff = real ? static_cast<uint32_t>(kt0 + kt) * RB : 0u;
 #pragma unroll
       for (int i = 0; i < AI; ++i)
@@ -648,6 +737,21 @@ struct DlGemm {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(real ? brs0 : nul,
                                                    (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024),
                                                    16, boff[i], koff, 0, AUX);
+        return;
+      }
+      if constexpr (kChain) {
+        const int kn = kt - nk;
+        const bool ahead = !real && chained && kn < nx_nk;
+        const __amdgpu_buffer_rsrc_t r0 = real ? brs0 : (ahead ? nx.brs0 : nul);
+        const __amdgpu_buffer_rsrc_t r1 = real ? brs1 : (ahead ? nx.brs1 : nul);
+        const uint32_t koff = static_cast<uint32_t>(real ? kt0 + kt : (ahead ? nx.kt0 + kn : 0)) * kstride;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+          const bool second = kGated && ((wv * BI + i) * RPI >= BN / 2);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? r1 : r0,
+                                                   (__attribute__((address_space(3))) void*)(sb + (wv * BI + i) * 1024),
+                                                   16, real ? boff[i] : nx.boff[i], koff, 0, AUX);
+        }
         return;
       }
       // (steps past the end read through the empty descriptor: the offset is moot)
@@ -730,30 +834,39 @@ struct DlGemm {
       // issues as the steps before step 0 would have: B0 .. B(NBB-3), A0,
       // B(NBB-2), A1, B(NBB-1) (two buffers: B0 A0 A1 B1). At step kt's
       // barrier only the newest B batch, B(kt+NBB-1), may then be in flight.
-      if constexpr (NBB == 2) {
-        issue_b(0, 0, aux_c);
-        issue_a(0, 0);
-        issue_a(1, 1);
-        issue_b(1, 1, aux_c);
-      } else {
-        issue_b(0, 0, aux_c);
+      // Buffers of the tile's step 0 (step j uses A buffer (a0 + j) % 2 and B
+      // buffer (b0 + j) % NBB). A warm tile's loads of steps 0 .. NBB-1 (A:
+      // 0, 1) went out in that order during the previous tile's last steps;
+      // only the epilogue's stores can be newer, and they only make the wait
+      // below longer.
+      const int a0 = s0 & 1, b0 = s0 % NBB;
+      auto bslot = [&](int j) { return b0 + j < NBB ? b0 + j : b0 + j - NBB; };
+      if (!warm) {
+        if constexpr (NBB == 2) {
+          issue_b(bslot(0), 0, aux_c);
+          issue_a(a0, 0);
+          issue_a(a0 ^ 1, 1);
+          issue_b(bslot(1), 1, aux_c);
+        } else {
+          issue_b(bslot(0), 0, aux_c);
 #pragma unroll
-        for (int j = 1; j <= NBB - 3; ++j) issue_b(j, j, aux_c);
-        issue_a(0, 0);
-        issue_b(NBB - 2, NBB - 2, aux_c);
-        issue_a(1, 1);
-        issue_b(NBB - 1, NBB - 1, aux_c);
+          for (int j = 1; j <= NBB - 3; ++j) issue_b(bslot(j), j, aux_c);
+          issue_a(a0, 0);
+          issue_b(bslot(NBB - 2), NBB - 2, aux_c);
+          issue_a(a0 ^ 1, 1);
+          issue_b(bslot(NBB - 1), NBB - 1, aux_c);
+        }
       }
       wait_vmcnt<(NBB == 2 ? AI + BI : AI + 2 * BI)>();  // A0 and B0 landed
       lds_barrier();
       if constexpr (MA16 > 0) {
-        read_b(0, 0, 0);
+        read_b(0, 0, b0);
 #pragma unroll
-        for (int i = 0; i < MA16; ++i) read_a(i, 0, 0);
+        for (int i = 0; i < MA16; ++i) read_a(i, 0, a0);
       }
-      int bsl = 0;  // B buffer of step kt
+      int bsl = b0;  // B buffer of step kt
       for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
+        const int cur = (a0 + kt) & 1;
         const int bnx = bsl + 1 == NBB ? 0 : bsl + 1;
         constexpr int M = MA16 * NJ16, R = MA16 + NJ16, G = M > R ? M : R;
         if constexpr (MA16 > 0) {
@@ -778,7 +891,9 @@ struct DlGemm {
         __builtin_amdgcn_sched_barrier(0);
         bsl = bnx;
       }
-      wait_vmcnt<0>();  // the empty loads of the last steps still write LDS the epilogue reuses
+      // the loads of the last steps (the next tile's, or empty ones) still write
+      // LDS: an epilogue through LDS waits for them, one from registers does not
+      if (!(kChain && sp == 1)) wait_vmcnt<0>();
     };
 
     const int ma = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows - wm * TM + 31) / 32)));
@@ -852,6 +967,30 @@ struct DlGemm {
             f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * cp + col0 + c4);
             const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
             *dst = (g.accumulate && sp == 1) ? *dst + v : v;
+          }
+        }
+      }
+    } else if constexpr (kChain) {
+      // FC1 / FC2 outputs straight from the accumulators (the stage buffers may
+      // already hold the next tile's first steps): lane l holds rows
+      // 4 (l / 16) .. +3 of column l % 16 of each 16 x 16 block; FC1 stores
+      // SiLU(g) * u of its gate and up blocks.
+      bf16_t* C = static_cast<bf16_t*>(g.C);
+      constexpr int CJ = kGated ? NJ16 / 2 : NJ16;  // output column blocks of the wave
+      const int64_t col0 = static_cast<int64_t>(nb) * (kGated ? BN / 2 : BN) + wn * (kGated ? TN / 2 : TN) + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < MI16; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = wm * TM + 16 * i + 4 * (lane >> 4) + v;
+          if (r < rows) {
+            bf16_t* crow = C + static_cast<int64_t>(row0 + r) * N;
+#pragma unroll
+            for (int j = 0; j < CJ; ++j) {
+              const int64_t col = col0 + 16 * j;
+              const float val = kGated ? silu_mul(acc[i][j][v], acc[i][j + NJ16 / 2][v]) : acc[i][j][v];
+              if (col < N) crow[col] = static_cast<bf16_t>(f32_to_bf16_bits(val));
+            }
           }
         }
       }
@@ -934,7 +1073,26 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   // consecutive tiles of each round, which share A and B blocks in that XCD's L2.
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int64_t tile = slot; tile < ntiles; tile += G) D::tile(g, lds, tile, [](int) {}, [](int) {});
+  if constexpr (D::kChain) {
+    // whole tiles chained: each one's last steps issue the next one's first loads
+    typename D::Desc cur, nxt;
+    int s0 = 0;
+    bool warm = false;
+    if (slot < ntiles) D::describe(g, slot, cur);
+    for (int64_t tile = slot; tile < ntiles; tile += G) {
+      const bool more = tile + G < ntiles;
+      if (more) D::describe(g, tile + G, nxt);
+      // a tile's last steps issue loads up to NBB steps ahead: all of them must
+      // fall in the next tile (so it needs at least NBB steps)
+      const bool chain = more && cur.sp == 1 && nxt.sp == 1 && nxt.nk >= D::NBB;
+      D::run_tile(g, lds, cur, nxt, chain ? nxt.nk : 0, s0, warm, [](int) {});
+      s0 = chain ? s0 + cur.nk : 0;
+      warm = chain;
+      cur = nxt;
+    }
+  } else {
+    for (int64_t tile = slot; tile < ntiles; tile += G) D::tile(g, lds, tile, [](int) {}, [](int) {});
+  }
 #endif
 }
 
