@@ -228,27 +228,45 @@ __global__ __launch_bounds__(256, 2) void gate_lds_kernel(const bf16_t* __restri
     __syncthreads();
   }
 
+  // The butterfly over the 64 class sums, in-lane: for each of the lane's RT
+  // token rows in turn, every lane writes its G class sums of its RE logits
+  // to LDS, and one thread per logit reads back all 64 and adds the same pairs
+  // in the same order (s_j += s_{j+off}, off = 32 .. 1), then the bias. Row L
+  // of the [logits][64] block holds 4-class chunk k at slot k ^ (L % 16), so
+  // 16 threads reading chunk k of 16 consecutive rows hit 16 distinct banks.
+  constexpr int NL = (256 / TPP) * RE;  // logits per token row of the lanes
+  static_assert(NL * 64 <= 2 * WS, "a token row's class sums fit in the weight buffers");
+  float* red = &lw[0][0];
+  auto slot_of = [](int L, int cls) { return L * 64 + ((cls & ~3) ^ (4 * (L % 16))) + (cls & 3); };
 #pragma unroll
-  for (int a = 0; a < RT; ++a)
-#pragma unroll
-    for (int e = 0; e < RE; ++e) {
-#pragma unroll
-      for (int off = 32; off >= G; off >>= 1)
-#pragma unroll
-        for (int r = 0; r < G; ++r) acc[a][e][r] = acc[a][e][r] + __shfl_down(acc[a][e][r], off / G, TPP);
-#pragma unroll
-      for (int off = G / 2; off >= 1; off >>= 1)
-#pragma unroll
-        for (int r = 0; r < off; ++r) acc[a][e][r] = acc[a][e][r] + acc[a][e][r + off];
-    }
-  if (q != 0) return;
-#pragma unroll
-  for (int a = 0; a < RT; ++a)
+  for (int a = 0; a < RT; ++a) {
 #pragma unroll
     for (int e = 0; e < RE; ++e) {
-      const int t = t0 + RT * tg + a, ex = e0 + RE * eg + e;
-      if (t < T && ex < E) logits[static_cast<int64_t>(t) * E + ex] = acc[a][e][0] + (bias ? bias[ex] : 0.0f);
+      const int L = grp * RE + e;
+      *reinterpret_cast<fvec_t*>(&red[slot_of(L, G * q)]) = *reinterpret_cast<const fvec_t*>(&acc[a][e][0]);
     }
+    __syncthreads();
+    if (tid < NL) {
+      const int L = tid;
+      float sv[64];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&red[slot_of(L, 4 * k)]);
+        sv[4 * k] = v[0];
+        sv[4 * k + 1] = v[1];
+        sv[4 * k + 2] = v[2];
+        sv[4 * k + 3] = v[3];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int j = 0; j < off; ++j) sv[j] = sv[j] + sv[j + off];
+      const int lg = L / RE, le = L % RE;
+      const int t = t0 + RT * (lg / NEG) + a, ex = e0 + RE * (lg % NEG) + le;
+      if (t < T && ex < E) logits[static_cast<int64_t>(t) * E + ex] = sv[0] + (bias ? bias[ex] : 0.0f);
+    }
+    __syncthreads();  // the block is read out before the next token row overwrites it
+  }
 }
 
 template <int G, int RT, int RE>
