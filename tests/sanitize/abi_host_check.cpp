@@ -128,6 +128,12 @@ int main() {
   EXPECT(moe_layer_forward_packed(&f32, A, A, nullptr, A, A, A, A, nullptr, nullptr, nullptr, nullptr, nullptr,
                                   nullptr, nullptr, A, BIG, nullptr),
          MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_layer_forward_fused_packed(&f32, A, A, nullptr, A, A, A, A, nullptr, nullptr, nullptr, nullptr,
+                                        nullptr, nullptr, nullptr, A, BIG, nullptr),
+         MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_layer_forward_fused_packed(&small, A, A, nullptr, A, A, A, A, nullptr, nullptr, nullptr, nullptr,
+                                        nullptr, nullptr, nullptr, A, 1024, nullptr),
+         MOE_ERR_WORKSPACE);
   EXPECT(moe_layer_forward_shared(&small, 0, A, A, nullptr, A, A, A, A, A, A, A, nullptr, nullptr, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, A, BIG, nullptr),
          MOE_ERR_INVALID);
