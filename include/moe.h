@@ -173,12 +173,12 @@ int moe_layer_forward(const moe_dims_t* dims, const void* x, const void* wg, con
  * until the process ends. The call allocates nothing: no hipMalloc or
  * allocating library routine. Shapes whose workspace
  * (moe_workspace_bytes) exceeds that size are refused with MOE_ERR_SCRATCH
- * before anything is enqueued; 64 MiB covers a Mixtral-8x22B-shaped decode
- * step of up to several hundred tokens. Every call on one GPU shares that
+ * before anything is enqueued; 128 MiB covers a Mixtral-8x22B-shaped layer
+ * of up to about 700 tokens. Every call on one GPU shares that
  * GPU's array, so calls that overlap on one GPU (on different streams, or
  * from different threads) race and give undefined results; serialise them.
  * The first call on a device looks up the array's address there. */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 int moe_layer_forward_noalloc(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
                               const void* w1, const void* w3, const void* w2, void* out, float* logits,
                               int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -216,9 +216,10 @@ int moe_layer_forward_shared(const moe_dims_t* dims, int n_shared, const void* x
  * dispatch run inside the launch when E <= 64 and T*k <= 65536 (else as
  * separate launches before it; the MOE_FUSED_FRONT=0 environment switch
  * forces that). The tiles are those of moe_layer_forward: the same rows per
- * block, FC2 tile width and, for decode-sized batches with fewer tiles than
- * compute units, the same split of K (the workgroup that stores a split
- * tile's last part sums the parts in the same order), so the outputs and
+ * block, FC2 tile width and the same split of K (of every tile when a
+ * launch has fewer tiles than compute units, of FC2's last partial round of
+ * tiles at prefill sizes; the workgroup that stores a split tile's last part
+ * sums the parts in the same order), so the outputs and
  * routing arrays are bitwise equal. bf16 only (MOE_ERR_UNSUPPORTED
  * otherwise); other arguments, limits and the workspace size
  * (moe_workspace_bytes) as moe_layer_forward. */

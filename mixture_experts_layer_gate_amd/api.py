@@ -32,7 +32,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed"]
 
 # Bytes of the static scratch moe_layer_forward_noalloc uses (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h).
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class MoeError(RuntimeError):

@@ -59,15 +59,18 @@ struct GemmArgs {
   // and first column; fp32 forms: add to C instead of storing
   int64_t a_pitch, a_col0;
   int accumulate;
-  // split K, for launches with fewer tiles than CUs: the tiles past the last
-  // full round of split_target workgroups (all of them here) have their K
-  // steps cut into parts, each part's fp32 accumulators go to `partial`
+  // split K: the tiles past the last full round of split_target workgroups
+  // (all of them in a launch with fewer tiles than CUs) have their K steps
+  // cut into parts, each part's fp32 accumulators go to `partial`
   // ([part slot][BM][BN]), and splitk_reduce_kernel sums them in part order.
   // At most `splits` parts, at most split_target part slots (one round of the
-  // persistent grid), at most partial_cap of them stored.
+  // persistent grid), at most partial_cap of them stored; after full rounds,
+  // at least tail_min parts (2 if unset), else no split.
   float* partial;
-  int splits, split_target, partial_cap;
+  int splits, split_target, partial_cap, tail_min;
 };
+
+constexpr int kMaxSplitParts = 8;  // most K parts of a split tile
 
 // How a launch of ntiles tiles is cut: tiles [0, full) whole (the full rounds of
 // split_target workgroups), the rest in sp parts each, part slots in order.
@@ -83,7 +86,7 @@ __device__ __forceinline__ SplitCut split_cut(const GemmArgs& g, int64_t ntiles)
   int64_t s = g.split_target / rest;
   if (s > g.splits) s = g.splits;
   if (s * rest > g.partial_cap) s = g.partial_cap / rest;
-  if (s < 2) return {ntiles, 1};
+  if (s < 2 || (ntiles > rest && s < g.tail_min)) return {ntiles, 1};
   return {ntiles - rest, static_cast<int>(s)};
 }
 
@@ -1100,14 +1103,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
 // element, the sum of its parts in part order, then what the GEMM's bf16
 // epilogue applies: SiLU(g) * u for FC1 (a wave's TN accumulator columns hold
 // TN/2 gate columns then the TN/2 up columns of the same outputs), bf16
-// rounding. Threads tid, tid + nthr, ... of the caller share the tile.
+// rounding. Threads tid, tid + nthr, ... of the caller share the tile, four
+// output columns each step (16-byte loads of every part, all issued before
+// the sums; N is a multiple of 64, so a group of four is wholly inside or
+// outside the matrix).
 template <bool kGated, int BM, int BN, int WN>
 __device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, SplitCut cut, int nbc, int nmb,
                                                   int tid, int nthr) {
   constexpr int OC = kGated ? BN / 2 : BN;  // output columns of a tile
   constexpr int TN = BN / WN;
+  constexpr int OV = OC / 4;                // groups of four output columns
+  static_assert(OC % 4 == 0 && (TN / 2) % 4 == 0, "four columns never straddle a gate/up boundary");
   const int64_t N = g.N;
-  const int sp = cut.sp;
+  const int sp = cut.sp;  // at most kMaxSplitParts
   bf16_t* C = static_cast<bf16_t*>(g.C);
   int mb, nb;
   decode_group_tile(g, t, nbc, nmb, mb, nb);
@@ -1118,20 +1126,36 @@ __device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, 
   // loop's index arithmetic out of a caller's tile loop, where it would hold
   // registers through the GEMM)
   asm volatile("" : "+v"(tid));
-  for (int q = tid; q < rows * OC; q += nthr) {
-    const int r = q / OC, oc = q % OC;
+  for (int q = tid; q < rows * OV; q += nthr) {
+    const int r = q / OV, oc = (q % OV) * 4;
     const int64_t col = static_cast<int64_t>(nb) * OC + oc;
     if (col >= N) continue;
     const int pc = kGated ? (oc / (TN / 2)) * TN + oc % (TN / 2) : oc;
     const float* src = part + r * BN + pc;
-    float a = src[0];
-    float b = kGated ? src[TN / 2] : 0.f;
-    for (int p = 1; p < sp; ++p) {
-      a += src[p * (BM * BN)];
-      if constexpr (kGated) b += src[p * (BM * BN) + TN / 2];
+    f32x4_t va[kMaxSplitParts], vb[kMaxSplitParts];
+#pragma unroll
+    for (int p = 0; p < kMaxSplitParts; ++p) {
+      if (p < sp) {
+        va[p] = *reinterpret_cast<const f32x4_t*>(src + p * (BM * BN));
+        if constexpr (kGated) vb[p] = *reinterpret_cast<const f32x4_t*>(src + p * (BM * BN) + TN / 2);
+      }
     }
-    const float v = kGated ? silu_mul(a, b) : a;
-    C[static_cast<int64_t>(row0 + r) * N + col] = static_cast<bf16_t>(f32_to_bf16_bits(v));
+    f32x4_t a = va[0], b = kGated ? vb[0] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 1; p < kMaxSplitParts; ++p) {
+      if (p < sp) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a[c] = a[c] + va[p][c];
+          if constexpr (kGated) b[c] = b[c] + vb[p][c];
+        }
+      }
+    }
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = kGated ? silu_mul(a[c], b[c]) : a[c];
+    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row0 + r) * N + col) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
 }
 
@@ -1480,8 +1504,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   const int64_t nt = static_cast<int64_t>(nmb) * nbc;
   const SplitCut cut = split_cut(g, nt);
   if (cut.sp <= 1) return;  // the GEMM wrote its outputs itself
-  for (int64_t t = cut.full + blockIdx.x; t < nt; t += gridDim.x)
-    reduce_split_tile<kGated, BM, BN, WN>(g, t, cut, nbc, nmb, threadIdx.x, blockDim.x);
+  // R workgroups per split tile, each taking every R-th group of columns, so
+  // that a few large split tiles (a launch's last round) still spread over
+  // the whole grid
+  const int64_t ns = nt - cut.full;
+  const int64_t R = ns < gridDim.x ? gridDim.x / ns : 1;
+  for (int64_t b = blockIdx.x; b < ns * R; b += gridDim.x)
+    reduce_split_tile<kGated, BM, BN, WN>(g, cut.full + b / R, cut, nbc, nmb,
+                                          threadIdx.x + static_cast<int>(b % R) * blockDim.x,
+                                          static_cast<int>(R) * blockDim.x);
 }
 
 // Stage order of one expert-weight tensor W [E][N][K] (bf16, N and K multiples
@@ -1571,7 +1602,7 @@ hipError_t launch_pack_weights(const void* w1, const void* w3, const void* w2, v
 // Largest number of K parts per tile: each part keeps at least 8 K steps of
 // 64; MOE_SPLIT_K=0 in the environment turns splitting off (=n caps it at n).
 static int split_k_parts(int64_t K) {
-  int s = static_cast<int>(std::min<int64_t>(8, K / (64 * 8)));
+  int s = static_cast<int>(std::min<int64_t>(kMaxSplitParts, K / (64 * 8)));
   if (const char* env = getenv("MOE_SPLIT_K")) {
     const int v = atoi(env);
     if (v >= 0 && v < s) s = v;
@@ -1579,12 +1610,22 @@ static int split_k_parts(int64_t K) {
   return s;
 }
 
+// Whether a forward launch whose largest plan has nt tiles may split K (K
+// dimension K): every tile when even that plan has fewer tiles than CUs, the
+// last partial round when it spans two or more rounds. (A launch between the
+// two, a batch of a few hundred tokens, does neither, and keeps the smaller
+// workspace.)
+static bool may_split(int64_t nt, int64_t K) {
+  const int64_t cus = device_cu_count();
+  return (nt < cus || nt >= 2 * cus) && split_k_parts(K) > 1;
+}
+
 size_t splitk_partial_bytes(int dtype, int regime, int64_t max_mb, int64_t d, int64_t f) {
   if (dtype != 1 || regime < 1) return 0;
   const int64_t cus = device_cu_count();
-  // FC1 tiles: 128 output columns; FC2: 192 or 256
-  const bool fc1 = max_mb * ((f + 127) / 128) < cus && split_k_parts(d) > 1;
-  const bool fc2 = max_mb * ((d + 255) / 256) < cus && split_k_parts(f) > 1;
+  // FC1 tiles have 128 output columns, FC2 tiles up to 256
+  const bool fc1 = may_split(max_mb * ((f + 127) / 128), d);
+  const bool fc2 = may_split(max_mb * ((d + 255) / 256), f);
   const int64_t bm = regime_block_rows(regime);
   return fc1 || fc2 ? static_cast<size_t>(cus) * bm * 256 * sizeof(float) : 0;
 }
@@ -1622,26 +1663,33 @@ static hipError_t launch_big(const GemmArgs& a, int64_t max_mb, int64_t ncols, h
   return hipGetLastError();
 }
 
-// Forward FC1/FC2 launch, split along K when even the largest plan has fewer
-// tiles than CUs (few rows and few experts: a decode step of a handful of
-// tokens) and the partial buffer is there; the tiles' parts then run on all
-// CUs and a second kernel sums them. (Splitting only the last partial round
-// of a large launch was measured too: the halves and thirds of tiles it adds
-// cost as much as the idle CUs they fill.)
+// Forward FC1/FC2 launch, split along K where the partial buffer is there
+// (splitk_partial_bytes) and the plan calls for it: a launch with fewer tiles
+// than CUs (few rows and few experts: a decode step of a handful of tokens)
+// splits every tile, so that its parts run on all CUs; a launch of several
+// rounds splits the tiles of its last, partial round, whose CUs would
+// otherwise wait for most of a tile (Mixtral-8x22B prefill FC2: 1608 tiles, a
+// last round of 72 for 256 CUs). A second kernel sums the parts. FC2 splits
+// any partial last round (halving the tiles of the balanced prefill's
+// half-full one: FC2 2.75 -> 2.55 ms); FC1 only one cut into three or more
+// parts, a round at most a third full (its tiles have fewer K steps, and
+// halving the prefill's half-full last round cost 0.5 %, while the DBRX- and
+// DeepSeek-shaped FC1 gained 2-3 % from rounds cut into 8).
 // Whether a forward launch over up to max_mb m-blocks x nb column blocks
 // (tiles of tile_floats fp32 accumulators) splits K, given a partial buffer of
-// partial_bytes (0: none), and if so its split fields in a. The fused launch
-// takes the same decision, so its tiles split the same way.
+// partial_bytes (0: none), and if so its split fields in a; the plan on the
+// device decides which tiles. The fused launch takes the same decision, so its
+// tiles split the same way.
 static bool fwd_split(GemmArgs& a, int64_t max_mb, int64_t nb, int64_t tile_floats, float* partial,
-                      size_t partial_bytes) {
-  const int64_t cus = device_cu_count();
+                      size_t partial_bytes, int tail_min) {
   const int parts = split_k_parts(a.K);
   const int64_t cap = static_cast<int64_t>(partial_bytes / (sizeof(float) * tile_floats));
-  if (partial_bytes == 0 || parts < 2 || max_mb * nb >= cus || max_mb * nb * 2 > cap) return false;
+  if (partial_bytes == 0 || cap < 2 || !may_split(max_mb * nb, a.K)) return false;
   a.partial = partial;
   a.splits = parts;
-  a.split_target = static_cast<int>(cus);
+  a.split_target = static_cast<int>(device_cu_count());
   a.partial_cap = static_cast<int>(cap);
+  a.tail_min = tail_min;
   return true;
 }
 
@@ -1651,14 +1699,13 @@ static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* p
   const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
   const int64_t nb = (ncols + cols - 1) / cols;
   const int64_t cus = device_cu_count();
-  if (!fwd_split(a, max_mb, nb, static_cast<int64_t>(BM) * BN, partial, partial_bytes))
+  if (!fwd_split(a, max_mb, nb, static_cast<int64_t>(BM) * BN, partial, partial_bytes, kMode == kModeFc2 ? 2 : 3))
     return launch_big<kMode, BM, BN, WM, WN, kPacked>(a, max_mb, ncols, s);
   hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN, kPacked>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
                      a);
   if (hipError_t err = hipGetLastError()) return err;
-  hipLaunchKernelGGL((splitk_reduce_kernel<mode_gated(kMode), BM, BN, WN>),
-                     dim3(static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_mb * nb, cus)))), dim3(256), 0, s,
-                     a);
+  hipLaunchKernelGGL((splitk_reduce_kernel<mode_gated(kMode), BM, BN, WN>), dim3(static_cast<int>(2 * cus)), dim3(256),
+                     0, s, a);
   return hipGetLastError();
 }
 
@@ -1801,8 +1848,8 @@ static FusedShape fused_shape(FusedFfnArgs& a, int regime, int64_t max_mb, int64
   sh.rows128 = regime == 3;
   sh.narrow = fc2_narrow(regime, est_mb, d);
   const int64_t bm = sh.rows128 ? 128 : 256, bn2 = sh.narrow ? 192 : 256;
-  const bool sp1 = fwd_split(a.fc1, max_mb, (f + 127) / 128, bm * 256, partial, partial_bytes);
-  const bool sp2 = fwd_split(a.fc2, max_mb, (d + bn2 - 1) / bn2, bm * bn2, partial, partial_bytes);
+  const bool sp1 = fwd_split(a.fc1, max_mb, (f + 127) / 128, bm * 256, partial, partial_bytes, 3);
+  const bool sp2 = fwd_split(a.fc2, max_mb, (d + bn2 - 1) / bn2, bm * bn2, partial, partial_bytes, 2);
   const int64_t cus = device_cu_count();
   const int64_t g = (sp1 || sp2 ? cus : std::min<int64_t>(max_mb * ((f + 127) / 128), cus)) / 8 * 8;
   sh.grid = static_cast<int>(g < 8 ? 8 : g);

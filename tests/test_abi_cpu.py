@@ -273,6 +273,10 @@ def test_noalloc_refuses_shapes_beyond_its_scratch():
     assert call(k=0) == 1
     assert call(T=0) == 0
     assert b"static" in lib.moe_status_string(5)
-    # a decode step of the Mixtral-8x22B shape fits
-    assert lib.moe_workspace_bytes(ctypes.byref(_dims(T=256, d=6144, f=16384, E=8, k=2))) <= \
-        api.NOALLOC_SCRATCH_BYTES
+    # a decode step of the Mixtral-8x22B shape fits, and so does a 700-token batch
+    for T in (256, 700):
+        assert lib.moe_workspace_bytes(ctypes.byref(_dims(T=T, d=6144, f=16384, E=8, k=2))) <= \
+            api.NOALLOC_SCRATCH_BYTES
+    # the binding's copy of the size is the header's
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", open(HEADER).read())
+    assert m and int(m.group(1)) << 20 == api.NOALLOC_SCRATCH_BYTES

@@ -4,9 +4,10 @@ counters; MOE_FUSED_FRONT=0 keeps route and dispatch as separate launches before
 it, and both forms are tested.
 
 Its tiles do exactly the arithmetic of moe_layer_forward's separate launches:
-the same rows per block, FC2 tile width, weight layout and, for launches with
-fewer tiles than compute units, the same split of K, whose parts the workgroup
-storing the last one sums in the separate reduce's order. So the bar is
+the same rows per block, FC2 tile width, weight layout and split of K (every
+tile of a launch with fewer tiles than compute units; the last partial round
+of FC2 tiles at prefill sizes), whose parts the workgroup storing the last one
+sums in the separate reduce's order. So the bar is
 bitwise equality with that path (itself held to the oracle in
 test_gpu_parity.py), checked twice in a row on the same buffers (a missed
 wait or a stale read would show up as a difference), plus the oracle bar on
@@ -99,11 +100,13 @@ def test_fused_small_bitwise_and_oracle(shape):
 
 
 SPLIT_SHAPES = [
-    # T, d, f, E, k, bias scale: fewer tiles than CUs, K of 1024 or more
+    # T, d, f, E, k, bias scale: fewer tiles than CUs, K of 1024 or more, or a
+    # multi-round FC2 whose last partial round is split
     (1, 1024, 1024, 8, 2, 0.0),      # 128-row tiles, FC1 and FC2 split
     (300, 1024, 1024, 4, 2, 1.0),    # 256-row tiles, FC1 and FC2 split
     (16, 2048, 4096, 8, 2, 0.0),     # FC1 whole, FC2 in 4 parts of 16 K steps
     (5, 1536, 1024, 16, 4, 2.0),     # FC1 in 3 parts, FC2 in 2
+    (8300, 2048, 1024, 2, 2, 0.0),   # last rounds of 16 tiles (of 528) cut: FC1 in 4 parts, FC2 in 2
 ]
 
 

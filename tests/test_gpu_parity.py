@@ -242,13 +242,18 @@ SPLIT_SHAPES = [
     (600, 2048, 1024, 2, 1, 1.0),   # few experts with many rows: parts of up to 256 rows
     (100, 1024, 1536, 1, 1, 0.0),   # one expert: FC2 in 3 parts
     (1200, 1024, 4096, 4, 2, 0.0),  # 256-row tiles: FC1 unsplit (384 tiles), FC2 (72 tiles of 192) in 3 parts
+    # k = E: 33 blocks of 256 rows per expert; FC1 and FC2 have 528 tiles each, two
+    # full rounds of 256 CUs and a last round of 16 tiles, which alone are cut
+    # (FC1 in 4 parts, FC2 in 2)
+    (8300, 2048, 1024, 2, 2, 0.0),
 ]
 
 
 @pytest.mark.parametrize("regime", ["default", "1"])
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "T{}_d{}_f{}_E{}_k{}_s{}".format(*s))
 def test_split_k_launches(monkeypatch, shape, regime):
-    """Few-tile launches split along K: oracle bar, bitwise repeatable, and within the
+    """Launches split along K (every tile of a few-tile launch, or the last partial
+    round of a multi-round FC2): oracle bar, bitwise repeatable, and within the
     oracle bar of the same layer run unsplit (MOE_SPLIT_K=0); with the tiles the batch
     size picks and with 256-row tiles forced."""
     T, d, f, E, k, s = shape

@@ -84,6 +84,18 @@ def test_noalloc_mixtral_decode_then_single_token():
     _check(dims, inp, 1)
 
 
+@pytest.mark.timeout(600)
+def test_noalloc_mixtral_shape_700_then_300_tokens():
+    """The Mixtral-8x22B layer shape at 700 tokens (256-row blocks; near the largest
+    batch the scratch holds), then 300 tokens."""
+    _say("case noalloc mixtral shape T=700 then T=300")
+    inp = moe_inputs.random_inputs(700, 6144, 16384, 8, 2, "bf16", 1.0, seed=43, device="cuda")
+    dims = moe.Dims(700, 6144, 16384, 8, 2, torch.bfloat16)
+    assert moe.workspace_bytes(dims) <= moe.NOALLOC_SCRATCH_BYTES
+    _check(dims, inp, 700)
+    _check(dims, inp, 300)
+
+
 def test_noalloc_refuses_a_shape_beyond_its_scratch():
     cfg = moe_inputs.config("mixtral_prefill_skew")
     _say("case noalloc refuses prefill")
