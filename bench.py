@@ -189,12 +189,15 @@ def copy_probe():
 
 def stage_rooflines(cfg, kk: int, counts, elt: int, stage_ms: dict) -> dict:
     """Each forward stage against the bound of its own work: the gate's fp32
-    multiply-adds against the unpacked fp32 vector peak, FC1 and FC2 against
+    multiply-adds against the fp32 matrix-core peak where the library runs them
+    there, else the unpacked fp32 vector peak, FC1 and FC2 against
     bf16 MFMA or HBM (whichever their algorithmic work binds), the routing and
     data-movement stages against HBM by the bytes they must move (top-k and
     dispatch move a few MB at most and are bound by launch latency, so their
     fractions are small by nature). Where the gate and top-k run as one launch
     (small batches) the gate entry times both."""
+    import torch
+    import mixture_experts_layer_gate_amd as moe
     from mixture_experts_layer_gate_amd import roofline as rf
     T, d, f, E = cfg.T, cfg.d, cfg.f, cfg.E
     n = T * kk
@@ -210,7 +213,10 @@ def stage_rooflines(cfg, kk: int, counts, elt: int, stage_ms: dict) -> dict:
 
     hbm = rf.PEAK_HBM_BYTES_PER_S / 1e9
     mfma = (rf.PEAK_MFMA_BF16_FLOPS if cfg.dtype == "bf16" else rf.PEAK_MFMA_FP32_FLOPS) / 1e12
-    put("gate", "valu", 2 * T * d * E, round(rf.PEAK_VALU_FP32_UNPACKED_FLOPS / 1e12, 1), "TFLOP/s", 1e12)
+    if moe.gate_on_matrix_cores(moe.Dims(T, d, f, E, kk, torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)) == 1:
+        put("gate", "mfma", 2 * T * d * E, round(rf.PEAK_MFMA_FP32_FLOPS / 1e12, 1), "TFLOP/s", 1e12)
+    else:
+        put("gate", "valu", 2 * T * d * E, round(rf.PEAK_VALU_FP32_UNPACKED_FLOPS / 1e12, 1), "TFLOP/s", 1e12)
     put("topk", "hbm", T * E * 4 + n * 8, hbm, "GB/s", 1e9)
     put("dispatch", "hbm", n * 4 * 2 + n * 8, hbm, "GB/s", 1e9)
     for stage, flops, nbytes in (("fc1", rf.fc1_flops(n, d, f), rf.fc1_bytes(T, d, f, kk, counts, elt)),

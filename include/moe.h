@@ -95,6 +95,15 @@ size_t moe_workspace_bytes(const moe_dims_t* dims);
  * invalid. Host-only query: no device work. */
 int moe_ffn_block_rows(const moe_dims_t* dims);
 
+/* Whether the gate GEMM (MegaScale-Infer, Fused Kernels, step 1) of `dims`
+ * runs on the fp32 matrix cores (1) or the vector ALUs (0); -1 if dims is
+ * invalid. Both give the same logits, bit for bit. The matrix cores take bf16
+ * batches with d a multiple of 64, E >= 32 and at least 256 tiles of 32 tokens
+ * x 32 experts; the MOE_GATE_CFG environment switch overrides ("mfma" forces
+ * them where they can run, a VALU tile name forces the VALU). Host-only query:
+ * no device work. */
+int moe_gate_on_matrix_cores(const moe_dims_t* dims);
+
 /* Gate GEMM + bias, top-k selection and renormalised weights
  * (MegaScale-Infer, Fused Kernels, steps 1 and 3).
  *   x      [T][d]   tokens

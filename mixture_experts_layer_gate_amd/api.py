@@ -27,7 +27,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_timing_enable",
            "moe_timing_disable", "moe_timing_read", "moe_probe_cus", "moe_probe_hbm_read", "moe_probe_mfma",
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
-           "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_pack_weights",
+           "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_gate_on_matrix_cores", "moe_pack_weights",
            "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed",
            "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed"]
 
@@ -85,6 +85,8 @@ def load_library():
     lib.moe_workspace_bytes.argtypes = [_DP]
     lib.moe_ffn_block_rows.restype = ctypes.c_int
     lib.moe_ffn_block_rows.argtypes = [_DP]
+    lib.moe_gate_on_matrix_cores.restype = ctypes.c_int
+    lib.moe_gate_on_matrix_cores.argtypes = [_DP]
     lib.moe_route.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_permute.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _S, _P]
     lib.moe_grouped_ffn.argtypes = [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]
@@ -153,6 +155,12 @@ def workspace_bytes(dims: Dims) -> int:
 def ffn_block_rows(dims: Dims) -> int:
     """Rows per m-block of the grouped FFN for these dims (128 or 256; 0 if invalid)."""
     return int(load_library().moe_ffn_block_rows(ctypes.byref(dims.c())))
+
+
+def gate_on_matrix_cores(dims: Dims) -> int:
+    """1 if the gate GEMM of these dims runs on the fp32 matrix cores, 0 on the vector
+    ALUs, -1 if the dims are invalid."""
+    return int(load_library().moe_gate_on_matrix_cores(ctypes.byref(dims.c())))
 
 
 def make_workspace(dims: Dims, device="cuda") -> torch.Tensor:

@@ -12,6 +12,9 @@ constexpr int kBlockRows = 128;
 constexpr int kTileGroup = 8;
 
 // Gate logits l[t][e] in the fixed fp32 order. Requires d % 8 == 0.
+// Whether launch_gate_logits runs the gate of a T x d x E batch on the fp32
+// matrix cores (gate_mfma_kernel) rather than the vector ALUs.
+bool gate_uses_mfma(int dtype, int64_t T, int64_t d, int E);
 hipError_t launch_gate_logits(int dtype, const void* x, const void* wg, const float* bias,
                               float* logits, int64_t T, int64_t d, int E, hipStream_t s);
 // Top-k selection + renormalised softmax weights from logits.

@@ -517,6 +517,11 @@ int moe_ffn_block_rows(const moe_dims_t* dm) {
   return regime_block_rows(gemm_regime(dm));
 }
 
+int moe_gate_on_matrix_cores(const moe_dims_t* dm) {
+  if (check_dims(dm) != MOE_OK) return -1;
+  return gate_uses_mfma(dm->dtype, dm->T, dm->d, dm->E) ? 1 : 0;
+}
+
 size_t moe_workspace_bytes(const moe_dims_t* dm) {
   if (check_dims(dm) != MOE_OK) return 0;
   size_t m = layer_ws(dm, nullptr, nullptr);

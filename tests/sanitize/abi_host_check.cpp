@@ -60,10 +60,14 @@ int main() {
     EXPECT(moe_workspace_bytes_shared(&b, 1), 0);
     EXPECT(moe_backward_workspace_bytes(&b), 0);
     EXPECT(moe_ffn_block_rows(&b), 0);
+    EXPECT(moe_gate_on_matrix_cores(&b), -1);
   }
   EXPECT(moe_workspace_bytes(nullptr), 0);
   EXPECT(moe_ffn_block_rows(&decode), 128);
   EXPECT(moe_ffn_block_rows(&prefill), 256);
+  EXPECT(moe_gate_on_matrix_cores(&prefill), 0);
+  const moe_dims_t deepseek = dims(4096, 7168, 2048, 256, 8);
+  EXPECT(moe_gate_on_matrix_cores(&deepseek), 1);
   const moe_dims_t widest = dims(2000000, 64, 64, 1024, 1024);   // T*k just under 2^31
   EXPECT(moe_workspace_bytes(&widest) > 0, 1);
   const moe_dims_t big_e = dims(4096, 7168, 2048, 1024, 8);

@@ -73,6 +73,26 @@ def test_ffn_block_rows_choice(monkeypatch):
     assert rows(T=8192) == 128
 
 
+def test_gate_unit_query(monkeypatch):
+    """The fp32 matrix cores take bf16 gates with E >= 32 and >= 256 tiles of 32 x 32;
+    the environment switch overrides; invalid dims give -1."""
+    monkeypatch.delenv("MOE_GATE_CFG", raising=False)
+    lib = moe.load_library()
+
+    def mc(**kw):
+        return lib.moe_gate_on_matrix_cores(ctypes.byref(_dims(**kw)))
+    assert mc(T=4096, d=7168, f=2048, E=256, k=8) == 1       # DeepSeek-V3 shape: 128 x 8 tiles
+    assert mc(T=8192, d=6144, f=16384, E=8, k=2) == 0        # 8 experts: the VALU tiles
+    assert mc(T=992, d=7168, f=2048, E=256, k=8) == 0        # 31 x 8 tiles
+    assert mc(T=1024, d=7168, f=2048, E=256, k=8) == 1       # 32 x 8
+    assert mc(T=4096, d=7168, f=2048, E=256, k=8, dtype=0) == 0  # fp32 data
+    assert mc(k=0) == -1
+    monkeypatch.setenv("MOE_GATE_CFG", "lds")
+    assert mc(T=4096, d=7168, f=2048, E=256, k=8) == 0
+    monkeypatch.setenv("MOE_GATE_CFG", "mfma")
+    assert mc(T=77, d=512, f=64, E=8, k=2) == 1
+
+
 def test_workspace_bytes_grows_with_shape():
     lib = moe.load_library()
     a = lib.moe_workspace_bytes(ctypes.byref(_dims()))

@@ -302,8 +302,9 @@ def test_grouped_ffn_partial_blocks(monkeypatch, regime):
     assert err <= OUT_TOL
 
 
-@pytest.mark.parametrize("gate_cfg", ["8,2,4", "4,4,4", "2,4,8", "lds", "lds2", ""])
-@pytest.mark.parametrize("shape", [(300, 200, 24), (77, 512, 8), (1000, 1024, 64), (500, 832, 48)],
+@pytest.mark.parametrize("gate_cfg", ["8,2,4", "4,4,4", "2,4,8", "lds", "lds2", "mfma", ""])
+@pytest.mark.parametrize("shape", [(300, 200, 24), (77, 512, 8), (1000, 1024, 64), (500, 832, 48), (45, 576, 40),
+                                   (130, 7168, 256)],
                          ids=lambda s: "T{}_d{}_E{}".format(*s))
 def test_gate_tile_configs_bit_exact(monkeypatch, gate_cfg, shape):
     """Every gate register-tile configuration (forced via MOE_GATE_CFG) gives the oracle's logits bit for bit."""
