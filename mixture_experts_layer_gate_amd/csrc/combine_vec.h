@@ -15,22 +15,34 @@ __device__ __forceinline__ void combine_vec(const void* __restrict__ y, const in
   float acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    int64_t p = inv_perm[t * k + j];
-    p = p < 0 ? 0 : (p >= n_assign ? n_assign - 1 : p);
-    const float wj = w[t * k + j];
-    float v[8];
-    if constexpr (kDtype == 1) {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(y) + p * d + c * 8);
-      v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-      v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
-    } else {
-      const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(y) + p * d + c * 8);
-      const float4 a = q[0], b = q[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  // slots in groups of up to 4: the group's row loads are all issued before
+  // its multiply-adds, which then run in slot order
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    float wj[4], v[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (j0 + q < k) {
+        int64_t p = inv_perm[t * k + j0 + q];
+        p = p < 0 ? 0 : (p >= n_assign ? n_assign - 1 : p);
+        wj[q] = w[t * k + j0 + q];
+        if constexpr (kDtype == 1) {
+          const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(y) + p * d + c * 8);
+          v[q][0] = bf16_lo(u.x); v[q][1] = bf16_hi(u.x); v[q][2] = bf16_lo(u.y); v[q][3] = bf16_hi(u.y);
+          v[q][4] = bf16_lo(u.z); v[q][5] = bf16_hi(u.z); v[q][6] = bf16_lo(u.w); v[q][7] = bf16_hi(u.w);
+        } else {
+          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(y) + p * d + c * 8);
+          const float4 a = src[0], b = src[1];
+          v[q][0] = a.x; v[q][1] = a.y; v[q][2] = a.z; v[q][3] = a.w;
+          v[q][4] = b.x; v[q][5] = b.y; v[q][6] = b.z; v[q][7] = b.w;
+        }
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = __builtin_fmaf(wj, v[r], acc[r]);
+    for (int q = 0; q < 4; ++q)
+      if (j0 + q < k) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] = __builtin_fmaf(wj[q], v[q][r], acc[r]);
+      }
   }
   // shared experts: rows n_assign + s*T + t, weight 1, after the routed slots
   for (int sh = 0; sh < n_shared; ++sh) {
