@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(
     int block_rows, int64_t max_mb, int4* __restrict__ mblocks, int32_t* __restrict__ n_mblocks) {
   __shared__ int32_t wh[kFusedWaves][kMaxExperts];  // per-wave counts, then per-wave running positions
   __shared__ int32_t wsum[kFusedWaves];
-  dispatch_block<kFusedThreads>(idx, n, E, counts, offsets, perm, inv_perm, block_rows, max_mb, mblocks, n_mblocks,
+  dispatch_block<kFusedThreads, true>(idx, n, E, counts, offsets, perm, inv_perm, block_rows, max_mb, mblocks, n_mblocks,
                                 wh, wsum);
 }
 
@@ -235,7 +235,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * block_rows, r, tile_group(start, i, nb));
     }
   }
-  if (e == 1023) n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(before + incl), max_mb));
+  if (e == 1023) {
+    n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(before + incl), max_mb));
+    for (int i = 0; i < 2 * kTileQueueWords; ++i) n_mblocks[kTileQueueFc1 + i * kTileQueueStride] = 0;
+  }
 }
 
 hipError_t launch_plan(const int32_t* counts, const int32_t* offsets, int E, int64_t n_assign,

@@ -68,6 +68,9 @@ struct GemmArgs {
   // at least tail_min parts (2 if unset), else no split.
   float* partial;
   int splits, split_target, partial_cap, tail_min;
+  // Forward 256-row launches: 8 tile-queue counters kTileQueueStride words
+  // apart, zero at launch (null: every workgroup takes a fixed share of the tiles).
+  int32_t* tileq;
 };
 
 constexpr int kMaxSplitParts = 8;  // most K parts of a split tile
@@ -1063,6 +1066,15 @@ struct DlGemm {
   }
 };
 
+// A value every lane holds the same, moved to scalar registers (the compiler
+// cannot tell that a word read from LDS is uniform).
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
   // device-only body: the buffer-resource builtins have no host form, and the
@@ -1092,6 +1104,41 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       s0 = chain ? s0 + cur.nk : 0;
       warm = chain;
       cur = nxt;
+    }
+  } else if (g.tileq != nullptr && G % 8 == 0) {
+    // Tile queues. Tiles of unequal length (partial m-blocks, the K parts of
+    // a last round) leave CUs and whole XCDs idle at the end of a launch whose
+    // workgroups each take a fixed share. Queue q lists, round by round, the
+    // tiles the fixed order gives XCD q (G/8 consecutive ones, which share
+    // operand panels in that L2); a workgroup takes the next tile of its own
+    // XCD's queue and, once that is drained, of the other queues. A queue's
+    // tile index grows with its counter, so a queue seen drained stays
+    // drained, and every tile is taken once.
+    const int per = G / 8;
+    int q = blockIdx.x % 8, left = 8;  // used by thread 0 only
+    int64_t* bcast = reinterpret_cast<int64_t*>(lds);  // free between tiles
+    for (;;) {
+      if (threadIdx.x == 0) {
+        int64_t t = -1;
+        while (left > 0) {
+          const int i = atomicAdd(g.tileq + q * kTileQueueStride, 1);
+          const int64_t cand = static_cast<int64_t>(i / per) * G + q * per + i % per;
+          if (i >= 0 && cand < ntiles) {  // (a counter that is not a claim count reads as drained)
+            t = cand;
+            break;
+          }
+          q = (q + 1) % 8;
+          --left;
+        }
+        *bcast = t;
+      }
+      __syncthreads();
+      // the same in every lane: held in scalar registers, as the fixed order's
+      // index is (buffer descriptors derived from it must be scalar)
+      const int64_t tile = uniform(*reinterpret_cast<volatile int64_t*>(bcast));
+      __syncthreads();  // read by every thread before the tile's loads refill the buffer
+      if (tile < 0) break;
+      D::tile(g, lds, tile, [](int) {}, [](int) {});
     }
   } else {
     for (int64_t tile = slot; tile < ntiles; tile += G) D::tile(g, lds, tile, [](int) {}, [](int) {});
@@ -1392,14 +1439,6 @@ __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
   return wait_count(a.sync + kSyncPlanReady, 1, err, a.spin_limit, s_flag, 2);
 }
 
-// A value every lane holds the same, moved to scalar registers (the compiler
-// cannot tell that a word read from LDS is uniform).
-__device__ __forceinline__ int64_t uniform(int64_t v) {
-  const uint64_t u = static_cast<uint64_t>(v);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 // After storing a split tile's part: whether this workgroup stored the tile's
 // last part (then, after an acquire, it sees every part).
@@ -1693,12 +1732,24 @@ static bool fwd_split(GemmArgs& a, int64_t max_mb, int64_t nb, int64_t tile_floa
   return true;
 }
 
+// Tile queues for the 256-row forward launches; MOE_TILE_QUEUES=0 in the
+// environment gives every workgroup a fixed share of the tiles instead (the
+// same outputs, bit for bit).
+static bool tile_queues_on() {
+  const char* env = getenv("MOE_TILE_QUEUES");
+  return !(env && env[0] == '0');
+}
+
 template <int kMode, int BM, int BN, int WM, int WN, bool kPacked = false>
 static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* partial, size_t partial_bytes,
-                             hipStream_t s) {
+                             bool queues, hipStream_t s) {
   const int64_t cols = mode_gated(kMode) ? BN / 2 : BN;
   const int64_t nb = (ncols + cols - 1) / cols;
   const int64_t cus = device_cu_count();
+  // 256-row tiles (not chained) take their tiles from the plan's queues
+  static_assert(kMode == kModeFc1 || kMode == kModeFc2, "forward forms");
+  if (BM == 256 && queues && tile_queues_on())
+    a.tileq = const_cast<int32_t*>(a.n_mblocks) + (kMode == kModeFc1 ? kTileQueueFc1 : kTileQueueFc2);
   if (!fwd_split(a, max_mb, nb, static_cast<int64_t>(BM) * BN, partial, partial_bytes, kMode == kModeFc2 ? 2 : 3))
     return launch_big<kMode, BM, BN, WM, WN, kPacked>(a, max_mb, ncols, s);
   hipLaunchKernelGGL((gemm_dl_kernel<kMode, BM, BN, WM, WN, kPacked>), dim3(static_cast<int>(cus)), dim3(64 * WM * WN), 0, s,
@@ -1712,18 +1763,19 @@ static hipError_t launch_fwd(GemmArgs a, int64_t max_mb, int64_t ncols, float* p
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s) {
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, bool queues,
+                      hipStream_t s) {
   GemmArgs a{x, perm, k, T, w1, w3, h, mblocks, n_mblocks, d, f,
              T * k, sh.w1, sh.w3, sh.n > 0 ? sh.E_routed : INT32_MAX};
   // packed: w1, w3 in stage order (pack_weights_kernel), read by the large-tile
   // kernels only
   if (dtype == 1 && packed)
-    return regime == 3 ? launch_fwd<kModeFc1, 128, 256, 2, 4, true>(a, max_mb, f, partial, partial_bytes, s)
-                       : launch_fwd<kModeFc1, 256, 256, 2, 4, true>(a, max_mb, f, partial, partial_bytes, s);
+    return regime == 3 ? launch_fwd<kModeFc1, 128, 256, 2, 4, true>(a, max_mb, f, partial, partial_bytes, queues, s)
+                       : launch_fwd<kModeFc1, 256, 256, 2, 4, true>(a, max_mb, f, partial, partial_bytes, queues, s);
   if (dtype == 1 && regime == 3)
-    return launch_fwd<kModeFc1, 128, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, s);
+    return launch_fwd<kModeFc1, 128, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, queues, s);
   if (dtype == 1 && regime >= 1)
-    return launch_fwd<kModeFc1, 256, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, s);
+    return launch_fwd<kModeFc1, 256, 256, 2, 4>(a, max_mb, f, partial, partial_bytes, queues, s);
   const int grid = persistent_grid(max_mb * (f / (kBNW / 2)));
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -1746,23 +1798,24 @@ static bool fc2_narrow(int regime, int64_t est_mb, int64_t d) {
 
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s) {
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, bool queues,
+                      hipStream_t s) {
   GemmArgs a{h, nullptr, 1, 0, w2, nullptr, y, mblocks, n_mblocks, f, d,
              0, sh.w2, nullptr, sh.n > 0 ? sh.E_routed : INT32_MAX};
   if (dtype == 1 && regime >= 1) {
     const bool narrow = fc2_narrow(regime, est_mb, d);
     if (packed) {  // W2 in stage order (pack_weights_kernel)
       if (regime == 3)
-        return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s)
-                      : launch_fwd<kModeFc2, 128, 256, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s);
-      return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2, true>(a, max_mb, d, partial, partial_bytes, s)
-                    : launch_fwd<kModeFc2, 256, 256, 2, 4, true>(a, max_mb, d, partial, partial_bytes, s);
+        return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4, true>(a, max_mb, d, partial, partial_bytes, queues, s)
+                      : launch_fwd<kModeFc2, 128, 256, 2, 4, true>(a, max_mb, d, partial, partial_bytes, queues, s);
+      return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2, true>(a, max_mb, d, partial, partial_bytes, queues, s)
+                    : launch_fwd<kModeFc2, 256, 256, 2, 4, true>(a, max_mb, d, partial, partial_bytes, queues, s);
     }
     if (regime == 3)
-      return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4>(a, max_mb, d, partial, partial_bytes, s)
-                    : launch_fwd<kModeFc2, 128, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, s);
-    return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2>(a, max_mb, d, partial, partial_bytes, s)
-                  : launch_fwd<kModeFc2, 256, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, s);
+      return narrow ? launch_fwd<kModeFc2, 128, 192, 2, 4>(a, max_mb, d, partial, partial_bytes, queues, s)
+                    : launch_fwd<kModeFc2, 128, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, queues, s);
+    return narrow ? launch_fwd<kModeFc2, 256, 192, 4, 2>(a, max_mb, d, partial, partial_bytes, queues, s)
+                  : launch_fwd<kModeFc2, 256, 256, 2, 4>(a, max_mb, d, partial, partial_bytes, queues, s);
   }
   const int grid = persistent_grid(max_mb * ((d + kBNW - 1) / kBNW));
   if (dtype == 1)

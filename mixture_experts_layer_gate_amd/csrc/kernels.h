@@ -43,6 +43,14 @@ hipError_t launch_dispatch_fused(const int32_t* idx, int64_t n, int E, int32_t* 
                                  int4* mblocks, int32_t* n_mblocks, hipStream_t s);
 
 // Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most block_rows rows.
+// The m-block count n_mblocks[0] heads a workspace piece of kPlanWords
+// words that also holds the tile queues of the FC1 and FC2 launches reading
+// the plan: 8 counters each (one per XCD), kTileQueueStride words apart so
+// that no two share a cache line, at kTileQueueFc1 and kTileQueueFc2 + q *
+// kTileQueueStride; the kernel that writes the count zeroes them.
+constexpr int kTileQueueStride = 64, kTileQueueWords = 8;
+constexpr int kTileQueueFc1 = kTileQueueStride, kTileQueueFc2 = kTileQueueFc1 + kTileQueueWords * kTileQueueStride;
+constexpr int kPlanWords = kTileQueueFc2 + kTileQueueWords * kTileQueueStride;
 int64_t max_mblocks(int64_t n_assign, int E);
 // With n_shared > 0, shared experts E .. E+n_shared-1 of T rows each follow the
 // routed rows (E + n_shared <= 1024).
@@ -69,13 +77,18 @@ struct SharedExperts {
 
 int choose_gemm_regime(int64_t T, int k, int E);
 int regime_block_rows(int regime);
+// queues: the 256-row forms take their tiles from the plan's tile queues
+// (n_mblocks must then head a plan piece of kPlanWords words, zeroed by the
+// kernel that wrote the plan); otherwise every workgroup takes a fixed share.
 hipError_t launch_fc1(int dtype, int regime, const void* x, const int32_t* perm, int k, int64_t T,
                       const void* w1, const void* w3, void* h, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s);
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, bool queues,
+                      hipStream_t s);
 hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void* y, const int4* mblocks,
                       const int32_t* n_mblocks, int64_t max_mb, int64_t est_mb, int64_t d, int64_t f,
-                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, hipStream_t s);
+                      const SharedExperts& sh, float* partial, size_t partial_bytes, bool packed, bool queues,
+                      hipStream_t s);
 // Forward weights in stage order (packed = true above): each of w1, w3, w2
 // re-laid within its own E x N x K footprint (bf16, N, K multiples of 64).
 hipError_t launch_pack_weights(const void* w1, const void* w3, const void* w2, void* w1p, void* w3p, void* w2p,

@@ -143,7 +143,7 @@ size_t ffn_ws(const moe_dims_t* dm, void* ws, FfnWs* out, int n_shared = 0) {
   r.mblocks_off = c.off;
   r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
   r.n_mblocks_off = c.off;
-  r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
+  r.n_mblocks = c.take<int32_t>(sizeof(int32_t) * kPlanWords);  // count + tile queues
   r.h = c.take<char>(size_t(elt_bytes(dm)) * ffn_rows(dm, n_shared) * dm->f);
   r.sync_off = c.off;
   r.sync = c.take<int32_t>(sizeof(int32_t) * fused_sync_words(r.max_mb));  // fused FFN's readiness counters
@@ -228,7 +228,7 @@ size_t bwd_ws(const moe_dims_t* dm, void* ws, BwdWs* out) {
   r.max_mb = max_mblocks(P, dm->E);
   r.pp = (P + 63) / 64 * 64 + 64 * E;
   r.mblocks = c.take<int4>(sizeof(int4) * size_t(r.max_mb));
-  r.n_mblocks = c.take<int32_t>(sizeof(int32_t));
+  r.n_mblocks = c.take<int32_t>(sizeof(int32_t) * kPlanWords);  // count + tile queues
   r.gu = c.take<char>(size_t(2) * P * 2 * f);
   r.dgu = c.take<char>(size_t(2) * P * 2 * f);
   r.q = c.take<float>(sizeof(float) * P * f);
@@ -313,6 +313,16 @@ int layer_regime(const moe_dims_t* dm, bool packed) {
   return packed && r == 0 ? 1 : r;
 }
 
+// Tile queues pay where experts' rows span several m-blocks: tiles then differ
+// in length (partial m-blocks) and fixed shares left CUs and XCDs idle at the
+// end of the DBRX- and Mixtral-prefill-shaped launches. Where every expert's
+// rows are expected within one m-block (weight streaming, tiles of one
+// length), the fixed shares measured faster.
+bool ffn_tile_queues(const moe_dims_t* dm, int regime) {
+  const int64_t n = dm->T * dm->k, active = n < dm->E ? n : dm->E;
+  return active > 0 && (n + active - 1) / active > regime_block_rows(regime);
+}
+
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
            const FfnWs& fw, hipStream_t s, bool planned = false, const SharedExperts& sh = SharedExperts{},
@@ -327,13 +337,13 @@ int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32
     StageScope sc(MOE_STAGE_FC1, s);
     if (int st = hip_status(launch_fc1(dm->dtype, regime, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
                                        fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, fw.partial, fw.partial_bytes, packed,
-                                       s)))
+                                       ffn_tile_queues(dm, regime), s)))
       return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
   return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
                                expected_mblocks(dm, regime_block_rows(regime), fw.max_mb, sh.n), dm->d, dm->f, sh,
-                               fw.partial, fw.partial_bytes, packed, s));
+                               fw.partial, fw.partial_bytes, packed, ffn_tile_queues(dm, regime), s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
