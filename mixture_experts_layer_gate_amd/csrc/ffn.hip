@@ -1213,17 +1213,18 @@ __device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, 
 // rows may start as soon as that block's FC1 tiles are stored; MegaFlux,
 // section 2.1, MegaMoE's tiled FC1/FC2).
 //
-// Tiles are handed out by atomic counters, one per group of workgroups
-// b = x (mod 8) (the workgroups of one XCD): group x takes, in order, its share
-// of the FC1 tiles, then its share of the FC2 tiles, then its share of the
-// combine's blocks (512 16-byte vectors of the output, one per thread), each
-// share being the tiles the separate launches' XCD-aware numbering gives that
-// XCD (so neighbouring tiles meet in one L2).
+// The group of workgroups b = x (mod 8) (the workgroups of one XCD) owns, in
+// order, its share of the FC1 tiles, then its share of the FC2 tiles, then its
+// share of the combine's blocks (512 16-byte vectors of the output, one per
+// thread), each share being the tiles the separate launches' XCD-aware
+// numbering gives that XCD (so neighbouring tiles meet in one L2); workgroup r
+// of the group takes the group's units r, r + W, r + 2W, ... (W workgroups
+// per group), with no atomics, and chains consecutive 128-row FC1 tiles as the
+// separate launch does.
 // An FC2 tile waits until every FC1 tile of its m-block has been stored; a
 // combine block waits until every FC2 tile has. No launch can deadlock: a
-// group takes an FC2 tile only after all of its FC1 tiles are taken, every
-// taken FC1 tile belongs to a running workgroup that finishes it without
-// waiting, and likewise for FC2 tiles under the combine; the grid is a
+// workgroup starts its first FC2 tile only after all of its FC1 tiles, which
+// never wait, and likewise for FC2 tiles under the combine; the grid is a
 // multiple of 8, so every group has workgroups. This needs every workgroup of
 // the grid resident at once (the host checks the occupancy before the launch).
 // Each wait is bounded: past spin_limit polls the workgroup sets bit 0 of the
@@ -1231,9 +1232,8 @@ __device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, 
 // reads the word through moe_fused_status). Producers publish with a device-scope release
 // (their stores reach the point of coherence of every XCD's L2); consumers
 // take a device-scope acquire before reading.
-// sync words: [0..7] next tile of each group, [8] FC2 tiles stored,
-// [kFusedErrorWord] error flags, [10] next route tile, [11] route tiles
-// stored, [12] plan ready, [13] m-block count of the plan, [14] split FC1
+// sync words: [8] FC2 tiles stored, [kFusedErrorWord] error flags, [11] route
+// tiles stored, [12] plan ready, [13] m-block count of the plan, [14] split FC1
 // tiles summed, [16 + mb] FC1 tiles of m-block mb stored, then
 // [16 + max_mb + i] parts stored of split FC1 tile i and
 // [16 + max_mb + kMaxSplitTiles + i] of split FC2 tile i.
@@ -1249,8 +1249,8 @@ __device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, 
 // and the weight layout (as stored or in stage order) follow the separate
 // launches too, so the fused launch's outputs are bitwise theirs.
 //
-// Route and dispatch as the launch's first phases (front): workgroups first
-// take route tiles (one token each: its E logits in the contract order, one
+// Route and dispatch as the launch's first phases (front): workgroup b first
+// routes tokens b, b + G, ... (a route tile per token: its E logits in the contract order, one
 // wave per expert, then its top k and weights, the same device code as the
 // small-batch route kernel); the workgroup that stores the last route tile then
 // runs the one-workgroup dispatch and tile plan (the same device code as the
@@ -1264,7 +1264,7 @@ __device__ __forceinline__ void reduce_split_tile(const GemmArgs& g, int64_t t, 
 // instead routed and dispatched by every workgroup for itself, which costs a
 // few logits per workgroup and no wait at all.
 constexpr int kFusedSyncHead = 16;
-[[maybe_unused]] constexpr int kSyncRouteNext = 10, kSyncRouteDone = 11, kSyncPlanReady = 12, kSyncPlanCount = 13,
+[[maybe_unused]] constexpr int kSyncRouteDone = 11, kSyncPlanReady = 12, kSyncPlanCount = 13,
               kSyncSplit1Done = 14;
 // split tiles of one phase: fewer than the split target (the CU count)
 constexpr int kMaxSplitTiles = 1024;
@@ -1400,7 +1400,6 @@ __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
     fused_front_local(a, lds);
     return true;
   }
-  int64_t* s_tile = reinterpret_cast<int64_t*>(lds);
   int* s_flag = reinterpret_cast<int*>(lds + 8);
   float* srow = reinterpret_cast<float*>(lds + 64);        // [<= 64] logits of the token
   float* sel = reinterpret_cast<float*>(lds + 512);        // [<= 64] selected logits
@@ -1408,14 +1407,9 @@ __device__ __forceinline__ bool fused_front(const FusedFfnArgs& a, char* lds) {
   int32_t(*wh)[kMaxExperts] = reinterpret_cast<int32_t(*)[kMaxExperts]>(lds + 2048);  // [8][1024]
   int32_t* err = a.sync + kFusedErrorWord;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (;;) {
-    __syncthreads();
-    if (threadIdx.x == 0)
-      *s_tile = __hip_atomic_fetch_add(a.sync + kSyncRouteNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int64_t t = *s_tile;
-    __syncthreads();
-    if (t >= a.T) break;
+  // route tile t (one token) is workgroup t % G's, in token order
+  for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
+    __syncthreads();  // the previous tile's logits are read before they are rewritten
     for (int e = wv; e < a.E; e += 8) {
       const float l = gate_logit_wave<1, kFrontLoads>(a.fc1.A, a.wg, a.bias, t, e, a.d);
       if (lane == 0) {
@@ -1457,8 +1451,9 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
   static_assert(F1::NT == 512 && F2::NT == 512, "both tile forms use 8 waves");
   constexpr int LDS = F1::LDS_BYTES > F2::LDS_BYTES ? F1::LDS_BYTES : F2::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[LDS];
-  int64_t* s_tile = reinterpret_cast<int64_t*>(lds);  // the tile buffers are free between tiles
-  int* s_flag = reinterpret_cast<int*>(lds + 16);     // (free whenever a wait runs: before a tile's loads)
+  // an LDS word for the waits, free whenever a wait runs: between tiles, when
+  // no loads of a chained tile are in flight (publish() drains them first)
+  int* s_flag = reinterpret_cast<int*>(lds + 16);
   if (a.front && !fused_front(a, lds)) return;
   const int nmb = a.fc1.n_mblocks[0];
   const int nbc1 = static_cast<int>((a.fc1.N + 127) / 128);  // FC1 tiles per m-block
@@ -1480,57 +1475,79 @@ __global__ __launch_bounds__(512, 1) void ffn_fused_kernel(FusedFfnArgs a) {
   auto share = [&](int64_t n) { return (n / G) * W + min(max(n % G - x * W, int64_t(0)), W); };
   auto nth = [&](int64_t j) { return (j / W) * G + x * W + j % W; };
   const int64_t s1 = share(n1), s2 = share(n2), sc = share(nc);
-  for (;;) {
-    __syncthreads();  // the previous tile is done with the buffers
-    if (threadIdx.x == 0)
-      *s_tile = __hip_atomic_fetch_add(a.sync + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int64_t j = uniform(*s_tile);  // the same in every lane: scalar registers
-    __syncthreads();  // every thread has read it before the tile's loads refill the buffers
-    if (j < s1) {
-      const int64_t v = nth(j);
-      F1::tile(a.fc1, lds, v, [](int) {}, [&](int mb) {
-        if (v < c1.full) {
-          publish(done1 + mb);
-        } else {
-          const int64_t t = c1.full + (v - c1.full) / c1.sp;
-          if (last_part(parts1 + (t - c1.full), c1.sp, s_flag)) {
-            reduce_split_tile<true, BM, 256, 4>(a.fc1, t, c1, nbc1, nmb, threadIdx.x, 512);
-            publish(done1 + mb);
-            publish(a.sync + kSyncSplit1Done);
-          }
-        }
-      });
-    } else if (j < s1 + s2) {
-      const int64_t v = nth(j - s1);
-      const bool part = v >= c2.full;
-      F2::tile(a.fc2, lds, v,
-               [&](int mb) {
-                 wait_count(done1 + mb, nbc1, err, a.spin_limit, s_flag);
-                 // the partial buffer is free once every split FC1 tile is summed
-                 if (part && c1.sp > 1)
-                   wait_count(a.sync + kSyncSplit1Done, static_cast<int>(nt1 - c1.full), err, a.spin_limit, s_flag);
-               },
-               [&](int) {
-                 if (!part) {
-                   publish(fc2_done);
-                 } else {
-                   const int64_t t = c2.full + (v - c2.full) / c2.sp;
-                   if (last_part(parts2 + (t - c2.full), c2.sp, s_flag)) {
-                     reduce_split_tile<false, BM, BN2, WN2>(a.fc2, t, c2, nbc2, nmb, threadIdx.x, 512);
-                     publish(fc2_done);
-                   }
-                 }
-               });
-    } else if (j < s1 + s2 + sc) {
-      wait_count(fc2_done, static_cast<int>(nt2), err, a.spin_limit, s_flag);
-      const int64_t q = nth(j - s1 - s2) * kCombineVecs + threadIdx.x;
-      if (q < a.T * nvec)
-        combine_vec<1>(a.fc2.C, a.inv_perm, a.topk_w, a.out, a.d, a.k, a.T * a.k, a.n_shared, a.T, q / nvec,
-                       q % nvec);
+  // Workgroup r of group x takes the group's units r, r + W, r + 2W, ...: FC1
+  // tiles, then FC2 tiles, then combine units, in one fixed order (no claim
+  // atomics). FC1 tiles never wait, and a workgroup finishes all its FC1
+  // tiles before its first FC2 tile, which waits only for FC1 tiles; every
+  // workgroup is resident (checked on the host), so every wait is met.
+  const int64_t r = blockIdx.x / 8;
+  int64_t j = r;
+  auto post1 = [&](int64_t v, int mb) {
+    if (v < c1.full) {
+      publish(done1 + mb);
     } else {
-      break;
+      const int64_t t = c1.full + (v - c1.full) / c1.sp;
+      if (last_part(parts1 + (t - c1.full), c1.sp, s_flag)) {
+        reduce_split_tile<true, BM, 256, 4>(a.fc1, t, c1, nbc1, nmb, threadIdx.x, 512);
+        publish(done1 + mb);
+        publish(a.sync + kSyncSplit1Done);
+      }
     }
+  };
+  if constexpr (F1::kChain) {
+    // 128-row tiles chained as in the separate launch: the last K steps of a
+    // tile issue the next tile's first loads when both are whole tiles (then
+    // the tile's post only publishes, which touches no LDS)
+    if (j < s1) {
+      typename F1::Desc cur, nxt;
+      F1::describe(a.fc1, nth(j), cur);
+      int s0 = 0;
+      bool warm = false;
+      for (; j < s1; j += W) {
+        const int64_t v = nth(j);
+        const bool more = j + W < s1;
+        if (more) F1::describe(a.fc1, nth(j + W), nxt);
+        const bool chain = more && cur.sp == 1 && nxt.sp == 1 && nxt.nk >= F1::NBB;
+        F1::run_tile(a.fc1, lds, cur, nxt, chain ? nxt.nk : 0, s0, warm, [&](int mb) { post1(v, mb); });
+        s0 = chain ? s0 + cur.nk : 0;
+        warm = chain;
+        cur = nxt;
+      }
+    }
+  } else {
+    for (; j < s1; j += W) {
+      const int64_t v = nth(j);
+      F1::tile(a.fc1, lds, v, [](int) {}, [&](int mb) { post1(v, mb); });
+    }
+  }
+  for (; j < s1 + s2; j += W) {
+    const int64_t v = nth(j - s1);
+    const bool part = v >= c2.full;
+    F2::tile(a.fc2, lds, v,
+             [&](int mb) {
+               wait_count(done1 + mb, nbc1, err, a.spin_limit, s_flag);
+               // the partial buffer is free once every split FC1 tile is summed
+               if (part && c1.sp > 1)
+                 wait_count(a.sync + kSyncSplit1Done, static_cast<int>(nt1 - c1.full), err, a.spin_limit, s_flag);
+             },
+             [&](int) {
+               if (!part) {
+                 publish(fc2_done);
+               } else {
+                 const int64_t t = c2.full + (v - c2.full) / c2.sp;
+                 if (last_part(parts2 + (t - c2.full), c2.sp, s_flag)) {
+                   reduce_split_tile<false, BM, BN2, WN2>(a.fc2, t, c2, nbc2, nmb, threadIdx.x, 512);
+                   publish(fc2_done);
+                 }
+               }
+             });
+  }
+  if (j < s1 + s2 + sc) wait_count(fc2_done, static_cast<int>(nt2), err, a.spin_limit, s_flag);
+  for (; j < s1 + s2 + sc; j += W) {
+    const int64_t q = nth(j - s1 - s2) * kCombineVecs + threadIdx.x;
+    if (q < a.T * nvec)
+      combine_vec<1>(a.fc2.C, a.inv_perm, a.topk_w, a.out, a.d, a.k, a.T * a.k, a.n_shared, a.T, q / nvec,
+                     q % nvec);
   }
 #endif
 }
