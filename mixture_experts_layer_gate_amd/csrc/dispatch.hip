@@ -235,8 +235,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       mblocks[start + i] = make_int4(e, static_cast<int>(row0) + i * block_rows, r, tile_group(start, i, nb));
     }
   }
+  const int multi = __syncthreads_or(e < E + n_shared && nb > 1);
   if (e == 1023) {
     n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(before + incl), max_mb));
+    n_mblocks[kPlanMulti] = multi ? 1 : 0;
     for (int i = 0; i < 2 * kTileQueueWords; ++i) n_mblocks[kTileQueueFc1 + i * kTileQueueStride] = 0;
   }
 }

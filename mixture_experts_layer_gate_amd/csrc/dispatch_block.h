@@ -33,8 +33,8 @@ __device__ __forceinline__ int tile_group(int start, int i, int nb) {
 // path, whatever NT. Thread e scans expert e, so E <= NT; wh [NT/64][1024] and
 // wsum [NT/64] are LDS arrays of the caller; every thread of the workgroup
 // calls it. kQueues: the count heads a plan piece of the workspace, whose
-// tile-queue counters are zeroed with it (not where the fused launch keeps
-// the count among its readiness counters).
+// multi-block flag is written and tile-queue counters zeroed with it (not
+// where the fused launch keeps the count among its readiness counters).
 
 template <int NT, bool kQueues = false>
 __device__ __forceinline__ void dispatch_block(const int32_t* __restrict__ idx, int64_t n, int E,
@@ -98,10 +98,15 @@ __device__ __forceinline__ void dispatch_block(const int32_t* __restrict__ idx, 
       for (int i = 0; i < nb && start + i < max_mb; ++i)
         mblocks[start + i] = make_int4(tid, excl + i * block_rows, min(block_rows, c - i * block_rows),
                                        tile_group(start, i, nb));
-    if (tid == kFusedThreads - 1) {
-      n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(bbefore + bi), max_mb));
-      if constexpr (kQueues)
+    if constexpr (kQueues) {
+      const int multi = __syncthreads_or(tid < E && nb > 1);
+      if (tid == kFusedThreads - 1) {
+        n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(bbefore + bi), max_mb));
+        n_mblocks[kPlanMulti] = multi ? 1 : 0;
         for (int i = 0; i < 2 * kTileQueueWords; ++i) n_mblocks[kTileQueueFc1 + i * kTileQueueStride] = 0;
+      }
+    } else if (tid == kFusedThreads - 1) {
+      n_mblocks[0] = static_cast<int32_t>(min(static_cast<int64_t>(bbefore + bi), max_mb));
     }
   }
   __syncthreads();

@@ -1105,15 +1105,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dl_kernel(GemmArgs g) {
       warm = chain;
       cur = nxt;
     }
-  } else if (g.tileq != nullptr && G % 8 == 0) {
-    // Tile queues. Tiles of unequal length (partial m-blocks, the K parts of
-    // a last round) leave CUs and whole XCDs idle at the end of a launch whose
-    // workgroups each take a fixed share. Queue q lists, round by round, the
-    // tiles the fixed order gives XCD q (G/8 consecutive ones, which share
-    // operand panels in that L2); a workgroup takes the next tile of its own
-    // XCD's queue and, once that is drained, of the other queues. A queue's
-    // tile index grows with its counter, so a queue seen drained stays
-    // drained, and every tile is taken once.
+  } else if (g.tileq != nullptr && G % 8 == 0 && g.n_mblocks[kPlanMulti] != 0) {
+    // Tile queues, where some expert's rows span several m-blocks (else the
+    // tiles are of one length, the weights streamed once, and the fixed
+    // shares below measured faster). Tiles of unequal length (partial
+    // m-blocks, the K parts of a last round) leave CUs and whole XCDs idle at
+    // the end of a launch whose workgroups each take a fixed share. Queue q
+    // lists, round by round, the tiles the fixed order gives XCD q (G/8
+    // consecutive ones, which share operand panels in that L2); a workgroup
+    // takes the next tile of its own XCD's queue and, once that is drained,
+    // of the other queues. A queue's tile index grows with its counter, so a
+    // queue seen drained stays drained, and every tile is taken once.
     const int per = G / 8;
     int q = blockIdx.x % 8, left = 8;  // used by thread 0 only
     int64_t* bcast = reinterpret_cast<int64_t*>(lds);  // free between tiles

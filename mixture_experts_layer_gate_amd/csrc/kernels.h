@@ -44,10 +44,13 @@ hipError_t launch_dispatch_fused(const int32_t* idx, int64_t n, int E, int32_t* 
 
 // Tile plan: m-blocks (expert, first sorted row, rows, 0) of at most block_rows rows.
 // The m-block count n_mblocks[0] heads a workspace piece of kPlanWords
-// words that also holds the tile queues of the FC1 and FC2 launches reading
-// the plan: 8 counters each (one per XCD), kTileQueueStride words apart so
-// that no two share a cache line, at kTileQueueFc1 and kTileQueueFc2 + q *
-// kTileQueueStride; the kernel that writes the count zeroes them.
+// words that also holds, in word kPlanMulti, whether some expert's rows span
+// more than one m-block, and the tile queues of the FC1 and FC2 launches
+// reading the plan: 8 counters each (one per XCD), kTileQueueStride words
+// apart so that no two share a cache line, at kTileQueueFc1 and kTileQueueFc2
+// + q * kTileQueueStride; the kernel that writes the count writes the flag
+// and zeroes the counters.
+constexpr int kPlanMulti = 1;
 constexpr int kTileQueueStride = 64, kTileQueueWords = 8;
 constexpr int kTileQueueFc1 = kTileQueueStride, kTileQueueFc2 = kTileQueueFc1 + kTileQueueWords * kTileQueueStride;
 constexpr int kPlanWords = kTileQueueFc2 + kTileQueueWords * kTileQueueStride;

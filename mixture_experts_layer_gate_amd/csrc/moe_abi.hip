@@ -313,16 +313,6 @@ int layer_regime(const moe_dims_t* dm, bool packed) {
   return packed && r == 0 ? 1 : r;
 }
 
-// Tile queues pay where experts' rows span several m-blocks: tiles then differ
-// in length (partial m-blocks) and fixed shares left CUs and XCDs idle at the
-// end of the DBRX- and Mixtral-prefill-shaped launches. Where every expert's
-// rows are expected within one m-block (weight streaming, tiles of one
-// length), the fixed shares measured faster.
-bool ffn_tile_queues(const moe_dims_t* dm, int regime) {
-  const int64_t n = dm->T * dm->k, active = n < dm->E ? n : dm->E;
-  return active > 0 && (n + active - 1) / active > regime_block_rows(regime);
-}
-
 int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32_t* counts,
            const int32_t* offsets, const void* w1, const void* w3, const void* w2, void* y,
            const FfnWs& fw, hipStream_t s, bool planned = false, const SharedExperts& sh = SharedExperts{},
@@ -337,13 +327,13 @@ int do_ffn(const moe_dims_t* dm, const void* x, const int32_t* perm, const int32
     StageScope sc(MOE_STAGE_FC1, s);
     if (int st = hip_status(launch_fc1(dm->dtype, regime, x, perm, dm->k, dm->T, w1, w3, fw.h, fw.mblocks,
                                        fw.n_mblocks, fw.max_mb, dm->d, dm->f, sh, fw.partial, fw.partial_bytes, packed,
-                                       ffn_tile_queues(dm, regime), s)))
+                                       true, s)))
       return st;
   }
   StageScope sc(MOE_STAGE_FC2, s);
   return hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, y, fw.mblocks, fw.n_mblocks, fw.max_mb,
                                expected_mblocks(dm, regime_block_rows(regime), fw.max_mb, sh.n), dm->d, dm->f, sh,
-                               fw.partial, fw.partial_bytes, packed, ffn_tile_queues(dm, regime), s));
+                               fw.partial, fw.partial_bytes, packed, true, s));
 }
 
 int do_combine(const moe_dims_t* dm, const void* y, const int32_t* inv, const float* w, void* out,
