@@ -259,7 +259,9 @@ int moe_fused_status(const moe_dims_t* dims, const void* ws, size_t ws_bytes, in
  * the m-blocks the grouped FFN's tiles covered -- tile-aligned token blocks of
  * at most moe_ffn_block_rows rows, at most one partial block per expert
  * (MegaFlux, section 3.1) -- and the int32 at count_offset holds count
- * (<= *max_mblocks). Each m-block is four int32: expert, first sorted row,
+ * (<= *max_mblocks), and the int32 after it is 1 if some expert's rows span
+ * more than one m-block, else 0 (the grouped FFN's 256-row launches then take
+ * their tiles from per-XCD queues). Each m-block is four int32: expert, first sorted row,
  * rows, and (first m-block of its tile group << 4) | group size (the runs of
  * up to 8 m-blocks of one expert the GEMM walks together). n_shared = 0 for
  * layers without shared experts. MOE_ERR_INVALID for bad dims, a null

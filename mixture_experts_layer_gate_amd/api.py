@@ -296,6 +296,14 @@ def read_plan(dims: Dims, ws, n_shared: int = 0) -> torch.Tensor:
     return ws[mo:mo + 16 * count].cpu().view(torch.int32).view(count, 4).clone()
 
 
+def read_plan_multi_block(dims: Dims, ws, n_shared: int = 0) -> int:
+    """The plan's flag word after the m-block count (moe_layer_plan_layout): 1 if some expert's
+    rows span more than one m-block in the last layer call on ws. Synchronises the device."""
+    _, co, _ = plan_layout(dims, n_shared)
+    torch.cuda.synchronize()
+    return int(ws[co + 4:co + 8].cpu().view(torch.int32)[0])
+
+
 def layer_forward_noalloc(dims: Dims, x, wg, bias, w1, w3, w2, out, routing=None, stream=None):
     """moe_layer_forward_noalloc: the layer with the library's static scratch as workspace.
     out and the optional routing outputs (a dict of preallocated tensors under the names

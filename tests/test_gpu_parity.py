@@ -389,6 +389,7 @@ def test_full_size_workload(name):
     _say(f"  routing bit-exact; counts min {counts.min()} max {counts.max()} active {(counts > 0).sum()}")
     beta = moe.ffn_block_rows(dims)
     check_plan(plan, counts, ref["offsets"], beta, cfg.T * cfg.k)
+    assert moe.read_plan_multi_block(dims, ws) == int((counts > beta).any()), "plan's multi-block flag"
     _say(f"  plan: {len(plan)} m-blocks of <= {beta} rows, invariants hold")
     assert torch.isfinite(out.float()).all()
     w1, w3, w2 = (_host(inp[n], cfg.dtype) for n in ("w1", "w3", "w2"))

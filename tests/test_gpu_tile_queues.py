@@ -63,6 +63,7 @@ def test_queues_bitwise_equal_fixed_shares(shape, stage_order):
     packed = moe.pack_weights(dims, inp["w1"], inp["w3"], inp["w2"]) if stage_order else None
     ws = torch.empty(moe.workspace_bytes(dims), dtype=torch.uint8, device="cuda")
     ref = _run(dims, inp, ws, packed, queues=False)
+    assert moe.read_plan_multi_block(dims, ws) == 1, "these shapes have experts of several m-blocks"
     for rep in range(2):  # the second call reuses the workspace: the plan re-arms the queues
         got = _run(dims, inp, ws, packed, queues=True)
         assert torch.equal(got, ref), f"call {rep}: queued tile order changed the output bits"
