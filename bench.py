@@ -10,6 +10,7 @@ moe_layer_forward on the weights as stored.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceilings]
   python bench.py --backward [--workload NAME] ...   (the layer's backward instead)
+  python bench.py --backward --saved ...             (with FC1's g|u kept by the forward)
 
 The default workload is the Mixtral-8x22B-shaped prefill layer (T=8192,
 d=6144, f=16384, E=8, top-2, bf16, routing skewed by the gate-logit bias
@@ -66,6 +67,9 @@ def parse():
                         "weights as stored; auto: packed for bf16 layers without shared experts")
     p.add_argument("--backward", action="store_true",
                    help="time the layer's backward (moe_layer_backward) instead of the forward")
+    p.add_argument("--saved", action="store_true",
+                   help="with --backward: the forward keeps FC1's g|u (moe_layer_forward_train) and the backward "
+                        "reads it (moe_layer_backward_saved); also times forward + backward both ways")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run 5 device copies of 1 GiB (reference kernel for HBM byte counters)")
     return p.parse_args()
@@ -375,20 +379,58 @@ def run_backward(args, seed: int) -> dict:
     dout = moe_inputs.output_grad(cfg.T, cfg.d, cfg.dtype, seed, dev)
     dims = moe.Dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.torch_dtype)
     stream = torch.cuda.current_stream()
-    _, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
-                             return_routing=True)
+    gu = None
+    if args.saved:
+        _, r, gu = moe.layer_forward_train(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"],
+                                           inp["w2"])
+    else:
+        _, r = moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                 return_routing=True)
     counts = r["counts"].cpu().tolist()
     ws = torch.empty(moe.backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     grads = moe.layer_backward(dims, inp["x"], inp["wg"], inp["w1"], inp["w3"], inp["w2"], r, dout, ws=ws,
-                               want_dlogits=True, want_dtopk_w=True)
+                               want_dlogits=True, want_dtopk_w=True, gu=gu)
 
-    def step():
+    def step(keep=gu):
         moe.layer_backward(dims, inp["x"], inp["wg"], inp["w1"], inp["w3"], inp["w2"], r, dout, ws=ws,
-                           stream=stream, want_dlogits=True, want_dtopk_w=True, grads=grads)
+                           stream=stream, want_dlogits=True, want_dtopk_w=True, grads=grads, gu=keep)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    pair = None
+    if args.saved:
+        # forward + backward both ways, same process and buffers: the plain
+        # forward with the FC1 recompute, and the forward keeping g | u
+        fws = moe.make_workspace(dims, dev)
+        out = torch.empty((cfg.T, cfg.d), dtype=cfg.torch_dtype, device=dev)
+
+        def fwd_plain():
+            moe.layer_forward(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], out=out,
+                              ws=fws, stream=stream)
+
+        def fwd_train():
+            moe.layer_forward_train(dims, inp["x"], inp["wg"], inp["bias"], inp["w1"], inp["w3"], inp["w2"],
+                                    out=out, gu=gu, ws=fws, stream=stream)
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+        pair = {"forward_ms": timed(fwd_plain), "backward_ms": timed(lambda: step(None)),
+                "forward_train_ms": timed(fwd_train), "backward_saved_ms": timed(step)}
+        pair = {n: round(v, 4) for n, v in pair.items()}
+        pair["step_ms_recompute"] = round(pair["forward_ms"] + pair["backward_ms"], 4)
+        pair["step_ms_saved"] = round(pair["forward_train_ms"] + pair["backward_saved_ms"], 4)
+        pair["gu_bytes"] = gu.numel() * gu.element_size()
+        del fws, out
     bwd = [s_ for s_ in moe.STAGES if s_.startswith("bwd_")] + ["plan"]
     # untimed pass with every stage recorded: per-stage times, and the dominant GEMM
     nbreak = min(args.steps, 5)
@@ -441,15 +483,18 @@ def run_backward(args, seed: int) -> dict:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "pass": "backward", "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+        "config": {"workload": cfg.name, "pass": "backward (g|u kept by the forward)" if args.saved else "backward",
+                   "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "k": cfg.k, "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 1),
-                  "recompute_tflop": round(rf.fc1_flops(P, cfg.d, cfg.f) / 1e12, 3),
+                  "recompute_tflop": 0.0 if args.saved else round(rf.fc1_flops(P, cfg.d, cfg.f) / 1e12, 3),
                   "kappa": round(rf.kappa(counts), 3), "active_experts": rf.active_experts(counts)},
         "gemm_tflops": gemm_rates,
         "stages_ms": {s_: round(v, 4) for s_, v in stage_ms.items()},
     }
+    if pair is not None:
+        res["train_pair"] = pair
     if not args.no_cpu_baseline:
         ntok = min(cfg.T, args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else 32)
         res["cpu_baseline"] = cpu_baseline_backward(cfg, inp, dout, ntok, seed)

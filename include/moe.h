@@ -352,6 +352,43 @@ int moe_layer_backward(const moe_dims_t* dims, const void* x, const void* wg, co
                        void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2,
                        float* dlogits, float* dtopk_w, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- training pair: FC1's g | u kept from the forward for the backward ----
+ * The backward above recomputes FC1 (g = x W1_e^T, u = x W3_e^T per sorted
+ * row) because the forward keeps only h. MegaFlux (section 2.1) runs the
+ * backward as its own DGrad and WGrad streams and is silent on what the
+ * forward saves; this pair trades [T*k][2f] bf16 of memory for that
+ * recompute (4 d f FLOP per sorted row).
+ *
+ * moe_layer_forward_train: moe_layer_forward (same arguments, routing outputs,
+ * optional NULLs and workspace, moe_workspace_bytes) plus the output
+ * gu [T*k][2f] bf16 (device, caller-allocated, 16-byte aligned; required when
+ * T > 0): row p holds g then u of sorted row p (the order of perm), rounded to
+ * bf16. FC1 runs over 256-row tiles of the same plan as the backward's
+ * recompute, so gu is bit for bit what moe_layer_backward computes internally;
+ * the same launch forms h = SiLU(g) u from the fp32 sums, as moe_layer_forward
+ * does, so `out` has the plain forward's arithmetic (it can differ from
+ * moe_layer_forward's in the last bf16 bit where that call sums a tile's K
+ * range in parts, and is held to the same 2e-2 bar against the fp64
+ * definition). bf16 only; d and f multiples of 256;
+ * no shared experts; errors as moe_layer_backward's limits
+ * (MOE_ERR_UNSUPPORTED) and moe_layer_forward's arguments.
+ *
+ * moe_layer_backward_saved: moe_layer_backward with `gu` (as written by
+ * moe_layer_forward_train for the same x, W1, W3 and routing arrays) read
+ * instead of recomputed; every output is bit for bit moe_layer_backward's.
+ * Same workspace (moe_backward_workspace_bytes), limits and errors; gu must be
+ * 16-byte aligned when T > 0 (MOE_ERR_INVALID otherwise). */
+int moe_layer_forward_train(const moe_dims_t* dims, const void* x, const void* wg, const float* bias,
+                            const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                            int32_t* perm, int32_t* inv_perm, void* gu, void* ws, size_t ws_bytes, void* stream);
+int moe_layer_backward_saved(const moe_dims_t* dims, const void* x, const void* wg, const void* w1,
+                             const void* w3, const void* w2, const int32_t* topk_idx, const float* topk_w,
+                             const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                             const int32_t* inv_perm, const void* dout, const void* gu, void* dx, float* dwg,
+                             float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits, float* dtopk_w,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ---- stage timing (instrumentation; process-wide, not thread-safe) ----
  * While enabled, every kernel the library launches is bracketed by HIP events
  * recorded on the stream it is launched on. Stages: */

@@ -11,6 +11,6 @@ from .api import (  # noqa: F401
     MoeError, Dims, workspace_bytes, route, permute, grouped_ffn, combine, layer_forward,
     library_path, load_library, STAGES, EXPORTS, make_workspace, timing_enable, timing_disable, timing_read,
     probe_hbm_read_gbps, probe_mfma_tflops, workspace_bytes_shared, layer_forward_shared,
-    backward_workspace_bytes, layer_backward, ffn_block_rows, gate_on_matrix_cores, pack_weights, pack_weights_transposed,
+    backward_workspace_bytes, layer_backward, layer_forward_train, ffn_block_rows, gate_on_matrix_cores, pack_weights, pack_weights_transposed,
     fused_status, plan_layout, read_plan, read_plan_multi_block, layer_forward_noalloc, NOALLOC_SCRATCH_BYTES,
 )

@@ -29,7 +29,8 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_workspace_bytes_shared", "moe_layer_forward_shared", "moe_backward_workspace_bytes",
            "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_gate_on_matrix_cores", "moe_pack_weights",
            "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed",
-           "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed"]
+           "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed", "moe_layer_forward_train",
+           "moe_layer_backward_saved"]
 
 # Bytes of the static scratch moe_layer_forward_noalloc uses (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h).
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -107,6 +108,8 @@ def load_library():
     lib.moe_backward_workspace_bytes.restype = _S
     lib.moe_backward_workspace_bytes.argtypes = [_DP]
     lib.moe_layer_backward.argtypes = [_DP] + [_P] * 21 + [_S, _P]
+    lib.moe_layer_forward_train.argtypes = [_DP] + [_P] * 16 + [_S, _P]
+    lib.moe_layer_backward_saved.argtypes = [_DP] + [_P] * 22 + [_S, _P]
     lib.moe_timing_enable.argtypes = [ctypes.c_int, ctypes.c_uint]
     lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.moe_probe_cus.restype = ctypes.c_int
@@ -368,6 +371,42 @@ def layer_forward(dims: Dims, x, wg, bias, w1, w3, w2, out=None, ws=None, stream
     return (out, r) if return_routing else out
 
 
+def layer_forward_train(dims: Dims, x, wg, bias, w1, w3, w2, out=None, gu=None, ws=None, stream=None):
+    """The layer's forward that also keeps FC1's g | u for the backward
+    (moe_layer_forward_train). Returns (out, routing, gu): routing as
+    layer_forward(..., return_routing=True) gives it, gu [T*k][2f] bf16 with
+    g then u of each sorted row; pass gu to layer_backward to skip its FC1
+    recompute."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", dims.dtype, (dims.T, dims.d))
+    _need(wg, "wg", dims.dtype, (dims.E, dims.d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (dims.E,))
+    for name, w, shp in (("w1", w1, (dims.E, dims.f, dims.d)), ("w3", w3, (dims.E, dims.f, dims.d)),
+                         ("w2", w2, (dims.E, dims.d, dims.f))):
+        _need(w, name, dims.dtype, shp)
+    n = dims.T * dims.k
+    if out is None:
+        out = torch.empty((dims.T, dims.d), dtype=dims.dtype, device=dev)
+    if gu is None:
+        gu = torch.empty((n, 2 * dims.f), dtype=dims.dtype, device=dev)
+    _need(gu, "gu", dims.dtype, (n, 2 * dims.f))
+    r = {"logits": torch.empty((dims.T, dims.E), dtype=torch.float32, device=dev),
+         "topk_idx": torch.empty((dims.T, dims.k), dtype=torch.int32, device=dev),
+         "topk_w": torch.empty((dims.T, dims.k), dtype=torch.float32, device=dev),
+         "counts": torch.empty(dims.E, dtype=torch.int32, device=dev),
+         "offsets": torch.empty(dims.E + 1, dtype=torch.int32, device=dev),
+         "perm": torch.empty(n, dtype=torch.int32, device=dev),
+         "inv_perm": torch.empty(n, dtype=torch.int32, device=dev)}
+    ws, nws = _ws(dims, ws)
+    _check("moe_layer_forward_train", lib.moe_layer_forward_train(
+        ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+        _ptr(r["logits"]), _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+        _ptr(r["perm"]), _ptr(r["inv_perm"]), _ptr(gu), _ptr(ws), nws, _stream(stream)))
+    return out, r, gu
+
+
 def workspace_bytes_shared(dims: Dims, n_shared: int) -> int:
     return int(load_library().moe_workspace_bytes_shared(ctypes.byref(dims.c()), n_shared))
 
@@ -414,14 +453,16 @@ def backward_workspace_bytes(dims: Dims) -> int:
 
 
 def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, stream=None,
-                   want_dlogits=False, want_dtopk_w=False, grads=None):
+                   want_dlogits=False, want_dtopk_w=False, grads=None, gu=None):
     """Gradients of the layer for output gradient dout [T][d] (bf16).
 
     routing: the forward's topk_idx, topk_w, counts, offsets, perm, inv_perm
     (layer_forward(..., return_routing=True)). Returns a dict with dx [T][d]
     (bf16), dwg [E][d], dbias [E], dw1, dw3 [E][f][d], dw2 [E][d][f] (fp32) and,
     when asked for, dlogits [T][E] and dtopk_w [T][k]. ``grads`` may hold
-    preallocated output tensors under those names."""
+    preallocated output tensors under those names. ``gu``: the g | u rows that
+    layer_forward_train kept (moe_layer_backward_saved; the same gradients
+    without the FC1 recompute)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", dims.dtype, (dims.T, dims.d))
@@ -450,12 +491,16 @@ def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, 
         _need(g[name], name, dt, shp)
     if ws is None:
         ws = torch.empty(max(backward_workspace_bytes(dims), 256), dtype=torch.uint8, device=dev)
-    _check("moe_layer_backward", lib.moe_layer_backward(
-        ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(routing["topk_idx"]),
-        _ptr(routing["topk_w"]), _ptr(routing["counts"]), _ptr(routing["offsets"]), _ptr(routing["perm"]),
-        _ptr(routing["inv_perm"]), _ptr(dout), _ptr(g["dx"]), _ptr(g["dwg"]), _ptr(g["dbias"]), _ptr(g["dw1"]),
-        _ptr(g["dw3"]), _ptr(g["dw2"]), _ptr(g.get("dlogits")), _ptr(g.get("dtopk_w")), _ptr(ws), ws.numel(),
-        _stream(stream)))
+    head = (ctypes.byref(dims.c()), _ptr(x), _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(routing["topk_idx"]),
+            _ptr(routing["topk_w"]), _ptr(routing["counts"]), _ptr(routing["offsets"]), _ptr(routing["perm"]),
+            _ptr(routing["inv_perm"]), _ptr(dout))
+    tail = (_ptr(g["dx"]), _ptr(g["dwg"]), _ptr(g["dbias"]), _ptr(g["dw1"]), _ptr(g["dw3"]), _ptr(g["dw2"]),
+            _ptr(g.get("dlogits")), _ptr(g.get("dtopk_w")), _ptr(ws), ws.numel(), _stream(stream))
+    if gu is None:
+        _check("moe_layer_backward", lib.moe_layer_backward(*head, *tail))
+    else:
+        _need(gu, "gu", dims.dtype, (n, 2 * dims.f))
+        _check("moe_layer_backward_saved", lib.moe_layer_backward_saved(*head, _ptr(gu), *tail))
     return g
 
 

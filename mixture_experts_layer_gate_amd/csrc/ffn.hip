@@ -48,8 +48,10 @@ struct GemmArgs {
   const void* S0;         // shared experts' W1 (FC1) or W2 (FC2), [S][N][K]
   const void* S1;         // shared experts' W3 (FC1)
   int E_routed;           // experts e >= E_routed are shared expert e - E_routed
-  // weight gradients only (C[e] = A_e B_e^T with K = the expert's padded rows):
-  void* C2;               // second output tensor, for output rows >= split
+  // g | u form: h [rows][N] bf16 (from the fp32 sums) as well when non-null. Weight gradients
+  // (C[e] = A_e B_e^T with K = the expert's padded rows): the second output
+  // tensor, for output rows >= split.
+  void* C2;
   const int32_t* kofs;    // [E+1] first padded column of each expert in A and B
   int64_t pitch;          // row pitch (elements) of the transposed operands A and B
   int64_t M;              // output rows per expert (rows of A)
@@ -390,7 +392,7 @@ __device__ __forceinline__ void lds_barrier() {
 enum GemmMode : int {
   kModeFc1 = 0,    // h = SiLU(x W1^T) * (x W3^T), A rows gathered by token, bf16 out
   kModeFc2 = 1,    // y = h W2^T, A = the m-block's rows, bf16 out
-  kModeFc1GU = 2,  // g | u = x W1^T | x W3^T stored side by side ([rows][2N] bf16): the backward's recompute
+  kModeFc1GU = 2,  // g | u = x W1^T | x W3^T stored side by side ([rows][2N] bf16), optionally h as well
   kModeBwdQ = 3,   // q = dout W2 (B = W2 as stored, [K][N]), A rows gathered by token, fp32 out
   kModeBwdDx = 4,  // dx rows += dg W1 or du W3 (A = one half of the dg|du rows, B as stored, K = f), fp32 out
   kModeWgrad = 5,  // dW_e = A_e B_e^T, K = expert e's padded rows, fp32 out
@@ -1009,6 +1011,35 @@ struct DlGemm {
       static_assert(BM * CW * 2 <= LDS_BYTES, "epilogue tile fits in the stage buffers");
       lds_barrier();
       bf16_t* ct = reinterpret_cast<bf16_t*>(lds);
+      if constexpr (kMode == kModeFc1GU) {
+        if (g.C2 != nullptr) {
+          // h = SiLU(g) u from the fp32 accumulators, as the plain FC1 forms
+          // it, in a pass of its own ([BM][BN/2] through the same buffer)
+          constexpr int HW = BN / 2, HPR = HW / 8;
+#pragma unroll
+          for (int i = 0; i < MI16; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int r = wm * TM + 16 * i + 4 * (lane >> 4) + v;
+#pragma unroll
+              for (int j = 0; j < NJ16 / 2; ++j) {
+                const int c = wn * (TN / 2) + 16 * j + (lane & 15);
+                ct[r * HW + c] = static_cast<bf16_t>(f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + NJ16 / 2][v])));
+              }
+            }
+          }
+          __syncthreads();
+          bf16_t* H = static_cast<bf16_t*>(g.C2);
+          const int64_t col0 = static_cast<int64_t>(nb) * HW;
+          for (int q = tid; q < rows * HPR; q += NT) {
+            const int r = q / HPR, c8 = (q % HPR) * 8;
+            if (col0 + c8 < N)
+              *reinterpret_cast<u32x4_t*>(H + static_cast<int64_t>(row0 + r) * N + col0 + c8) =
+                  *reinterpret_cast<const u32x4_t*>(ct + r * HW + c8);
+          }
+          __syncthreads();  // h is read out before g | u refill the buffer
+        }
+      }
 #pragma unroll
       for (int i = 0; i < MI16; ++i) {
 #pragma unroll
@@ -1848,8 +1879,9 @@ hipError_t launch_fc2(int dtype, int regime, const void* h, const void* w2, void
 
 hipError_t launch_fc1_gu(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
                          void* gu, const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d,
-                         int64_t f, hipStream_t s) {
+                         int64_t f, hipStream_t s, void* h) {
   GemmArgs a{x, perm, k, T, w1, w3, gu, mblocks, n_mblocks, d, f, T * k, nullptr, nullptr, INT32_MAX};
+  a.C2 = h;
   return launch_big<kModeFc1GU, 256, 256, 2, 4>(a, max_mb, f, s);
 }
 

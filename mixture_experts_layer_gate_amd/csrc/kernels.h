@@ -146,10 +146,12 @@ hipError_t launch_combine(int dtype, const void* y, const int32_t* inv_perm, con
                           void* out, int64_t T, int64_t d, int k, hipStream_t s, int n_shared = 0);
 
 // ---------------- backward (bf16; d and f multiples of 256) ----------------
-// Recompute of FC1 for the backward: g | u side by side, gu [rows][2f] bf16.
+// FC1 with g | u kept: gu [rows][2f] bf16 side by side (the backward's
+// recompute), and, with h non-null, h [rows][f] bf16 = SiLU(g) u from the
+// fp32 sums, as the plain FC1 forms it (the training forward).
 hipError_t launch_fc1_gu(const void* x, const int32_t* perm, int k, int64_t T, const void* w1, const void* w3,
                          void* gu, const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d,
-                         int64_t f, hipStream_t s);
+                         int64_t f, hipStream_t s, void* h = nullptr);
 // q[p] = dout[token(p)] W2_e (w2 as stored, [E][d][f], read through transposing LDS loads), fp32 [rows][f].
 hipError_t launch_bwd_q(const void* dout, const int32_t* perm, int k, int64_t T, const void* w2, float* q,
                         const int4* mblocks, const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f,

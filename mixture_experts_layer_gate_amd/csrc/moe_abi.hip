@@ -717,16 +717,81 @@ int moe_layer_forward_shared(const moe_dims_t* dm, int n_shared, const void* x, 
                    inv_perm, ws, ws_bytes, stream);
 }
 
+// The forward with FC1's g | u kept for the backward: route, dispatch, FC1 in
+// its g | u form over 256-row tiles (the backward's own tile plan, so the
+// stored g | u is bit for bit the backward's recompute) with h derived from
+// the stored values in the same epilogue, then FC2 and the combine as in the
+// plain forward.
+int moe_layer_forward_train(const moe_dims_t* dm, const void* x, const void* wg, const float* bias,
+                            const void* w1, const void* w3, const void* w2, void* out, float* logits,
+                            int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                            int32_t* inv_perm, void* gu, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_dims(dm)) return st;
+  if (int st = bwd_shape_ok(dm)) return st;
+  if (dm->T == 0) return MOE_OK;
+  if (!ok16(x) || !ok16(wg) || !ok4_or_null(bias) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(out) ||
+      !ok16(gu) || !ok4_or_null(logits) || !ok4_or_null(topk_idx) || !ok4_or_null(topk_w) ||
+      !ok4_or_null(counts) || !ok4_or_null(offsets) || !ok4_or_null(perm) || !ok4_or_null(inv_perm))
+    return MOE_ERR_INVALID;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % kAlign)) return ws ? MOE_ERR_INVALID : MOE_ERR_WORKSPACE;
+  if (ws_bytes < layer_ws(dm, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  LayerWs lw{};
+  layer_ws(dm, ws, &lw);
+  if (!logits) logits = lw.logits;
+  if (!topk_idx) topk_idx = lw.idx;
+  if (!topk_w) topk_w = lw.w;
+  if (!counts) counts = lw.counts;
+  if (!offsets) offsets = lw.offsets;
+  if (!perm) perm = lw.perm;
+  if (!inv_perm) inv_perm = lw.inv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n = dm->T * dm->k;
+  if (int st = do_route(dm, x, wg, bias, logits, topk_idx, topk_w, s)) return st;
+  PermuteWs pw{};
+  permute_ws(dm, lw.sub, &pw);
+  if (int st = do_permute(dm, topk_idx, counts, offsets, perm, inv_perm, pw, s)) return st;
+  FfnWs fw{};
+  ffn_ws(dm, lw.sub, &fw);  // the permute scratch is dead once the permutation is written
+  {
+    StageScope sc(MOE_STAGE_PLAN, s);
+    if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, 256, fw.mblocks, fw.n_mblocks, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_FC1, s);
+    if (int st = hip_status(launch_fc1_gu(x, perm, dm->k, dm->T, w1, w3, gu, fw.mblocks, fw.n_mblocks, fw.max_mb,
+                                          dm->d, dm->f, s, fw.h)))
+      return st;
+  }
+  const int regime = gemm_regime(dm);
+  const int br = regime_block_rows(regime);
+  if (br != 256) {
+    StageScope sc(MOE_STAGE_PLAN, s);
+    if (int st = hip_status(launch_plan(counts, offsets, dm->E, n, fw.max_mb, br, fw.mblocks, fw.n_mblocks, s)))
+      return st;
+  }
+  {
+    StageScope sc(MOE_STAGE_FC2, s);
+    if (int st = hip_status(launch_fc2(dm->dtype, regime, fw.h, w2, lw.y, fw.mblocks, fw.n_mblocks, fw.max_mb,
+                                       expected_mblocks(dm, br, fw.max_mb, 0), dm->d, dm->f, SharedExperts{},
+                                       fw.partial, fw.partial_bytes, false, true, s)))
+      return st;
+  }
+  return do_combine(dm, lw.y, inv_perm, topk_w, out, s);
+}
+
 size_t moe_backward_workspace_bytes(const moe_dims_t* dm) {
   if (check_dims(dm) != MOE_OK) return 0;
   return bwd_ws(dm, nullptr, nullptr);
 }
 
-int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
-                       const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
-                       const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
-                       void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits,
-                       float* dtopk_w, void* ws, size_t ws_bytes, void* stream) {
+// gu_saved: g | u rows kept by moe_layer_forward_train (read instead of the
+// FC1 recompute), or null.
+static int run_backward(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
+                        const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                        const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
+                        void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits,
+                        float* dtopk_w, const void* gu_saved, void* ws, size_t ws_bytes, void* stream) {
   if (int st = check_dims(dm)) return st;
   if (!ok16(wg) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(dwg) || !ok4(dbias) || !ok16(dw1) || !ok16(dw3) ||
       !ok16(dw2) || !ok4(counts) || !ok4(offsets) || !ok4_or_null(dlogits) || !ok4_or_null(dtopk_w))
@@ -753,7 +818,9 @@ int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, cons
     StageScope sc(MOE_STAGE_PLAN, s);
     if (int st = hip_status(launch_plan(counts, offsets, E, P, b.max_mb, 256, b.mblocks, b.n_mblocks, s))) return st;
   }
-  {
+  if (gu_saved) {
+    b.gu = const_cast<void*>(gu_saved);  // only read from here on
+  } else {
     StageScope sc(MOE_STAGE_BWD_FC1, s);
     if (int st = hip_status(launch_fc1_gu(x, perm, k, T, w1, w3, b.gu, b.mblocks, b.n_mblocks, b.max_mb, d, f, s)))
       return st;
@@ -806,6 +873,26 @@ int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, cons
   }
   StageScope sc(MOE_STAGE_BWD_GATE, s);
   return hip_status(launch_gate_grad(x, perm, offsets, b.dl, T, k, d, E, b.gpart, b.bpart, dwg, dbias, s));
+}
+
+int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
+                       const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
+                       void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits,
+                       float* dtopk_w, void* ws, size_t ws_bytes, void* stream) {
+  return run_backward(dm, x, wg, w1, w3, w2, topk_idx, topk_w, counts, offsets, perm, inv_perm, dout, dx, dwg, dbias,
+                      dw1, dw3, dw2, dlogits, dtopk_w, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_layer_backward_saved(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
+                             const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                             const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
+                             const void* dout, const void* gu, void* dx, float* dwg, float* dbias, float* dw1,
+                             float* dw3, float* dw2, float* dlogits, float* dtopk_w, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (dm && dm->T > 0 && !ok16(gu)) return MOE_ERR_INVALID;
+  return run_backward(dm, x, wg, w1, w3, w2, topk_idx, topk_w, counts, offsets, perm, inv_perm, dout, dx, dwg, dbias,
+                      dw1, dw3, dw2, dlogits, dtopk_w, gu, ws, ws_bytes, stream);
 }
 
 int moe_timing_enable(int capacity, unsigned stage_mask) {

@@ -229,6 +229,36 @@ def test_layer_backward_validation():
     assert lib.moe_backward_workspace_bytes(ctypes.byref(_dims(k=0))) == 0
 
 
+@needs_no_gpu
+def test_training_pair_validation():
+    """moe_layer_forward_train and moe_layer_backward_saved check the kept g | u
+    buffer and the backward's limits before anything is launched."""
+    lib = moe.load_library()
+    good = dict(d=256, f=512)
+
+    def fwd(dims=None, gu=A, ws_bytes=1 << 40):
+        dm = _dims(**{**good, **(dims or {})})
+        return lib.moe_layer_forward_train(ctypes.byref(dm), A, A, None, A, A, A, A, None, None, None, None, None,
+                                           None, None, gu, A, ws_bytes, None)
+    assert fwd(gu=None) == 1                         # g | u output required
+    assert fwd(gu=A + 8) == 1                        # and 16-byte aligned
+    assert fwd(dims=dict(dtype=0)) == 2              # bf16 only, as the backward
+    assert fwd(dims=dict(d=192)) == 2                # d % 256 != 0
+    assert fwd(dims=dict(f=320)) == 2                # f % 256 != 0
+    assert fwd(ws_bytes=16) == 3                     # the forward's workspace
+    assert fwd(dims=dict(T=0), gu=None) == 0         # empty batch: nothing to do
+
+    def bwd(dims=None, gu=A, ws_bytes=1 << 40):
+        dm = _dims(**{**good, **(dims or {})})
+        return lib.moe_layer_backward_saved(ctypes.byref(dm), A, A, A, A, A, A, A, A, A, A, A, A, gu, A, A, A, A,
+                                            A, A, None, None, A, ws_bytes, None)
+    assert bwd(gu=None) == 1
+    assert bwd(gu=A + 8) == 1
+    assert bwd(dims=dict(dtype=0)) == 2
+    assert bwd(dims=dict(f=320)) == 2
+    assert bwd(ws_bytes=16) == 3
+
+
 def test_plan_layout_inside_the_workspace():
     """The tile plan's m-block list and count lie inside the layer workspace, 16- and
     4-byte aligned, and the list holds the most m-blocks any plan of the shape can have:
