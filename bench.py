@@ -11,6 +11,7 @@ moe_layer_forward on the weights as stored.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceilings]
   python bench.py --backward [--workload NAME] ...   (the layer's backward instead)
   python bench.py --backward --saved ...             (with FC1's g|u kept by the forward)
+  python bench.py --backward --wgrad-bf16 ...        (weight gradients written as bf16)
 
 The default workload is the Mixtral-8x22B-shaped prefill layer (T=8192,
 d=6144, f=16384, E=8, top-2, bf16, routing skewed by the gate-logit bias
@@ -67,6 +68,8 @@ def parse():
                         "weights as stored; auto: packed for bf16 layers without shared experts")
     p.add_argument("--backward", action="store_true",
                    help="time the layer's backward (moe_layer_backward) instead of the forward")
+    p.add_argument("--wgrad-bf16", action="store_true",
+                   help="with --backward: weight gradients written as bf16 (moe_layer_backward_ex)")
     p.add_argument("--saved", action="store_true",
                    help="with --backward: the forward keeps FC1's g|u (moe_layer_forward_train) and the backward "
                         "reads it (moe_layer_backward_saved); also times forward + backward both ways")
@@ -388,12 +391,14 @@ def run_backward(args, seed: int) -> dict:
                                  return_routing=True)
     counts = r["counts"].cpu().tolist()
     ws = torch.empty(moe.backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    wdt = torch.bfloat16 if args.wgrad_bf16 else torch.float32
     grads = moe.layer_backward(dims, inp["x"], inp["wg"], inp["w1"], inp["w3"], inp["w2"], r, dout, ws=ws,
-                               want_dlogits=True, want_dtopk_w=True, gu=gu)
+                               want_dlogits=True, want_dtopk_w=True, gu=gu, wgrad_dtype=wdt)
 
     def step(keep=gu):
         moe.layer_backward(dims, inp["x"], inp["wg"], inp["w1"], inp["w3"], inp["w2"], r, dout, ws=ws,
-                           stream=stream, want_dlogits=True, want_dtopk_w=True, grads=grads, gu=keep)
+                           stream=stream, want_dlogits=True, want_dtopk_w=True, grads=grads, gu=keep,
+                           wgrad_dtype=wdt)
 
     for _ in range(args.warmup):
         step()
@@ -484,7 +489,8 @@ def run_backward(args, seed: int) -> dict:
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "pass": "backward (g|u kept by the forward)" if args.saved else "backward",
-                   "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
+                   "weight_grads": "bf16" if args.wgrad_bf16 else "fp32", "T": cfg.T, "d": cfg.d, "f": cfg.f,
+                   "E": cfg.E,
                    "k": cfg.k, "bias_scale": cfg.bias_scale, "seed": seed, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 1),

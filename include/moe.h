@@ -389,6 +389,23 @@ int moe_layer_backward_saved(const moe_dims_t* dims, const void* x, const void* 
                              float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits, float* dtopk_w,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_backward with its options in one call: `gu` NULL recomputes FC1
+ * (moe_layer_backward), non-NULL reads it (moe_layer_backward_saved; 16-byte
+ * aligned); `wgrad_dtype` MOE_DTYPE_F32 writes dw1, dw3, dw2 as fp32 (as those
+ * two calls do), MOE_DTYPE_BF16 as bf16 [same shapes], each element the
+ * round-to-nearest-even bf16 of the fp32 value the fp32 form writes. The bf16
+ * form halves the bytes the weight-gradient products write (3 E d f values
+ * per call), which bound them when experts receive ~100 rows (the DeepSeek
+ * shape). dx, dwg, dbias, dlogits, dtopk_w are as in moe_layer_backward and
+ * bitwise the same. Workspace, limits and errors as moe_layer_backward;
+ * MOE_ERR_INVALID for another wgrad_dtype or a misaligned gu. */
+int moe_layer_backward_ex(const moe_dims_t* dims, const void* x, const void* wg, const void* w1, const void* w3,
+                          const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
+                          const void* gu, int wgrad_dtype, void* dx, float* dwg, float* dbias, void* dw1,
+                          void* dw3, void* dw2, float* dlogits, float* dtopk_w, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* ---- stage timing (instrumentation; process-wide, not thread-safe) ----
  * While enabled, every kernel the library launches is bracketed by HIP events
  * recorded on the stream it is launched on. Stages: */

@@ -30,7 +30,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_route
            "moe_layer_backward", "moe_layer_forward_fused", "moe_ffn_block_rows", "moe_gate_on_matrix_cores", "moe_pack_weights",
            "moe_layer_forward_packed", "moe_fused_status", "moe_layer_plan_layout", "moe_pack_weights_transposed",
            "moe_layer_forward_noalloc", "moe_layer_forward_fused_packed", "moe_layer_forward_train",
-           "moe_layer_backward_saved"]
+           "moe_layer_backward_saved", "moe_layer_backward_ex"]
 
 # Bytes of the static scratch moe_layer_forward_noalloc uses (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h).
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -110,6 +110,7 @@ def load_library():
     lib.moe_layer_backward.argtypes = [_DP] + [_P] * 21 + [_S, _P]
     lib.moe_layer_forward_train.argtypes = [_DP] + [_P] * 16 + [_S, _P]
     lib.moe_layer_backward_saved.argtypes = [_DP] + [_P] * 22 + [_S, _P]
+    lib.moe_layer_backward_ex.argtypes = [_DP] + [_P] * 13 + [ctypes.c_int] + [_P] * 9 + [_S, _P]
     lib.moe_timing_enable.argtypes = [ctypes.c_int, ctypes.c_uint]
     lib.moe_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.moe_probe_cus.restype = ctypes.c_int
@@ -453,7 +454,7 @@ def backward_workspace_bytes(dims: Dims) -> int:
 
 
 def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, stream=None,
-                   want_dlogits=False, want_dtopk_w=False, grads=None, gu=None):
+                   want_dlogits=False, want_dtopk_w=False, grads=None, gu=None, wgrad_dtype=torch.float32):
     """Gradients of the layer for output gradient dout [T][d] (bf16).
 
     routing: the forward's topk_idx, topk_w, counts, offsets, perm, inv_perm
@@ -462,7 +463,8 @@ def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, 
     when asked for, dlogits [T][E] and dtopk_w [T][k]. ``grads`` may hold
     preallocated output tensors under those names. ``gu``: the g | u rows that
     layer_forward_train kept (moe_layer_backward_saved; the same gradients
-    without the FC1 recompute)."""
+    without the FC1 recompute). ``wgrad_dtype`` torch.bfloat16 returns dw1,
+    dw3, dw2 in bf16, each the rounded fp32 value (moe_layer_backward_ex)."""
     lib = load_library()
     dev = x.device
     _need(x, "x", dims.dtype, (dims.T, dims.d))
@@ -478,9 +480,12 @@ def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, 
         _need(routing[name], name, dt, shp)
     g = dict(grads or {})
     f32 = torch.float32
+    if wgrad_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("wgrad_dtype must be torch.float32 or torch.bfloat16")
+    wt = wgrad_dtype
     shapes = {"dx": ((dims.T, dims.d), dims.dtype), "dwg": ((dims.E, dims.d), f32), "dbias": ((dims.E,), f32),
-              "dw1": ((dims.E, dims.f, dims.d), f32), "dw3": ((dims.E, dims.f, dims.d), f32),
-              "dw2": ((dims.E, dims.d, dims.f), f32)}
+              "dw1": ((dims.E, dims.f, dims.d), wt), "dw3": ((dims.E, dims.f, dims.d), wt),
+              "dw2": ((dims.E, dims.d, dims.f), wt)}
     if want_dlogits:
         shapes["dlogits"] = ((dims.T, dims.E), f32)
     if want_dtopk_w:
@@ -496,10 +501,13 @@ def layer_backward(dims: Dims, x, wg, w1, w3, w2, routing: dict, dout, ws=None, 
             _ptr(routing["inv_perm"]), _ptr(dout))
     tail = (_ptr(g["dx"]), _ptr(g["dwg"]), _ptr(g["dbias"]), _ptr(g["dw1"]), _ptr(g["dw3"]), _ptr(g["dw2"]),
             _ptr(g.get("dlogits")), _ptr(g.get("dtopk_w")), _ptr(ws), ws.numel(), _stream(stream))
-    if gu is None:
+    if gu is not None:
+        _need(gu, "gu", dims.dtype, (n, 2 * dims.f))
+    if wgrad_dtype == torch.bfloat16:
+        _check("moe_layer_backward_ex", lib.moe_layer_backward_ex(*head, _ptr(gu), 1, *tail))
+    elif gu is None:
         _check("moe_layer_backward", lib.moe_layer_backward(*head, *tail))
     else:
-        _need(gu, "gu", dims.dtype, (n, 2 * dims.f))
         _check("moe_layer_backward_saved", lib.moe_layer_backward_saved(*head, _ptr(gu), *tail))
     return g
 

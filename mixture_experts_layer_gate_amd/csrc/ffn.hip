@@ -61,6 +61,7 @@ struct GemmArgs {
   // and first column; fp32 forms: add to C instead of storing
   int64_t a_pitch, a_col0;
   int accumulate;
+  int out_bf16;           // weight gradients: store C (and C2) as bf16, rounded to nearest even
   // split K: the tiles past the last full round of split_target workgroups
   // (all of them in a launch with fewer tiles than CUs) have their K steps
   // cut into parts, each part's fp32 accumulators go to `partial`
@@ -395,7 +396,7 @@ enum GemmMode : int {
   kModeFc1GU = 2,  // g | u = x W1^T | x W3^T stored side by side ([rows][2N] bf16), optionally h as well
   kModeBwdQ = 3,   // q = dout W2 (B = W2 as stored, [K][N]), A rows gathered by token, fp32 out
   kModeBwdDx = 4,  // dx rows += dg W1 or du W3 (A = one half of the dg|du rows, B as stored, K = f), fp32 out
-  kModeWgrad = 5,  // dW_e = A_e B_e^T, K = expert e's padded rows, fp32 out
+  kModeWgrad = 5,  // dW_e = A_e B_e^T, K = expert e's padded rows, fp32 (or bf16) out
 };
 __host__ __device__ constexpr bool mode_gated(int m) { return m == kModeFc1 || m == kModeFc1GU; }
 __host__ __device__ constexpr bool mode_gather(int m) { return m == kModeFc1 || m == kModeFc1GU || m == kModeBwdQ; }
@@ -945,6 +946,7 @@ struct DlGemm {
       float* ct = reinterpret_cast<float*>(lds);
       // destination: rows of pitch cp from column col0, ncols columns in all
       float* cbase;
+      bf16_t* hbase = nullptr;  // weight gradients stored as bf16
       int64_t cp = N, col0 = static_cast<int64_t>(nb) * BN, ncols = N;
       if (sp > 1) {
         // one part of a split tile: the raw accumulators, [BM][BN]
@@ -953,8 +955,9 @@ struct DlGemm {
       } else if constexpr (kWgrad) {
         const int64_t m0 = static_cast<int64_t>(row0);
         const bool second = m0 >= g.split;
-        cbase = static_cast<float*>(second ? g.C2 : g.C) + static_cast<int64_t>(e) * g.split * N +
-                (second ? m0 - g.split : m0) * N;
+        const int64_t off = static_cast<int64_t>(e) * g.split * N + (second ? m0 - g.split : m0) * N;
+        cbase = static_cast<float*>(second ? g.C2 : g.C) + off;
+        if (g.out_bf16) hbase = static_cast<bf16_t*>(second ? g.C2 : g.C) + off;
       } else {
         cbase = static_cast<float*>(g.C) + static_cast<int64_t>(row0) * N;
       }
@@ -968,13 +971,32 @@ struct DlGemm {
           for (int j = 0; j < NJ16; ++j)
             ct[(wm * 16 + 4 * (lane >> 4) + v) * CP + wn * TN + 16 * j + (lane & 15)] = acc[i][j][v];
         __syncthreads();
-        for (int q = tid; q < SR * VPR; q += NT) {
-          const int rl = q / VPR, c4 = (q % VPR) * 4;
-          const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
-          if (r < rows && col0 + c4 < ncols) {
-            f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * cp + col0 + c4);
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
-            *dst = (g.accumulate && sp == 1) ? *dst + v : v;
+        if (kWgrad && hbase != nullptr) {
+          // bf16: 8 columns (16 bytes) per store
+          constexpr int VPR8 = BN / 8;
+          for (int q = tid; q < SR * VPR8; q += NT) {
+            const int rl = q / VPR8, c8 = (q % VPR8) * 8;
+            const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
+            if (r < rows && col0 + c8 < ncols) {
+              const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c8);
+              const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c8 + 4);
+              u32x4_t pk;
+              pk[0] = pack_bf16x2(v0[0], v0[1]);
+              pk[1] = pack_bf16x2(v0[2], v0[3]);
+              pk[2] = pack_bf16x2(v1[0], v1[1]);
+              pk[3] = pack_bf16x2(v1[2], v1[3]);
+              *reinterpret_cast<u32x4_t*>(hbase + static_cast<int64_t>(r) * cp + col0 + c8) = pk;
+            }
+          }
+        } else {
+          for (int q = tid; q < SR * VPR; q += NT) {
+            const int rl = q / VPR, c4 = (q % VPR) * 4;
+            const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
+            if (r < rows && col0 + c4 < ncols) {
+              f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * cp + col0 + c4);
+              const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
+              *dst = (g.accumulate && sp == 1) ? *dst + v : v;
+            }
           }
         }
       }
@@ -1904,10 +1926,11 @@ hipError_t launch_bwd_dx(const void* dgu, const void* w1, const void* w3, float*
   return launch_big<kModeBwdDx, 256, 256, 2, 4>(a, max_mb, d, s);
 }
 
-hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, const int32_t* kofs, int64_t pitch,
-                        int E, int64_t M, int64_t N, int64_t split, hipStream_t s) {
+hipError_t launch_wgrad(const void* at, const void* bt, void* c, void* c2, const int32_t* kofs, int64_t pitch,
+                        int E, int64_t M, int64_t N, int64_t split, hipStream_t s, bool out_bf16) {
   GemmArgs a{at, nullptr, 1, 0, bt, nullptr, c, nullptr, nullptr, 0, N, 0, nullptr, nullptr, INT32_MAX,
              c2, kofs, pitch, M, split, E};
+  a.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t tiles = static_cast<int64_t>(E) * (M / 256) * (N / 256);
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(tiles, device_cu_count())));
   hipLaunchKernelGGL((gemm_dl_kernel<kModeWgrad, 256, 256, 2, 4>), dim3(grid), dim3(512), 0, s, a);

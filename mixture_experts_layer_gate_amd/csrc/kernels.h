@@ -161,8 +161,9 @@ hipError_t launch_bwd_dx(const void* dgu, const void* w1, const void* w3, float*
                          const int32_t* n_mblocks, int64_t max_mb, int64_t d, int64_t f, hipStream_t s);
 // Weight gradients C_e = A_e B_e^T over expert e's padded K window [kofs[e], kofs[e+1]);
 // A [M][pitch], B [N][pitch] bf16; output rows >= split go to c2. M, N multiples of 256.
-hipError_t launch_wgrad(const void* at, const void* bt, float* c, float* c2, const int32_t* kofs, int64_t pitch,
-                        int E, int64_t M, int64_t N, int64_t split, hipStream_t s);
+// c and c2 fp32, or bf16 (the fp32 sums rounded to nearest even) with out_bf16.
+hipError_t launch_wgrad(const void* at, const void* bt, void* c, void* c2, const int32_t* kofs, int64_t pitch,
+                        int E, int64_t M, int64_t N, int64_t split, hipStream_t s, bool out_bf16 = false);
 hipError_t launch_colmap(const int32_t* counts, const int32_t* offsets, int E, int64_t rows, int64_t cols,
                          int32_t* kofs, int32_t* colmap, hipStream_t s);
 // mode 0: rows of src (x or dout) by token, 2: w * SiLU(g) u from gu, 3: dgu rows.

@@ -786,12 +786,13 @@ size_t moe_backward_workspace_bytes(const moe_dims_t* dm) {
 }
 
 // gu_saved: g | u rows kept by moe_layer_forward_train (read instead of the
-// FC1 recompute), or null.
+// FC1 recompute), or null. wgrad_bf16: dw1, dw3, dw2 are bf16 (else fp32).
 static int run_backward(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
                         const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                         const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
-                        void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits,
-                        float* dtopk_w, const void* gu_saved, void* ws, size_t ws_bytes, void* stream) {
+                        void* dx, float* dwg, float* dbias, void* dw1, void* dw3, void* dw2, float* dlogits,
+                        float* dtopk_w, const void* gu_saved, bool wgrad_bf16, void* ws, size_t ws_bytes,
+                        void* stream) {
   if (int st = check_dims(dm)) return st;
   if (!ok16(wg) || !ok16(w1) || !ok16(w3) || !ok16(w2) || !ok16(dwg) || !ok4(dbias) || !ok16(dw1) || !ok16(dw3) ||
       !ok16(dw2) || !ok4(counts) || !ok4(offsets) || !ok4_or_null(dlogits) || !ok4_or_null(dtopk_w))
@@ -809,8 +810,11 @@ static int run_backward(const moe_dims_t* dm, const void* x, const void* wg, con
   const int E = dm->E, k = dm->k;
   if (T == 0) {
     // no rows: every weight gradient is zero
-    for (auto pr : {std::make_pair(dw1, E * f * d), std::make_pair(dw3, E * f * d), std::make_pair(dw2, E * d * f),
-                    std::make_pair(dwg, E * d), std::make_pair(dbias, int64_t(E))})
+    // (a bf16 gradient of n elements is n / 2 zero floats; E f d is even)
+    const int64_t nw = wgrad_bf16 ? E * f * d / 2 : E * f * d;
+    for (auto pr : {std::make_pair(static_cast<float*>(dw1), nw), std::make_pair(static_cast<float*>(dw3), nw),
+                    std::make_pair(static_cast<float*>(dw2), nw), std::make_pair(dwg, E * d),
+                    std::make_pair(dbias, int64_t(E))})
       if (int st = hip_status(launch_fill_zero(pr.first, pr.second, s))) return st;
     return MOE_OK;
   }
@@ -864,12 +868,14 @@ static int run_backward(const moe_dims_t* dm, const void* x, const void* wg, con
   {
     StageScope sc(MOE_STAGE_BWD_WG2, s);
     // dW2_e [d][f] = dout^T (w h) over expert e's rows
-    if (int st = hip_status(launch_wgrad(b.dyt, b.ht, dw2, nullptr, b.kofs, b.pp, E, d, f, d, s))) return st;
+    if (int st = hip_status(launch_wgrad(b.dyt, b.ht, dw2, nullptr, b.kofs, b.pp, E, d, f, d, s, wgrad_bf16)))
+      return st;
   }
   {
     StageScope sc(MOE_STAGE_BWD_WG13, s);
     // [dW1_e ; dW3_e] [2f][d] = [dg | du]^T x over expert e's rows
-    if (int st = hip_status(launch_wgrad(b.dgut, b.xgt, dw1, dw3, b.kofs, b.pp, E, 2 * f, d, f, s))) return st;
+    if (int st = hip_status(launch_wgrad(b.dgut, b.xgt, dw1, dw3, b.kofs, b.pp, E, 2 * f, d, f, s, wgrad_bf16)))
+      return st;
   }
   StageScope sc(MOE_STAGE_BWD_GATE, s);
   return hip_status(launch_gate_grad(x, perm, offsets, b.dl, T, k, d, E, b.gpart, b.bpart, dwg, dbias, s));
@@ -881,7 +887,7 @@ int moe_layer_backward(const moe_dims_t* dm, const void* x, const void* wg, cons
                        void* dx, float* dwg, float* dbias, float* dw1, float* dw3, float* dw2, float* dlogits,
                        float* dtopk_w, void* ws, size_t ws_bytes, void* stream) {
   return run_backward(dm, x, wg, w1, w3, w2, topk_idx, topk_w, counts, offsets, perm, inv_perm, dout, dx, dwg, dbias,
-                      dw1, dw3, dw2, dlogits, dtopk_w, nullptr, ws, ws_bytes, stream);
+                      dw1, dw3, dw2, dlogits, dtopk_w, nullptr, false, ws, ws_bytes, stream);
 }
 
 int moe_layer_backward_saved(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
@@ -892,7 +898,18 @@ int moe_layer_backward_saved(const moe_dims_t* dm, const void* x, const void* wg
                              void* stream) {
   if (dm && dm->T > 0 && !ok16(gu)) return MOE_ERR_INVALID;
   return run_backward(dm, x, wg, w1, w3, w2, topk_idx, topk_w, counts, offsets, perm, inv_perm, dout, dx, dwg, dbias,
-                      dw1, dw3, dw2, dlogits, dtopk_w, gu, ws, ws_bytes, stream);
+                      dw1, dw3, dw2, dlogits, dtopk_w, gu, false, ws, ws_bytes, stream);
+}
+
+int moe_layer_backward_ex(const moe_dims_t* dm, const void* x, const void* wg, const void* w1, const void* w3,
+                          const void* w2, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, const void* dout,
+                          const void* gu, int wgrad_dtype, void* dx, float* dwg, float* dbias, void* dw1, void* dw3,
+                          void* dw2, float* dlogits, float* dtopk_w, void* ws, size_t ws_bytes, void* stream) {
+  if (wgrad_dtype != MOE_DTYPE_F32 && wgrad_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (gu && (reinterpret_cast<uintptr_t>(gu) & 15)) return MOE_ERR_INVALID;
+  return run_backward(dm, x, wg, w1, w3, w2, topk_idx, topk_w, counts, offsets, perm, inv_perm, dout, dx, dwg, dbias,
+                      dw1, dw3, dw2, dlogits, dtopk_w, gu, wgrad_dtype == MOE_DTYPE_BF16, ws, ws_bytes, stream);
 }
 
 int moe_timing_enable(int capacity, unsigned stage_mask) {

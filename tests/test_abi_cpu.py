@@ -231,8 +231,9 @@ def test_layer_backward_validation():
 
 @needs_no_gpu
 def test_training_pair_validation():
-    """moe_layer_forward_train and moe_layer_backward_saved check the kept g | u
-    buffer and the backward's limits before anything is launched."""
+    """moe_layer_forward_train, moe_layer_backward_saved and moe_layer_backward_ex
+    check the kept g | u buffer, the weight-gradient type and the backward's
+    limits before anything is launched."""
     lib = moe.load_library()
     good = dict(d=256, f=512)
 
@@ -257,6 +258,18 @@ def test_training_pair_validation():
     assert bwd(dims=dict(dtype=0)) == 2
     assert bwd(dims=dict(f=320)) == 2
     assert bwd(ws_bytes=16) == 3
+
+    def ex(dims=None, gu=None, wdt=1, ws_bytes=1 << 40):
+        dm = _dims(**{**good, **(dims or {})})
+        return lib.moe_layer_backward_ex(ctypes.byref(dm), A, A, A, A, A, A, A, A, A, A, A, A, gu, wdt, A, A, A,
+                                         A, A, A, None, None, A, ws_bytes, None)
+    assert ex(wdt=2) == 1                            # weight gradients fp32 or bf16 only
+    assert ex(wdt=-1) == 1
+    assert ex(gu=A + 8) == 1                         # optional g | u, 16-byte aligned
+    assert ex(dims=dict(dtype=0)) == 2
+    assert ex(dims=dict(d=192)) == 2
+    assert ex(ws_bytes=16) == 3
+    assert ex(gu=A, wdt=0, ws_bytes=16) == 3
 
 
 def test_plan_layout_inside_the_workspace():

@@ -9,8 +9,10 @@ g | u rows, and moe_layer_backward_saved reads them instead of recomputing FC1.
 * every gradient of moe_layer_backward_saved bit for bit moe_layer_backward's
   (whose parity with the backward oracle is tested on its own), so the kept
   g | u is exactly the backward's recompute.
-Small shapes check every element; the Mixtral prefill workload checks sampled
-tokens and rows, and every gradient element bit for bit.
+Small shapes check every element; the Mixtral prefill and DeepSeek-shaped
+workloads check sampled tokens and rows (the first, middle and last row of
+each expert, of up to 16 experts including the largest), and every gradient
+element bit for bit.
 """
 import sys
 
@@ -112,8 +114,9 @@ def test_train_pair_twice_on_one_workspace():
 
 
 @pytest.mark.timeout(900)
-def test_train_pair_full_size_sampled():
-    cfg = moe_inputs.config("mixtral_prefill_skew")
+@pytest.mark.parametrize("name", ["mixtral_prefill_skew", "deepseek_skew"])
+def test_train_pair_full_size_sampled(name):
+    cfg = moe_inputs.config(name)
     _say(f"case train pair full {cfg.name}: generating inputs on the GPU")
     inp = moe_inputs.make_layer_inputs(cfg, 0, "cuda")
     dout = moe_inputs.output_grad(cfg.T, cfg.d, cfg.dtype, 0, device="cuda")
@@ -129,7 +132,10 @@ def test_train_pair_full_size_sampled():
     assert rel_err(gpu_float(out_t[toks]), ref) <= TOL
     perm, offsets = r["perm"].cpu().numpy(), r["offsets"].cpu().numpy()
     rows = []
-    for e in range(cfg.E):
+    counts = np.diff(offsets)
+    experts = range(cfg.E) if cfg.E <= 16 else sorted(
+        set(np.linspace(0, cfg.E - 1, 15).astype(int).tolist()) | {int(np.argmax(counts))})
+    for e in experts:
         p0, p1 = int(offsets[e]), int(offsets[e + 1])
         if p1 > p0:
             rows += sorted({p0, (p0 + p1) // 2, p1 - 1})
