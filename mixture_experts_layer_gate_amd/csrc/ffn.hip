@@ -935,11 +935,11 @@ struct DlGemm {
     }
 
     if (mode_f32_out(kMode) || sp > 1) {
-      // fp32 epilogue through LDS, one 16-row block i of every wave's rows at a
-      // time (so the accumulators of block i die as it is stored): the waves
-      // write acc[i] into a [WM * 16][BN + 4] tile (the 4-float pad spreads a
-      // fragment's 4-row steps over distinct banks), then all threads store
-      // 16-byte row chunks.
+      // fp32 epilogue through LDS, IG 16-row blocks i of every wave's rows at a
+      // time (so the accumulators of those blocks die as they are stored): the
+      // waves write acc[i] into [IG][WM * 16][BN + 4] tiles (the 4-float pad
+      // spreads a fragment's 4-row steps over distinct banks), then all threads
+      // store 16-byte row chunks.
       constexpr int CP = BN + 4;
       constexpr int SR = WM * 16;  // rows per slice
       static_assert(SR * CP * 4 <= LDS_BYTES, "slice fits in the stage buffers");
@@ -962,36 +962,49 @@ struct DlGemm {
         cbase = static_cast<float*>(g.C) + static_cast<int64_t>(row0) * N;
       }
       constexpr int VPR = BN / 4;  // 16-byte vectors per tile row
-#pragma unroll
-      for (int i = 0; i < MI16; ++i) {
+      if (kWgrad && hbase != nullptr) {
+        // bf16 weight gradients: the whole tile at once, rounded into a
+        // [BM][BN + 8] bf16 tile (the pad spreads a fragment's 4-row steps
+        // over distinct banks), then 8 columns per 16-byte store
+        constexpr int HP = BN + 8, VPR8 = BN / 8;
+        static_assert(BM * HP * 2 <= LDS_BYTES, "bf16 tile fits in the stage buffers");
+        bf16_t* ht = reinterpret_cast<bf16_t*>(lds);
         lds_barrier();
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int i = 0; i < MI16; ++i)
 #pragma unroll
-          for (int j = 0; j < NJ16; ++j)
-            ct[(wm * 16 + 4 * (lane >> 4) + v) * CP + wn * TN + 16 * j + (lane & 15)] = acc[i][j][v];
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int j = 0; j < NJ16; ++j)
+              ht[(wm * TM + 16 * i + 4 * (lane >> 4) + v) * HP + wn * TN + 16 * j + (lane & 15)] =
+                  static_cast<bf16_t>(f32_to_bf16_bits(acc[i][j][v]));
         __syncthreads();
-        if (kWgrad && hbase != nullptr) {
-          // bf16: 8 columns (16 bytes) per store
-          constexpr int VPR8 = BN / 8;
-          for (int q = tid; q < SR * VPR8; q += NT) {
-            const int rl = q / VPR8, c8 = (q % VPR8) * 8;
-            const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
-            if (r < rows && col0 + c8 < ncols) {
-              const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c8);
-              const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c8 + 4);
-              u32x4_t pk;
-              pk[0] = pack_bf16x2(v0[0], v0[1]);
-              pk[1] = pack_bf16x2(v0[2], v0[3]);
-              pk[2] = pack_bf16x2(v1[0], v1[1]);
-              pk[3] = pack_bf16x2(v1[2], v1[3]);
-              *reinterpret_cast<u32x4_t*>(hbase + static_cast<int64_t>(r) * cp + col0 + c8) = pk;
-            }
-          }
-        } else {
-          for (int q = tid; q < SR * VPR; q += NT) {
+        for (int q = tid; q < rows * VPR8; q += NT) {
+          const int r = q / VPR8, c8 = (q % VPR8) * 8;
+          if (col0 + c8 < ncols)
+            *reinterpret_cast<u32x4_t*>(hbase + static_cast<int64_t>(r) * cp + col0 + c8) =
+                *reinterpret_cast<const u32x4_t*>(ht + r * HP + c8);
+        }
+      } else {
+        // IG blocks i per pass: as many as fit in the stage buffers for the
+        // backward's fp32 forms (fewer barriers), one for the forward's split parts
+        constexpr int IG = (mode_f32_out(kMode) && MI16 % 4 == 0 && 4 * SR * CP * 4 <= LDS_BYTES) ? 4 : 1;
+#pragma unroll
+        for (int i0 = 0; i0 < MI16; i0 += IG) {
+          lds_barrier();
+#pragma unroll
+          for (int ii = 0; ii < IG; ++ii)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+              for (int j = 0; j < NJ16; ++j)
+                ct[(ii * SR + wm * 16 + 4 * (lane >> 4) + v) * CP + wn * TN + 16 * j + (lane & 15)] =
+                    acc[i0 + ii][j][v];
+          __syncthreads();
+          for (int q = tid; q < IG * SR * VPR; q += NT) {
             const int rl = q / VPR, c4 = (q % VPR) * 4;
-            const int r = (rl / 16) * TM + 16 * i + rl % 16;  // row of the tile
+            const int rs = rl % SR;
+            const int r = (rs / 16) * TM + 16 * (i0 + rl / SR) + rs % 16;  // row of the tile
             if (r < rows && col0 + c4 < ncols) {
               f32x4_t* dst = reinterpret_cast<f32x4_t*>(cbase + static_cast<int64_t>(r) * cp + col0 + c4);
               const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + rl * CP + c4);
