@@ -336,7 +336,8 @@ int moe_layer_forward_fused_packed(const moe_dims_t* dims, const void* x, const 
  * dwg [E][d], dbias [E], dw1 [E][f][d], dw3 [E][f][d], dw2 [E][d][f] fp32
  * (every entry written, zero for experts that received no rows); optional
  * (NULL to skip) dlogits [T][E] and dtopk_w [T][k] fp32.
- * FC1 is recomputed (g and u are not kept by the forward); W1, W3 and W2
+ * FC1 is recomputed (moe_layer_forward keeps only h; moe_layer_forward_train
+ * and moe_layer_backward_saved below keep g and u instead); W1, W3 and W2
  * are read as stored (the DGrad products take them through transposing LDS
  * loads, no copies). Accumulation is fp32 throughout;
  * dg, du, h and w*dout enter the matrix products as bf16. Every reduction

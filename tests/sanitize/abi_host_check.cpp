@@ -177,6 +177,35 @@ int main() {
   EXPECT(backward(&bw, (float*)A, (float*)M2, BIG), MOE_ERR_INVALID);
   EXPECT(backward(&bw, (float*)A, nullptr, 16), MOE_ERR_WORKSPACE);
 
+  // training pair and the backward's options
+  auto train = [&](const moe_dims_t* m, void* gu, size_t wsb) {
+    return moe_layer_forward_train(m, A, A, nullptr, A, A, A, A, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, gu, A, wsb, nullptr);
+  };
+  EXPECT(train(&bw, nullptr, BIG), MOE_ERR_INVALID);
+  EXPECT(train(&bw, M2, BIG), MOE_ERR_INVALID);
+  EXPECT(train(&bw_f32, A, BIG), MOE_ERR_UNSUPPORTED);
+  EXPECT(train(&bw_d, A, BIG), MOE_ERR_UNSUPPORTED);
+  EXPECT(train(&bw, A, 16), MOE_ERR_WORKSPACE);
+  auto saved = [&](const moe_dims_t* m, const void* gu, size_t wsb) {
+    return moe_layer_backward_saved(m, A, A, A, A, A, (int32_t*)A, (float*)A, (int32_t*)A, (int32_t*)A, (int32_t*)A,
+                                    (int32_t*)A, A, gu, A, (float*)A, (float*)A, (float*)A, (float*)A, (float*)A,
+                                    nullptr, nullptr, A, wsb, nullptr);
+  };
+  EXPECT(saved(&bw, nullptr, BIG), MOE_ERR_INVALID);
+  EXPECT(saved(&bw, M2, BIG), MOE_ERR_INVALID);
+  EXPECT(saved(&bw_f32, A, BIG), MOE_ERR_UNSUPPORTED);
+  EXPECT(saved(&bw, A, 16), MOE_ERR_WORKSPACE);
+  auto ex = [&](const moe_dims_t* m, const void* gu, int wdt, size_t wsb) {
+    return moe_layer_backward_ex(m, A, A, A, A, A, (int32_t*)A, (float*)A, (int32_t*)A, (int32_t*)A, (int32_t*)A,
+                                 (int32_t*)A, A, gu, wdt, A, (float*)A, (float*)A, A, A, A, nullptr, nullptr, A, wsb,
+                                 nullptr);
+  };
+  EXPECT(ex(&bw, nullptr, 7, BIG), MOE_ERR_INVALID);
+  EXPECT(ex(&bw, M2, MOE_DTYPE_BF16, BIG), MOE_ERR_INVALID);
+  EXPECT(ex(&bw_d, nullptr, MOE_DTYPE_BF16, BIG), MOE_ERR_UNSUPPORTED);
+  EXPECT(ex(&bw, A, MOE_DTYPE_F32, 16), MOE_ERR_WORKSPACE);
+
   // stage timing and probes
   EXPECT(moe_timing_enable(0, 0), MOE_ERR_INVALID);
   EXPECT(moe_timing_read(99, nullptr, nullptr), MOE_ERR_INVALID);
